@@ -1,0 +1,546 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values the
+pages print (tests/golden/, each file cites its page and table/figure),
+brute force in exact rational arithmetic, closed forms, invariants and
+library routines (torch's float8_e4m3fn / bfloat16 casts, numpy int64 matmul).
+"""
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ---------------------------------------------------------------- exact helpers
+E2M1_FR = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2),
+           Fraction(3), Fraction(4), Fraction(6)]
+
+
+def bf_nearest_e2m1(v: Fraction) -> int:
+    """Brute force: index of the nearest of the 8 states to v >= 0 (exact),
+    half-way cases to the even index; everything above 6 takes 6."""
+    best, bd = None, None
+    for i, t in enumerate(E2M1_FR):
+        d = abs(v - t)
+        if bd is None or d < bd or (d == bd and i % 2 == 0):
+            best, bd = i, d
+    return best
+
+
+def e4m3_fr(code: int) -> Fraction:
+    e, m = (code >> 3) & 15, code & 7
+    if e == 0:
+        return Fraction(m, 8) * Fraction(1, 64)
+    return Fraction(8 + m, 8) * Fraction(2) ** (e - 7)
+
+
+E4M3_FR = [e4m3_fr(c) for c in range(0x7F)]
+
+
+def bf_nearest_e4m3(r: Fraction) -> int:
+    best, bd = None, None
+    for c, val in enumerate(E4M3_FR):
+        d = abs(r - val)
+        if bd is None or d < bd or (d == bd and c % 2 == 0):
+            best, bd = c, d
+    return best
+
+
+def bf_block_exponent(m: Fraction) -> int:
+    """Smallest integer e with m <= 6 * 2^e, after the emulation's guard
+    m >= 1e-8 (fp32)."""
+    m = max(m, Fraction(float(np.float32(1e-8))))
+    e = -200
+    while 6 * Fraction(2) ** e < m:
+        e += 1
+    return e
+
+
+def bf_mxfp4_block(xs, block_exp_override=None):
+    """Brute-force MXFP4 of one block (list of fp32 floats) -> (codes, E8M0 byte)."""
+    m = max(abs(Fraction(float(x))) for x in xs)
+    e = bf_block_exponent(m)
+    codes = []
+    for x in xs:
+        v = abs(Fraction(float(x))) / Fraction(2) ** e
+        c = bf_nearest_e2m1(v)
+        if np.signbit(np.float32(x)):
+            c |= 8
+        codes.append(c)
+    return codes, e + 127
+
+
+# ------------------------------------------------------------------- P1: E2M1
+def test_e2m1_table_matches_page():
+    rows = _rows("e2m1_table.txt")
+    assert len(rows) == 8
+    for bits, sign, exp, man, val in rows:
+        code = int(bits, 2)
+        assert sign == "+" and bits[1:3] == exp and bits[3] == man
+        assert O.E2M1_POSITIVE[code] == float(val)
+        assert O.e2m1_value_from_bits(code) == float(val)          # bit-field formula
+        assert O.e2m1_value_from_bits(code | 8) == -float(val)     # mirror
+    assert np.signbit(O.e2m1_value_from_bits(8)) and O.e2m1_value_from_bits(8) == 0.0  # -0
+
+
+def test_e2m1_decode_vector_equals_bitfields():
+    codes = np.arange(16)
+    dec = O.e2m1_decode(codes)
+    ref = np.array([O.e2m1_value_from_bits(int(c)) for c in codes])
+    assert np.array_equal(dec, ref) and np.array_equal(np.signbit(dec), np.signbit(ref))
+
+
+# ------------------------------------------------------------------- P2: storage
+def test_storage_closed_form_matches_pages():
+    rows = _rows("storage_footprint.txt")
+    d = {(r[0], r[1]): float(r[2]) for r in rows}
+    # 16 elements: 16 * 4 + 8 bits
+    assert 16 * 4 + 8 == d[("bits_per_block16", "72")]
+    R, K = 64, 4096
+    nv = O.storage_bytes(R, K, "nvfp4") - 4          # minus the per-tensor fp32
+    mx = O.storage_bytes(R, K, "mxfp4")
+    assert nv * 8 / (R * K) == d[("bits_per_elem", "block16_8bit_scale")]
+    assert mx * 8 / (R * K) == d[("bits_per_elem", "block32_8bit_scale")]
+    assert np.floor((1 - 4.25 / 8) * 1000) / 10 == d[("saving_vs_fp8_percent", "block32")]
+    for key, gb in [(k, v) for (kind, k), v in d.items() if kind == "footprint_gb"]:
+        params = int(float(key))
+        assert round(params * 4.5 / 8 / 1e9, 1) == gb
+
+
+# ------------------------------------------------------------------- P3: E8M0 scale
+def test_e8m0_decode_is_pure_power_of_two():
+    e = np.arange(0, 255)
+    v = O.e8m0_decode(e)
+    m, ex = np.frexp(v)
+    assert np.all(m == 0.5) and np.array_equal(ex - 1, e - 127)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_mx_scale_is_minimal_power_of_two(seed):
+    rng = np.random.default_rng(seed)
+    # block maxima spread over the whole exponent range, plus boundaries 6*2^k and +-1 ulp
+    mags = np.float32(np.exp2(rng.uniform(-40, 126, size=3000)))
+    k = np.arange(-35, 126)
+    b = (6.0 * np.exp2(k.astype(np.float64))).astype(np.float32)
+    mags = np.concatenate([mags, b, np.nextafter(b, np.float32(0)), np.nextafter(b, np.float32(np.inf)),
+                           np.float32([0.0, 1e-45, 1e-8, 6e-9, 1.1e-8])])
+    mags = mags[np.isfinite(mags)]
+    e = O.mx_block_exponent(mags.astype(np.float64))
+    for m, ee in zip(mags[::7], e[::7]):          # brute force on a subset
+        assert bf_block_exponent(Fraction(float(m))) == ee
+    mm = np.maximum(mags.astype(np.float64), float(np.float32(1e-8)))
+    assert np.all(mm <= 6 * np.exp2(e.astype(np.float64)))
+    assert np.all(mm > 6 * np.exp2((e - 1).astype(np.float64)))
+    assert e.min() >= -29
+
+
+# --------------------------------------------------------- P4: brute force, tiny
+def _special_values():
+    vals = [0.0, -0.0, 1e-45, -1e-45, 1e-39, 6.0, -6.0, 5.0, 3.5, 0.25, 0.75, 1.25, 1.75, 2.5]
+    out = []
+    for t in [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]:
+        for j in (-3, 0, 4):
+            c = np.float32(t * 2.0 ** j)
+            out += [c, np.nextafter(c, np.float32(0)), np.nextafter(c, np.float32(np.inf))]
+    return np.float32(vals + out)
+
+
+@pytest.mark.parametrize("block", [1, 2, 3, 4])
+def test_mxfp4_bruteforce_tiny_blocks(block):
+    rng = np.random.default_rng(100 + block)
+    spec = _special_values()
+    for trial in range(300):
+        if trial % 2:
+            xs = rng.choice(spec, size=block)
+        else:
+            xs = (rng.standard_normal(block) * np.exp2(rng.integers(-20, 20))).astype(np.float32)
+        # put the block inside an MXFP4 block of 32 (rest zeros) -> same result
+        x = np.zeros((1, 32), np.float32)
+        x[0, :block] = xs
+        codes, scales = O.mxfp4_quantize(x)
+        c = O.unpack_codes(codes)[0]
+        ref_c, ref_s = bf_mxfp4_block(list(x[0]))
+        assert scales[0, 0] == ref_s
+        assert list(c) == ref_c, (xs, list(c), ref_c)
+
+
+def bf_nvfp4(x):
+    """Brute force NVFP4 of a tiny [R, K] tensor with exact rationals.
+    The per-tensor scale is the correctly rounded fp32 of amax / 2688 (checked
+    here from its definition, not taken from the oracle)."""
+    a = max(abs(Fraction(float(v))) for v in x.ravel())
+    g = Fraction(float(np.float32(float(a)) / np.float32(2688.0))) if a else Fraction(1)
+    # g must be the fp32 value nearest to a / 2688
+    if a:
+        gf = np.float32(float(g))
+        exact = a / 2688
+        lo, hi = np.nextafter(gf, np.float32(0)), np.nextafter(gf, np.float32(np.inf))
+        assert abs(Fraction(float(gf)) - exact) <= abs(Fraction(float(lo)) - exact)
+        assert abs(Fraction(float(gf)) - exact) <= abs(Fraction(float(hi)) - exact)
+    R, K = x.shape
+    codes = np.zeros((R, K), np.uint8)
+    sbytes = np.zeros((R, K // 16), np.uint8)
+    for r in range(R):
+        for b in range(K // 16):
+            blk = x[r, b * 16:(b + 1) * 16]
+            m = max(abs(Fraction(float(v))) for v in blk)
+            sc = bf_nearest_e4m3(m / (6 * g))
+            sbytes[r, b] = sc
+            unit = E4M3_FR[sc] * g
+            for j, v in enumerate(blk):
+                mag = abs(Fraction(float(v)))
+                if unit == 0:
+                    c = 0
+                else:
+                    c = bf_nearest_e2m1(mag / unit)
+                if np.signbit(v):
+                    c |= 8
+                codes[r, b * 16 + j] = c
+    return codes, sbytes, g
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_nvfp4_bruteforce_tiny(seed):
+    rng = np.random.default_rng(seed)
+    x = (rng.standard_normal((3, 32)) * 0.5).astype(np.float32)
+    x[0, 3] = 40.0                               # tensor max
+    x[1, :16] = _special_values()[:16] * np.float32(1e-3)   # tiny block, sign of zero
+    x[2, 16:] *= np.float32(1e-6)                # block scale deep in E4M3 subnormals / zero
+    codes, sbytes, g = O.nvfp4_quantize(x)
+    rc, rs, rg = bf_nvfp4(x)
+    assert Fraction(float(g)) == rg
+    assert np.array_equal(sbytes, rs)
+    assert np.array_equal(O.unpack_codes(codes), rc)
+    # saturation happens: some |x|/(s g) > 6 exist only when s rounded down
+    assert sbytes.max() <= 0x7E
+
+
+# --------------------------------------------------------- P5: exhaustive bf16
+def test_exhaustive_bf16_elements_bruteforce():
+    """Every finite bf16 bit pattern appears as an element, in a block where it
+    is the maximum and in one anchored block (anchor 6*2^e sets the scale so
+    the element lands in a chosen rounding region); oracle vs exact brute force
+    with integer arithmetic."""
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    n = vals.size
+    d = np.arange(n) % 6 - 1                     # region selector, -1..4
+    mag = np.abs(vals).astype(np.float64)
+    fl = np.floor(np.log2(np.where(mag > 0, mag, 1.0))).astype(np.int64)
+    e_anchor = np.clip(fl + d, -29, 125)
+    anchor = (6.0 * np.exp2(e_anchor.astype(np.float64))).astype(np.float32)
+    x = np.zeros((n, 64), np.float32)
+    x[:, 0] = vals          # block 0: the element alone (it is the max)
+    x[:, 32] = vals         # block 1: element + anchor
+    x[:, 33] = anchor
+    codes, scales = O.mxfp4_quantize(x)
+    c = O.unpack_codes(codes)
+    # brute force with Python integers: v = |x| / 2^e is compared exactly with
+    # the states via numerator/denominator arithmetic.
+    for col, sc_col in ((0, 0), (32, 1)):
+        for i in range(0, n, 1):
+            xv = float(x[i, col])
+            m = max(abs(Fraction(xv)), abs(Fraction(float(x[i, 33]))) if col == 32 else Fraction(0))
+            e = int(scales[i, sc_col]) - 127
+            if i % 97 == 0:                      # scale rule by brute force on a subset
+                assert bf_block_exponent(m) == e
+            v = abs(Fraction(xv)) / Fraction(2) ** e
+            ref = bf_nearest_e2m1(v) | (8 if np.signbit(x[i, col]) else 0)
+            assert c[i, col] == ref, (xv, e, c[i, col], ref)
+
+
+# -------------------------------------------------- P6: outlier containment
+@pytest.mark.parametrize("block", [32, 16])
+def test_outlier_changes_only_its_block(block):
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((4, 256)).astype(np.float32)
+    c0, s0 = O.mxfp4_quantize(x, block=block)
+    for (r, k) in [(0, 14), (2, 100), (3, 255)]:
+        y = x.copy()
+        y[r, k] = np.float32(50.0) * np.abs(x[r]).max()     # an outlier 50x the row's maximum
+        c1, s1 = O.mxfp4_quantize(y, block=block)
+        ch_s = np.argwhere(s0 != s1)
+        assert ch_s.tolist() == [[r, k // block]]
+        u0, u1 = O.unpack_codes(c0), O.unpack_codes(c1)
+        ch_c = np.argwhere(u0 != u1)
+        assert len(ch_c) > 0 and np.all(ch_c[:, 0] == r) and np.all(ch_c[:, 1] // block == k // block)
+
+
+def test_nvfp4_outlier_contained_at_fixed_global_scale():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((2, 128)).astype(np.float32)
+    g = np.float32(0.01)
+    c0, s0, _ = O.nvfp4_quantize(x, global_scale=g)
+    y = x.copy()
+    y[1, 37] = np.float32(50.0) * np.abs(x[1]).max()
+    c1, s1, _ = O.nvfp4_quantize(y, global_scale=g)
+    assert np.argwhere(s0 != s1).tolist() == [[1, 2]]
+    ch = np.argwhere(O.unpack_codes(c0) != O.unpack_codes(c1))
+    assert np.all(ch[:, 0] == 1) and np.all(ch[:, 1] // 16 == 2)
+
+
+# ------------------------------------------------------------ P7: invariants
+def test_mx_sign_symmetry_and_power_of_two_equivariance():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((8, 128)) * 3).astype(np.float32)
+    c, s = O.mxfp4_quantize(x)
+    cn, sn = O.mxfp4_quantize(-x)
+    assert np.array_equal(s, sn)
+    assert np.array_equal(O.unpack_codes(c) ^ 8, O.unpack_codes(cn))
+    for j in (-5, 3, 17):
+        cj, sj = O.mxfp4_quantize((x * np.float32(2.0 ** j)).astype(np.float32))
+        assert np.array_equal(cj, c)
+        assert np.array_equal(sj.astype(int), s.astype(int) + j)
+
+
+def test_mx_dequant_quant_idempotent():
+    rng = np.random.default_rng(10)
+    x = (rng.standard_normal((16, 256)) * np.exp2(rng.integers(-10, 10, size=(16, 1)))).astype(np.float32)
+    c, s = O.mxfp4_quantize(x)
+    xh = O.dequantize("mxfp4", c, s)
+    c2, s2 = O.mxfp4_quantize(xh)
+    assert np.array_equal(O.dequantize("mxfp4", c2, s2), xh)
+
+
+def test_mx_every_block_max_round_trip():
+    """For every possible quantized block maximum (each state times each
+    scale in range), quantizing the dequantized block reproduces it."""
+    for e in range(-29, 126, 7):
+        for i in range(1, 8):
+            blk = np.zeros((1, 32), np.float32)
+            blk[0, 0] = np.float32(O.E2M1_POSITIVE[i] * 2.0 ** e)
+            blk[0, 1:8] = np.float32(np.array(O.E2M1_POSITIVE[:7]) * 2.0 ** e)
+            c, s = O.mxfp4_quantize(blk)
+            assert np.array_equal(O.dequantize("mxfp4", c, s), blk)
+
+
+# ------------------------------------------- P8: the pages' emulation and demo
+def page_emulation_quantize(t: torch.Tensor, block_size: int) -> torch.Tensor:
+    """The pages' PyTorch emulation ("End-to-End Implementation"), written
+    from its description: pad, view as blocks, block max, clamp at 1e-8,
+    S = 2^ceil(log2(max / 6)) in fp32, divide, nearest of the 8 states by
+    argmin (lowest index on ties) times sign; returns the dequantized tensor."""
+    states = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    flat = t.flatten()
+    pad = (-flat.numel()) % block_size
+    flat = torch.cat([flat, torch.zeros(pad)])
+    blocks = flat.view(-1, block_size)
+    mx = blocks.abs().max(dim=-1, keepdim=True).values.clamp(min=1e-8)
+    scale = torch.pow(2.0, torch.ceil(torch.log2(mx / 6.0)))
+    v = blocks / scale
+    idx = torch.argmin((v.abs().unsqueeze(-1) - states).abs(), dim=-1)
+    q = torch.sign(v) * states[idx]
+    out = (q * scale).flatten()
+    return out[: t.numel()].view(t.shape)
+
+
+@pytest.mark.parametrize("block", [32, 16])
+def test_agrees_with_page_emulation_on_gaussian_fp32(block):
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(64, 512, generator=g) * 0.7
+    x[:, 5] *= 40
+    emu = page_emulation_quantize(x, block).numpy()
+    c, s = O.mxfp4_quantize(x.numpy(), block=block)
+    ora = O.dequantize("mxfp4", c, s)
+    assert np.array_equal(np.abs(emu), np.abs(ora))
+    nz = emu != 0
+    assert np.array_equal(np.sign(emu[nz]), np.sign(ora[nz]))
+
+
+def test_page_demo_block_beats_naive():
+    """The emulation's demo input (seed 42, 1024 x N(0, 0.5^2), outliers 24.5 at
+    42 and -31.2 at 512, blocks of 16): the block-scaled reconstruction has a
+    higher SNR than the naive per-tensor one (the page prints no numbers)."""
+    torch.manual_seed(42)
+    x = torch.randn(1024) * 0.5
+    x[42] = 24.5
+    x[512] = -31.2
+    xn = x.numpy().reshape(1, -1)
+    c, s = O.mxfp4_quantize(xn, block=16)
+    rec = O.dequantize("mxfp4", c, s)[0].astype(np.float64)
+    naive = O.naive_per_tensor_fp4(xn[0])
+    x64 = xn[0].astype(np.float64)
+    snr_b = 10 * np.log10(np.sum(x64 ** 2) / np.sum((x64 - rec) ** 2))
+    snr_n = 10 * np.log10(np.sum(x64 ** 2) / np.sum((x64 - naive) ** 2))
+    assert snr_b > snr_n + 10
+    # and the block scales exist only per 16 elements: 64 of them
+    assert s.shape == (1, 64)
+
+
+def test_naive_per_tensor_worked_example():
+    rows = _rows("naive_outlier_example.txt")
+    x = np.array([float(r[0]) for r in rows])
+    q_ref = np.array([float(r[1]) for r in rows])
+    rec = O.naive_per_tensor_fp4(x)
+    s = np.abs(x).max() / 6.0
+    assert np.allclose(rec / s, q_ref, atol=0)
+    # contrast: MXFP4 keeps resolution outside the outlier's block
+    blk = np.zeros((1, 64), np.float32)
+    blk[0, :6] = np.float32(x)
+    blk[0, 40:46] = np.float32(x[[0, 1, 2, 4, 5, 0]])
+    c, sc = O.mxfp4_quantize(blk)
+    rec_mx = O.dequantize("mxfp4", c, sc)[0]
+    assert np.all(rec_mx[40:46] != 0)
+
+
+# ------------------------------------------------------- P9: E4M3 codec
+def test_e4m3_decode_matches_torch():
+    b = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    o = O.e4m3_decode(np.arange(256))
+    same = (b == o) | (np.isnan(b) & np.isnan(o))
+    assert np.all(same)
+
+
+def test_e4m3_encode_matches_torch_cast():
+    # dense sweep of fp32 values between 2^-12 and 464 (below the NaN overflow)
+    bits = np.arange(np.float32(2.0 ** -12).view(np.uint32), np.float32(460.0).view(np.uint32), 4099,
+                     dtype=np.uint32)
+    v = bits.view(np.float32)
+    mids = np.array([(O.e4m3_value_from_bits(c) + O.e4m3_value_from_bits(c + 1)) / 2 for c in range(0x7E)],
+                    dtype=np.float32)
+    v = np.concatenate([v, mids, np.float32([0.0, 448.0, 449.0, 2.0 ** -10, 2.0 ** -9])])
+    ref = torch.from_numpy(np.minimum(v, 448.0).astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = O.e4m3_nearest_code(v.astype(np.float64), np.ones(v.shape))
+    assert np.array_equal(got, ref)
+
+
+def test_nvfp4_global_scale_self_consistency():
+    """Parity unpinned reading, checked for consistency: the block holding the
+    tensor maximum gets scale 448 and dequantized values stay within the
+    E2M1 half-step of the input."""
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    x[4, 77] = 3.0
+    c, s, g = O.nvfp4_quantize(x)
+    assert g == np.float32(3.0) / np.float32(2688.0)
+    assert s[4, 77 // 16] == 0x7E
+    xh = O.dequantize("nvfp4", c, s, g)
+    unit = np.repeat(O.e4m3_decode(s), 16, axis=1) * float(g)
+    assert np.all(np.abs(xh - x) <= unit * 1.0 + 1e-12)
+
+
+# ------------------------------------------------ P10/P11: products
+def test_gemm_unit_scales_is_integer_gemm():
+    rng = np.random.default_rng(12)
+    M, N, K = 16, 24, 256
+    ca = rng.integers(0, 256, size=(M, K // 2), dtype=np.uint8)
+    cb = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    ones_a = np.full((M, K // 32), 127, np.uint8)
+    ones_b = np.full((N, K // 32), 127, np.uint8)
+    a = O.dequantize("mxfp4", ca, ones_a)
+    b = O.dequantize("mxfp4", cb, ones_b)
+    y = O.gemm(a, b)
+    ia = (2 * O.e2m1_decode(O.unpack_codes(ca))).astype(np.int64)   # 2q is an integer
+    ib = (2 * O.e2m1_decode(O.unpack_codes(cb))).astype(np.int64)
+    exact = (ia @ ib.T)
+    assert np.array_equal(y.astype(np.float64) * 4, exact.astype(np.float64))
+
+
+def _exact_dot_rows(a, b):
+    return [[sum(Fraction(float(a[m, k])) * Fraction(float(b[n, k])) for k in range(a.shape[1]))
+             for n in range(b.shape[0])] for m in range(a.shape[0])]
+
+
+def test_gemm_with_scales_bruteforce():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((3, 64)).astype(np.float32)
+    w = (rng.standard_normal((5, 64)) * 0.02).astype(np.float32)
+    ca, sa = O.mxfp4_quantize(x)
+    cb, sb = O.mxfp4_quantize(w)
+    a = O.dequantize("mxfp4", ca, sa)
+    b = O.dequantize("mxfp4", cb, sb)
+    y = O.gemm(a, b)
+    ex = _exact_dot_rows(a, b)
+    for m in range(3):
+        for n in range(5):
+            assert y[m, n] == np.float32(float(ex[m][n]))   # one rounding of the exact sum
+    yb = O.gemm(a, b, out="bf16")
+    ref_bf = torch.from_numpy(y).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(yb, ref_bf)
+
+
+def test_dequant_values_bruteforce():
+    rng = np.random.default_rng(14)
+    x = rng.standard_normal((2, 32)).astype(np.float32)
+    c, s, g = O.nvfp4_quantize(x)
+    xh = O.dequantize("nvfp4", c, s, g)
+    codes = O.unpack_codes(c)
+    for r in range(2):
+        for k in range(32):
+            q = E2M1_FR[codes[r, k] & 7] * (-1 if codes[r, k] & 8 else 1)
+            exact = q * E4M3_FR[s[r, k // 16]] * Fraction(float(g))
+            assert xh[r, k] == np.float32(float(exact))
+    cm, sm = O.mxfp4_quantize(x)
+    xm = O.dequantize("mxfp4", cm, sm)
+    cu = O.unpack_codes(cm)
+    for r in range(2):
+        for k in range(32):
+            q = E2M1_FR[cu[r, k] & 7] * (-1 if cu[r, k] & 8 else 1)
+            assert Fraction(float(xm[r, k])) == q * Fraction(2) ** (int(sm[r, k // 32]) - 127)
+
+
+def test_gemv_bruteforce():
+    rng = np.random.default_rng(15)
+    xb = torch.from_numpy(rng.standard_normal((2, 96)).astype(np.float32)).to(torch.bfloat16)
+    xv = xb.to(torch.float32).numpy()
+    w = (rng.standard_normal((7, 96)) * 0.02).astype(np.float32)
+    cw, sw = O.mxfp4_quantize(w)
+    y = O.gemv(xv, cw, sw)
+    wh = O.dequantize("mxfp4", cw, sw)
+    ex = _exact_dot_rows(xv, wh)
+    for m in range(2):
+        for n in range(7):
+            f32 = np.float32(float(ex[m][n]))
+            assert y[m, n] == torch.tensor(float(f32)).to(torch.bfloat16).item()
+
+
+def test_grouped_equals_per_group_loop():
+    rng = np.random.default_rng(16)
+    G, N, K, T = 3, 8, 64, 11
+    x = torch.from_numpy(rng.standard_normal((T, K)).astype(np.float32)).to(torch.bfloat16).float().numpy()
+    w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+    offs = np.array([0, 4, 4, 11], np.int32)          # includes an empty expert
+    wc = np.stack([O.mxfp4_quantize(w[g])[0] for g in range(G)])
+    ws = np.stack([O.mxfp4_quantize(w[g])[1] for g in range(G)])
+    y, ac, as_ = O.grouped_gemm(x, offs, wc, ws)
+    for g in range(G):
+        r0, r1 = offs[g], offs[g + 1]
+        for r in range(r0, r1):
+            c1, s1 = O.mxfp4_quantize(x[r:r + 1])
+            assert np.array_equal(ac[r:r + 1], c1) and np.array_equal(as_[r:r + 1], s1)
+            a = O.dequantize("mxfp4", c1, s1)
+            b = O.dequantize("mxfp4", wc[g], ws[g])
+            ex = _exact_dot_rows(a, b)
+            for n in range(N):
+                f32 = np.float32(float(ex[0][n]))
+                assert y[r, n] == torch.tensor(float(f32)).to(torch.bfloat16).item()
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(17)
+    bits = rng.integers(0, 0x7F000000, size=200000, dtype=np.uint32)
+    bits[:3] = [0x3F808000, 0x3F818000, 0x3F80FFFF]   # ties to even and just below
+    v = bits.view(np.float32)
+    v = np.concatenate([v, -v])
+    ref = torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(O.round_to_bf16(v), ref)
+
+
+def test_tolerance_covers_bf16_rounding():
+    a = np.ones((1, 4))
+    b = np.ones((1, 4))
+    y = np.array([[3.0]], np.float32)
+    tol = O.gemm_tolerance(a, b, y, out="bf16")
+    assert np.isclose(tol[0, 0], 4e-5 + 2.0 ** -6)
