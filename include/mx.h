@@ -1,0 +1,181 @@
+/*
+ * mx.h -- C ABI of libmx: block-scaled 4-bit floating-point quantization
+ * (MXFP4, NVFP4) and the matrix products that consume it, for AMD gfx950.
+ *
+ * Formats (sources are the web pages this library implements):
+ *   E2M1 element: 1 sign, 2 exponent (bias 1), 1 mantissa bit; states
+ *     {0, 0.5, 1, 1.5, 2, 3, 4, 6} and their negatives, zero signed
+ *     ("NVFP4 Architecture: Microscaling & 4-Bit LLMs on Blackwell", section
+ *     "1. The E2M1 Floating-Point Format", table "The Complete Discrete State
+ *     Mapping of E2M1").
+ *   MXFP4: 32-element blocks, one E8M0 scale byte per block, S = 2^(E-127)
+ *     ("How Microscaling FP4 (MXFP4) Halves Memory Bandwidth", section "The
+ *     Microscaling Breakthrough: 32-Element Blocks"; "NVFP4 Architecture",
+ *     section "2. Micro-Block Exponent Scaling: E8M0 Format").
+ *   NVFP4: 16-element blocks ("NVIDIA NVFP4 quantization", section "The Physics
+ *     of NVFP4"), one FP8 E4M3 scale byte per block and one fp32 scale per
+ *     tensor (dual-level scaling, "NVFP4 Architecture", section "1. The
+ *     Dual-Level Mathematical Formulation").
+ *
+ * Memory layout of a quantized [rows, cols] tensor (blocks run along cols):
+ *   codes  uint8 [rows, cols/2], row pitch cols/2 bytes; element 2j of a row
+ *          in the low nibble of byte j, element 2j+1 in the high nibble.
+ *   scales uint8 [rows, cols/k], row pitch cols/k bytes (k = 32 or 16).
+ *   global_scale  fp32[1] (NVFP4 only).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or keeps them.  Scalars are passed by value.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Results are visible after the caller synchronizes.
+ *   - Arguments are validated on the host before any HIP call; an invalid call
+ *     returns a negative mx_status and enqueues nothing.  A failed launch
+ *     returns MX_ERR_HIP.  Faults inside kernels surface at the caller's sync.
+ *   - Device pointers must be 16-byte aligned; leading dimensions are in
+ *     elements and must keep every row 16-byte aligned.
+ *   - The library has no global state and is thread-safe; calls on one stream
+ *     run in order.
+ */
+#ifndef MX_H_
+#define MX_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mx_status {
+  MX_OK = 0,
+  MX_ERR_NULL = -1,         /* a required pointer is NULL */
+  MX_ERR_SHAPE = -2,        /* negative or inconsistent sizes / leading dims */
+  MX_ERR_ALIGN = -3,        /* pointer or row not 16-byte aligned */
+  MX_ERR_DTYPE = -4,        /* unknown or unsupported element type */
+  MX_ERR_UNSUPPORTED = -5,  /* valid but not provided (e.g. cols % k != 0) */
+  MX_ERR_HIP = -6,          /* a HIP launch failed */
+  MX_ERR_WORKSPACE = -7,    /* workspace missing or too small */
+  MX_ERR_FORMAT = -8        /* unknown format or mismatched operand formats */
+} mx_status;
+
+enum { MX_FMT_MXFP4 = 0, MX_FMT_NVFP4 = 1 };
+enum { MX_DT_F32 = 0, MX_DT_BF16 = 1 };
+
+/* mx_quantize flags */
+enum {
+  MX_QUANT_DEFAULT = 0,
+  /* NVFP4: use *global_scale as given (a calibrated, static per-tensor scale)
+     instead of computing it from the tensor's max |x|. */
+  MX_QUANT_STATIC_GLOBAL = 1
+};
+
+/* mx_workspace_bytes operations */
+enum { MX_OP_QUANTIZE = 0, MX_OP_GEMM = 1 };
+
+typedef struct mx_tensor {
+  int32_t fmt;            /* MX_FMT_MXFP4 or MX_FMT_NVFP4 */
+  int32_t reserved;       /* must be 0 */
+  int64_t rows, cols;     /* logical shape; cols is the blocked (K) axis */
+  uint8_t *codes;         /* device [rows, cols/2] */
+  uint8_t *scales;        /* device [rows, cols/k] */
+  float *global_scale;    /* device fp32[1]; NVFP4 only, NULL for MXFP4 */
+} mx_tensor;
+
+/*
+ * mx_quantize -- quantize a row-major [out->rows, out->cols] fp32/bf16 tensor.
+ *
+ * MXFP4 ("NVFP4 Architecture", section "1. The Dual-Level Mathematical
+ * Formulation", equations S_block and q_i, with S_global = 1, and the pages'
+ * PyTorch emulation): per 32-element block, m = max|x|;
+ * e = max(-29, smallest integer with m <= 6*2^e) (the emulation's
+ * max >= 1e-8 guard); scale byte e + 127; each element takes the E2M1 state
+ * nearest to x/2^e, half-way cases to the even code, sign copied from x.
+ * NVFP4: g = fp32(max|x| / 2688) over the whole tensor (1 if the tensor is 0),
+ * or *global_scale with MX_QUANT_STATIC_GLOBAL; per 16-element block the E4M3
+ * byte nearest to m/(6g) (ties to even, saturating at 448); elements take the
+ * E2M1 state nearest to x/(s*g), saturating at +-6.  The computed g is written
+ * to *out->global_scale.
+ *   x          device, x_dtype (MX_DT_F32 / MX_DT_BF16), row pitch ld_x elems
+ *   out        descriptor of the destination (device buffers caller-owned)
+ *   workspace  device scratch of mx_workspace_bytes(MX_OP_QUANTIZE, out)
+ *              bytes (0 for MXFP4 and for NVFP4 with MX_QUANT_STATIC_GLOBAL)
+ * Requires cols % k == 0 (else MX_ERR_UNSUPPORTED).  rows == 0 is a no-op.
+ * Inputs must be finite.
+ */
+int mx_quantize(const void *x, int32_t x_dtype, int64_t ld_x, const mx_tensor *out,
+                int32_t flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * mx_dequantize -- x_hat = q * S_block * S_global ("NVFP4 Architecture",
+ * section "1. The Dual-Level Mathematical Formulation", reconstruction
+ * equation).  MXFP4: q * 2^(E-127) (exact in fp32).  NVFP4:
+ * fp32(fp32(q * s) * g).  bf16 output is the round-to-nearest-even of that
+ * fp32 value.  y is device [in->rows, in->cols] with row pitch ld_y elements.
+ */
+int mx_dequantize(const mx_tensor *in, void *y, int32_t y_dtype, int64_t ld_y, void *stream);
+
+/*
+ * mx_gemm -- C[M, N] = A[M, K] . B[N, K]^T in native W4A4
+ * (Y = X . W, "NVFP4 Architecture", section "1. The Dual-Level Mathematical
+ * Formulation"; the block-scaled dot product with fp32 accumulation of
+ * section "2. Hardware-Managed Tensor Core Dot-Products").
+ *   MXFP4 x MXFP4: C = sum_b 2^(eA+eB) sum_{k in b} qA qB, fp32 accumulate.
+ *   NVFP4 x NVFP4: C = gA gB sum_b sA sB sum_{k in b} qA qB.
+ * Grouped form (groups >= 1): b holds `groups` stacked [N, K] matrices
+ * (b->rows == groups * N); rows [off[g], off[g+1]) of A and C use matrix g.
+ * `group_offsets` is a device int32 array of groups + 1 non-decreasing
+ * entries with off[0] = 0 and off[groups] = M (entries are clamped to [0, M]
+ * on the device, so malformed offsets cannot index out of bounds).
+ * Dynamic activation quantization (MXFP4 only): pass a == NULL and
+ * a_raw (bf16/fp32 [M, K], pitch lda_raw elements); A is quantized to MXFP4
+ * once (as mx_quantize would) into a_codes_out/a_scales_out if given, else
+ * into the workspace, then multiplied.
+ * c_dtype is MX_DT_F32 or MX_DT_BF16 (round-to-nearest-even), row pitch ldc.
+ * Requires K % 32 == 0 (MXFP4) or K % 16 == 0 (NVFP4).
+ */
+typedef struct mx_gemm_args {
+  int64_t M, N, K;
+  const mx_tensor *a;            /* quantized A [M, K], or NULL (dynamic)   */
+  const void *a_raw;             /* dynamic path: unquantized A            */
+  int32_t a_raw_dtype;           /* MX_DT_F32 / MX_DT_BF16                  */
+  int32_t groups;                /* 0: dense; >= 1: grouped                 */
+  int64_t lda_raw;               /* elements                                */
+  const mx_tensor *b;            /* [N, K] or [groups*N, K]                 */
+  const int32_t *group_offsets;  /* device int32 [groups + 1] (grouped)     */
+  void *c;                       /* device [M, N]                           */
+  int32_t c_dtype;
+  int32_t reserved;              /* must be 0 */
+  int64_t ldc;                   /* elements                                */
+  uint8_t *a_codes_out;          /* optional [M, K/2] (dynamic path)        */
+  uint8_t *a_scales_out;         /* optional [M, K/32] (dynamic path)       */
+  void *workspace;
+  size_t workspace_bytes;
+} mx_gemm_args;
+
+int mx_gemm(const mx_gemm_args *args, void *stream);
+
+/*
+ * mx_gemv -- W4A16 decode product y[M, N] = x[M, K] . W_hat[N, K]^T with bf16
+ * activations and MXFP4 weights dequantized in registers (no matrix cores):
+ * weights stay compressed, the arithmetic is 16-bit x dequantized weight with
+ * fp32 accumulation ("Extreme Quantization and Precision Engineering", section
+ * "Key points", W4A16).  1 <= M <= 16; x bf16 [M, K] pitch ld_x; y bf16
+ * [M, N] pitch ld_y.  Requires K % 32 == 0.
+ */
+int mx_gemv(const void *x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_tensor *w,
+            void *y, int32_t y_dtype, int64_t ld_y, void *stream);
+
+/* Scratch bytes that op needs: desc is an mx_tensor* (MX_OP_QUANTIZE, with
+   flags as in mx_quantize) or an mx_gemm_args* (MX_OP_GEMM). */
+size_t mx_workspace_bytes(int32_t op, const void *desc, int32_t flags);
+
+/* Static, never-NULL description of a status code. */
+const char *mx_status_string(int status);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int mx_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MX_H_ */

@@ -1,0 +1,240 @@
+"""Python binding of libmx (block-scaled FP4 quantization and GEMM on gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of libmx.so.
+PyTorch provides device memory and the current stream.  The functions carry
+the C names (mx_quantize, mx_dequantize, mx_gemm, mx_gemv, ...); the raw
+ctypes entry points are available as ``lib().mx_*``.
+
+There is no fallback: if libmx.so is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = [
+    "MXError", "MXTensor", "lib", "library_path", "MX_FMT_MXFP4", "MX_FMT_NVFP4", "MX_DT_F32", "MX_DT_BF16",
+    "MX_QUANT_STATIC_GLOBAL", "MX_OP_QUANTIZE", "MX_OP_GEMM", "STATUS", "CMxTensor", "CMxGemmArgs",
+    "empty_quantized", "mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemv", "mx_workspace_bytes",
+    "mx_status_string", "mx_version",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "libmx.so")
+
+MX_FMT_MXFP4, MX_FMT_NVFP4 = 0, 1
+MX_DT_F32, MX_DT_BF16 = 0, 1
+MX_QUANT_DEFAULT, MX_QUANT_STATIC_GLOBAL = 0, 1
+MX_OP_QUANTIZE, MX_OP_GEMM = 0, 1
+STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_ALIGN", -4: "MX_ERR_DTYPE",
+          -5: "MX_ERR_UNSUPPORTED", -6: "MX_ERR_HIP", -7: "MX_ERR_WORKSPACE", -8: "MX_ERR_FORMAT"}
+_FMT = {"mxfp4": MX_FMT_MXFP4, "nvfp4": MX_FMT_NVFP4}
+_BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_NVFP4: 16}
+
+
+class MXError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {STATUS.get(status, status)} ({mx_status_string(status)})")
+
+
+class CMxTensor(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_void_p)]
+
+
+class CMxGemmArgs(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("a", ctypes.POINTER(CMxTensor)), ("a_raw", ctypes.c_void_p), ("a_raw_dtype", ctypes.c_int32),
+                ("groups", ctypes.c_int32), ("lda_raw", ctypes.c_int64), ("b", ctypes.POINTER(CMxTensor)),
+                ("group_offsets", ctypes.c_void_p), ("c", ctypes.c_void_p), ("c_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("ldc", ctypes.c_int64), ("a_codes_out", ctypes.c_void_p),
+                ("a_scales_out", ctypes.c_void_p), ("workspace", ctypes.c_void_p),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmx.so (built in-tree by build.py); raises if it is missing."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is not built: run `python -m microscaling_fp4_quantization_mx_amd.build`"
+                               " (there is no CPU fallback)")
+        L = ctypes.CDLL(library_path)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        L.mx_quantize.argtypes = [vp, i32, i64, ctypes.POINTER(CMxTensor), i32, vp, sz, vp]
+        L.mx_quantize.restype = ctypes.c_int
+        L.mx_dequantize.argtypes = [ctypes.POINTER(CMxTensor), vp, i32, i64, vp]
+        L.mx_dequantize.restype = ctypes.c_int
+        L.mx_gemm.argtypes = [ctypes.POINTER(CMxGemmArgs), vp]
+        L.mx_gemm.restype = ctypes.c_int
+        L.mx_gemv.argtypes = [vp, i32, i64, i64, ctypes.POINTER(CMxTensor), vp, i32, i64, vp]
+        L.mx_gemv.restype = ctypes.c_int
+        L.mx_workspace_bytes.argtypes = [i32, vp, i32]
+        L.mx_workspace_bytes.restype = sz
+        L.mx_status_string.argtypes = [ctypes.c_int]
+        L.mx_status_string.restype = ctypes.c_char_p
+        L.mx_version.argtypes = []
+        L.mx_version.restype = ctypes.c_int
+        _LIB = L
+    return _LIB
+
+
+def mx_status_string(status: int) -> str:
+    return lib().mx_status_string(int(status)).decode()
+
+
+def mx_version() -> int:
+    return lib().mx_version()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise MXError(status, where)
+
+
+def _stream(torch, device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dt(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MX_DT_F32
+    if t.dtype == torch.bfloat16:
+        return MX_DT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+@dataclass
+class MXTensor:
+    """A quantized [rows, cols] tensor: packed codes, scale bytes and (NVFP4)
+    the per-tensor fp32 scale, all torch device tensors."""
+    fmt: int
+    rows: int
+    cols: int
+    codes: object          # uint8 [rows, cols/2]
+    scales: object         # uint8 [rows, cols/k]
+    global_scale: object = None   # float32 [1] (NVFP4)
+
+    def desc(self) -> CMxTensor:
+        return CMxTensor(self.fmt, 0, self.rows, self.cols, self.codes.data_ptr(), self.scales.data_ptr(),
+                         self.global_scale.data_ptr() if self.global_scale is not None else None)
+
+    @property
+    def block(self) -> int:
+        return _BLOCK[self.fmt]
+
+
+def empty_quantized(rows: int, cols: int, fmt="mxfp4", device="cuda", lead=()) -> MXTensor:
+    """Allocate an uninitialised quantized tensor (optionally with leading
+    dims, e.g. lead=(G,) for stacked expert weights: rows then means G*N)."""
+    import torch
+    f = _FMT[fmt] if isinstance(fmt, str) else fmt
+    k = _BLOCK[f]
+    codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=device)
+    scales = torch.empty(rows, cols // k, dtype=torch.uint8, device=device)
+    g = torch.ones(1, dtype=torch.float32, device=device) if f == MX_FMT_NVFP4 else None
+    return MXTensor(f, rows, cols, codes, scales, g)
+
+
+def mx_workspace_bytes(op: int, desc, flags: int = 0) -> int:
+    return int(lib().mx_workspace_bytes(op, ctypes.cast(ctypes.pointer(desc), ctypes.c_void_p), flags))
+
+
+def mx_quantize(x, fmt="mxfp4", out: MXTensor | None = None, static_global=None, workspace=None) -> MXTensor:
+    """Quantize a 2-D fp32/bf16 CUDA tensor (row pitch x.stride(0))."""
+    import torch
+    assert x.dim() == 2 and x.stride(1) == 1
+    rows, cols = x.shape
+    if out is None:
+        out = empty_quantized(rows, cols, fmt, x.device)
+    flags = MX_QUANT_DEFAULT
+    if static_global is not None:
+        out.global_scale.fill_(float(static_global))
+        flags = MX_QUANT_STATIC_GLOBAL
+    d = out.desc()
+    need = mx_workspace_bytes(MX_OP_QUANTIZE, d, flags)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() if workspace is not None else 0
+    _check(lib().mx_quantize(x.data_ptr(), _dt(x), x.stride(0), ctypes.byref(d), flags, ws_ptr, ws_bytes,
+                             _stream(torch, x.device)), "mx_quantize")
+    return out
+
+
+def mx_dequantize(t: MXTensor, dtype=None, out=None):
+    import torch
+    dtype = dtype or torch.float32
+    if out is None:
+        out = torch.empty(t.rows, t.cols, dtype=dtype, device=t.codes.device)
+    d = t.desc()
+    _check(lib().mx_dequantize(ctypes.byref(d), out.data_ptr(), _dt(out), out.stride(0),
+                               _stream(torch, out.device)), "mx_dequantize")
+    return out
+
+
+def mx_gemm(a, b: MXTensor, N: int | None = None, out_dtype=None, out=None, groups: int = 0, offsets=None,
+            a_codes_out=None, a_scales_out=None, workspace=None):
+    """C[M, N] = A . B^T.  a is an MXTensor (W4A4) or a raw fp32/bf16 tensor
+    (dynamic MXFP4 quantization inside the call).  Grouped: b holds `groups`
+    stacked [N, K] matrices and offsets is an int32 CUDA tensor [groups+1]."""
+    import torch
+    out_dtype = out_dtype or torch.bfloat16
+    if isinstance(a, MXTensor):
+        M, K = a.rows, a.cols
+        dev = a.codes.device
+    else:
+        M, K = a.shape
+        dev = a.device
+    if N is None:
+        N = b.rows // max(groups, 1)
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=dev)
+    bd = b.desc()
+    args = CMxGemmArgs()
+    args.M, args.N, args.K = M, N, K
+    if isinstance(a, MXTensor):
+        ad = a.desc()
+        args.a = ctypes.pointer(ad)
+    else:
+        assert a.stride(1) == 1
+        args.a = None
+        args.a_raw = a.data_ptr()
+        args.a_raw_dtype = _dt(a)
+        args.lda_raw = a.stride(0)
+        if a_codes_out is not None:
+            args.a_codes_out = a_codes_out.data_ptr()
+            args.a_scales_out = a_scales_out.data_ptr()
+    args.groups = groups
+    args.b = ctypes.pointer(bd)
+    args.group_offsets = offsets.data_ptr() if offsets is not None else None
+    args.c = out.data_ptr()
+    args.c_dtype = _dt(out)
+    args.ldc = out.stride(0)
+    need = mx_workspace_bytes(MX_OP_GEMM, args)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        args.workspace = workspace.data_ptr()
+        args.workspace_bytes = workspace.numel()
+    _check(lib().mx_gemm(ctypes.byref(args), _stream(torch, dev)), "mx_gemm")
+    return out
+
+
+def mx_gemv(x, w: MXTensor, out=None):
+    """W4A16: y[M, N] = x[M, K] (bf16) . dequant(w)[N, K]^T, bf16 out, M <= 16."""
+    import torch
+    M, K = x.shape
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=torch.bfloat16, device=x.device)
+    d = w.desc()
+    _check(lib().mx_gemv(x.data_ptr(), _dt(x), M, x.stride(0), ctypes.byref(d), out.data_ptr(), _dt(out),
+                         out.stride(0), _stream(torch, x.device)), "mx_gemv")
+    return out

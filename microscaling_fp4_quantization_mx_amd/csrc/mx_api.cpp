@@ -1,0 +1,204 @@
+// libmx C ABI: argument validation, workspace layout and kernel dispatch.
+// Every check runs on the host before any HIP call, so an invalid call
+// returns a negative status without touching the device.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "../../include/mx.h"
+#include "mx_kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 33;   // rows * cols limit (32-bit vector indices)
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr size_t kNvPartialBytes = 4096 * sizeof(uint32_t);
+
+inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline int block_of(int32_t fmt) { return fmt == MX_FMT_MXFP4 ? 32 : 16; }
+inline size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+inline int esize(int32_t dt) { return dt == MX_DT_F32 ? 4 : 2; }
+inline bool dtype_ok(int32_t dt) { return dt == MX_DT_F32 || dt == MX_DT_BF16; }
+
+// Descriptor checks common to every entry point.
+int check_tensor(const mx_tensor* t) {
+  if (!t) return MX_ERR_NULL;
+  if (t->fmt != MX_FMT_MXFP4 && t->fmt != MX_FMT_NVFP4) return MX_ERR_FORMAT;
+  if (t->reserved != 0) return MX_ERR_SHAPE;
+  if (t->rows < 0 || t->cols < 0 || t->rows > kMaxDim || t->cols > kMaxDim) return MX_ERR_SHAPE;
+  if (t->rows > 0 && t->cols > 0 && t->rows > kMaxElems / t->cols) return MX_ERR_SHAPE;
+  if (t->cols % block_of(t->fmt) != 0) return MX_ERR_UNSUPPORTED;
+  if (t->rows == 0 || t->cols == 0) return MX_OK;
+  if (!t->codes || !t->scales) return MX_ERR_NULL;
+  if (t->fmt == MX_FMT_NVFP4 && !t->global_scale) return MX_ERR_NULL;
+  if (!al16(t->codes) || !al16(t->scales)) return MX_ERR_ALIGN;
+  if (t->global_scale && (reinterpret_cast<uintptr_t>(t->global_scale) & 3u)) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+int check_dense_input(const void* x, int32_t dt, int64_t ld, int64_t rows, int64_t cols) {
+  if (!dtype_ok(dt)) return MX_ERR_DTYPE;
+  if (ld < cols) return MX_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return MX_OK;
+  if (!x) return MX_ERR_NULL;
+  if (!al16(x) || (ld * esize(dt)) % 16 != 0) return MX_ERR_ALIGN;
+  return MX_OK;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
+
+size_t dyn_a_bytes(int64_t M, int64_t K) { return round256((size_t)(M * K / 2)) + round256((size_t)(M * K / 32)); }
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_status_string(int status) {
+  switch (status) {
+    case MX_OK: return "MX_OK: success";
+    case MX_ERR_NULL: return "MX_ERR_NULL: a required pointer is NULL";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE: negative or inconsistent sizes or leading dimensions";
+    case MX_ERR_ALIGN: return "MX_ERR_ALIGN: pointer or row not 16-byte aligned";
+    case MX_ERR_DTYPE: return "MX_ERR_DTYPE: unknown or unsupported element type";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED: valid but not provided by this library";
+    case MX_ERR_HIP: return "MX_ERR_HIP: a HIP launch failed";
+    case MX_ERR_WORKSPACE: return "MX_ERR_WORKSPACE: workspace missing or too small";
+    case MX_ERR_FORMAT: return "MX_ERR_FORMAT: unknown format or mismatched operand formats";
+    default: return "unknown mx_status";
+  }
+}
+
+int mx_version(void) { return 10000; }
+
+size_t mx_workspace_bytes(int32_t op, const void* desc, int32_t flags) {
+  if (!desc) return 0;
+  if (op == MX_OP_QUANTIZE) {
+    const mx_tensor* t = static_cast<const mx_tensor*>(desc);
+    if (t->fmt == MX_FMT_NVFP4 && !(flags & MX_QUANT_STATIC_GLOBAL)) return kNvPartialBytes;
+    return 0;
+  }
+  if (op == MX_OP_GEMM) {
+    const mx_gemm_args* a = static_cast<const mx_gemm_args*>(desc);
+    if (!a->a && !(a->a_codes_out && a->a_scales_out) && a->M > 0 && a->K > 0) return dyn_a_bytes(a->M, a->K);
+    return 0;
+  }
+  return 0;
+}
+
+int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* out, int32_t flags, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  int st = check_tensor(out);
+  if (st) return st;
+  if (flags != MX_QUANT_DEFAULT && flags != MX_QUANT_STATIC_GLOBAL) return MX_ERR_UNSUPPORTED;
+  if (out->fmt == MX_FMT_MXFP4 && flags != MX_QUANT_DEFAULT) return MX_ERR_UNSUPPORTED;
+  st = check_dense_input(x, x_dtype, ld_x, out->rows, out->cols);
+  if (st) return st;
+  const bool dyn_nv = out->fmt == MX_FMT_NVFP4 && !(flags & MX_QUANT_STATIC_GLOBAL);
+  if (dyn_nv && (!workspace || workspace_bytes < kNvPartialBytes || !al16(workspace))) return MX_ERR_WORKSPACE;
+  if (out->rows == 0 || out->cols == 0) return MX_OK;
+  const int bf = x_dtype == MX_DT_BF16;
+  hipError_t e;
+  if (out->fmt == MX_FMT_MXFP4) {
+    e = mxk::launch_quant_mx(x, bf, ld_x, out->rows, out->cols, out->codes, out->scales, as_stream(stream));
+  } else {
+    e = mxk::launch_quant_nv(x, bf, ld_x, out->rows, out->cols, out->codes, out->scales, out->global_scale, !dyn_nv,
+                             static_cast<uint32_t*>(workspace), as_stream(stream));
+  }
+  return hip_status(e);
+}
+
+int mx_dequantize(const mx_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, void* stream) {
+  int st = check_tensor(in);
+  if (st) return st;
+  st = check_dense_input(y, y_dtype, ld_y, in->rows, in->cols);
+  if (st) return st;
+  if (in->rows == 0 || in->cols == 0) return MX_OK;
+  return hip_status(mxk::launch_dequant(in->fmt == MX_FMT_NVFP4, in->codes, in->scales, in->global_scale, in->rows,
+                                        in->cols, y, y_dtype == MX_DT_BF16, ld_y, as_stream(stream)));
+}
+
+int mx_gemm(const mx_gemm_args* a, void* stream) {
+  if (!a) return MX_ERR_NULL;
+  if (a->reserved != 0) return MX_ERR_SHAPE;
+  if (a->M < 0 || a->N < 0 || a->K < 0 || a->M > kMaxDim || a->N > kMaxDim || a->K > kMaxDim) return MX_ERR_SHAPE;
+  if (a->groups < 0) return MX_ERR_SHAPE;
+  int st = check_tensor(a->b);
+  if (st) return st;
+  const int32_t fmt = a->b->fmt;
+  if (a->b->cols != a->K) return MX_ERR_SHAPE;
+  if (a->groups == 0) {
+    if (a->b->rows != a->N) return MX_ERR_SHAPE;
+  } else {
+    if (a->b->rows != (int64_t)a->groups * a->N) return MX_ERR_SHAPE;
+    if (!a->group_offsets) return MX_ERR_NULL;
+    if (fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
+  }
+  if (!dtype_ok(a->c_dtype)) return MX_ERR_DTYPE;
+  if (a->ldc < a->N) return MX_ERR_SHAPE;
+  if (a->M > 0 && a->N > 0) {
+    if (!a->c) return MX_ERR_NULL;
+    if (!al16(a->c)) return MX_ERR_ALIGN;
+  }
+  const uint8_t* a_codes = nullptr;
+  const uint8_t* a_scales = nullptr;
+  const float* a_global = nullptr;
+  bool dynamic = false;
+  if (a->a) {
+    st = check_tensor(a->a);
+    if (st) return st;
+    if (a->a->fmt != fmt) return MX_ERR_FORMAT;
+    if (a->a->rows != a->M || a->a->cols != a->K) return MX_ERR_SHAPE;
+    a_codes = a->a->codes; a_scales = a->a->scales; a_global = a->a->global_scale;
+  } else {
+    if (fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;   // dynamic path quantizes A to MXFP4
+    st = check_dense_input(a->a_raw, a->a_raw_dtype, a->lda_raw, a->M, a->K);
+    if (st) return st;
+    if (a->M > kMaxElems / (a->K > 0 ? a->K : 1)) return MX_ERR_SHAPE;
+    dynamic = true;
+    if (a->a_codes_out || a->a_scales_out) {
+      if (!a->a_codes_out || !a->a_scales_out) return MX_ERR_NULL;
+      if (!al16(a->a_codes_out) || !al16(a->a_scales_out)) return MX_ERR_ALIGN;
+      a_codes = a->a_codes_out; a_scales = a->a_scales_out;
+    } else if (a->M > 0 && a->K > 0) {
+      const size_t need = dyn_a_bytes(a->M, a->K);
+      if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace)) return MX_ERR_WORKSPACE;
+      a_codes = static_cast<const uint8_t*>(a->workspace);
+      a_scales = static_cast<const uint8_t*>(a->workspace) + round256((size_t)(a->M * a->K / 2));
+    }
+  }
+  if (fmt == MX_FMT_NVFP4 && a->K % 32 != 0) return MX_ERR_UNSUPPORTED;
+  if (a->M == 0 || a->N == 0) return MX_OK;
+  hipStream_t s = as_stream(stream);
+  if (dynamic && a->K > 0) {
+    hipError_t e = mxk::launch_quant_mx(a->a_raw, a->a_raw_dtype == MX_DT_BF16, a->lda_raw, a->M, a->K,
+                                        const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), s);
+    if (e != hipSuccess) return MX_ERR_HIP;
+  }
+  const int cbf = a->c_dtype == MX_DT_BF16;
+  if (fmt == MX_FMT_MXFP4)
+    return hip_status(mxk::launch_gemm_mx(a_codes, a_scales, a->b->codes, a->b->scales, a->c, cbf, a->ldc, a->M, a->N,
+                                          a->K, a->groups, a->group_offsets, s));
+  return hip_status(mxk::launch_gemm_nv(a_codes, a_scales, a_global, a->b->codes, a->b->scales, a->b->global_scale,
+                                        a->c, cbf, a->ldc, a->M, a->N, a->K, s));
+}
+
+int mx_gemv(const void* x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_tensor* w, void* y, int32_t y_dtype,
+            int64_t ld_y, void* stream) {
+  int st = check_tensor(w);
+  if (st) return st;
+  if (x_dtype != MX_DT_BF16 || y_dtype != MX_DT_BF16) return MX_ERR_DTYPE;
+  if (w->fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
+  if (M < 0) return MX_ERR_SHAPE;
+  if (M > 16) return MX_ERR_UNSUPPORTED;
+  const int64_t N = w->rows, K = w->cols;
+  if (ld_y < N) return MX_ERR_SHAPE;
+  st = check_dense_input(x, x_dtype, ld_x, M, K);
+  if (st) return st;
+  if (M == 0 || N == 0) return MX_OK;
+  if (!y) return MX_ERR_NULL;
+  if (!al16(y)) return MX_ERR_ALIGN;
+  return hip_status(mxk::launch_gemv(x, ld_x, M, w->codes, w->scales, N, K, y, ld_y, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,22 @@
+// Host-side launchers of the gfx950 kernels (internal to libmx).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxk {
+hipError_t launch_quant_mx(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, hipStream_t st);
+int nv_partials_count(int64_t rows, int64_t cols, int xdt_bf16);
+hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, float* gscale, bool static_global, uint32_t* partial, hipStream_t st);
+hipError_t launch_dequant(bool nv, const uint8_t* codes, const uint8_t* scales, const float* gscale, int64_t rows,
+                          int64_t cols, void* y, bool out_bf16, int64_t ldy, hipStream_t st);
+hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                          const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                          int groups, const int32_t* offsets, hipStream_t st);
+hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                          const uint8_t* b_codes, const uint8_t* b_scales, const float* b_global, void* c, int c_bf16,
+                          int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st);
+hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
+                       int64_t K, void* y, int64_t ldy, hipStream_t st);
+}  // namespace mxk

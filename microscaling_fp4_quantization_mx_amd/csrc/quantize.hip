@@ -1,0 +1,350 @@
+// Block-scaled FP4 quantization and dequantization kernels for gfx950.
+//
+// MXFP4: "NVFP4 Architecture: Microscaling & 4-Bit LLMs on Blackwell",
+// section "1. The Dual-Level Mathematical Formulation" (equations S_block and
+// q_i, S_global = 1) with 32-element blocks ("How Microscaling FP4 (MXFP4)
+// Halves Memory Bandwidth", section "The Microscaling Breakthrough").
+// NVFP4: the same equations with 16-element blocks, an FP8 E4M3 block scale
+// and an fp32 per-tensor scale ("NVIDIA NVFP4 quantization", section "The
+// Physics of NVFP4").
+//
+// Streaming design: every lane owns one 16-byte input vector (4 fp32 or 8 bf16
+// elements); a wave covers 64 consecutive vectors, so each load instruction is
+// one contiguous 1 KiB request.  A block spans 2..8 lanes; its max |x| is an
+// integer max over the abs bit patterns reduced with xor shuffles.  Each lane
+// then writes its own packed codes (2 or 4 bytes), one lane per block the
+// scale byte.  Several vectors per lane are loaded before any is used so that
+// enough bytes are in flight to cover HBM latency.
+#include "mx_device.h"
+#include "mx_kernels.h"
+
+namespace mxk {
+
+constexpr int QT = 256;    // threads per workgroup
+constexpr int QU = 4;      // vectors per lane per iteration (loads in flight)
+
+// ---------------------------------------------------------------------------
+// MXFP4 quantize
+// ---------------------------------------------------------------------------
+// Vector v of the tensor: flat index v in [0, rows * cols / EPL).  With a
+// contiguous tensor (ld == cols) its elements sit at x + v * EPL; otherwise
+// row = v / vpr.
+template <typename TIn, bool CONTIG>
+__global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr,
+                                                 uint32_t nvec, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales) {
+  constexpr int EPL = 16 / (int)sizeof(TIn);  // elements per vector
+  constexpr int LPB = 32 / EPL;               // lanes per 32-element block
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave_global = (blockIdx.x * QT + threadIdx.x) >> 6;
+  const uint32_t nwaves = (gridDim.x * QT) >> 6;
+  for (uint32_t base = wave_global * (64 * QU); base < nvec; base += nwaves * (64 * QU)) {
+    u32x4 d[QU];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      uint32_t v = base + u * 64 + lane;
+      const TIn* p;
+      if (CONTIG) {
+        p = x + (size_t)v * EPL;
+      } else {
+        uint32_t r = v / vpr, c = v - r * vpr;
+        p = x + (size_t)r * ldx + (size_t)c * EPL;
+      }
+      d[u] = (v < nvec) ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const uint32_t v = base + u * 64 + lane;
+      float f[EPL];
+      if constexpr (EPL == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) f[i] = ffrom(d[u][i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[2 * i] = bf16_lo(d[u][i]);
+          f[2 * i + 1] = bf16_hi(d[u][i]);
+        }
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) am = max(am, fbits(f[i]) & 0x7fffffffu);
+#pragma unroll
+      for (int m = 1; m < LPB; m <<= 1) am = umax_xor(am, m);
+      const int e = mx_block_exp(am);
+      const float s = pow2f(e);
+      uint32_t out = 0;
+      out = cvt_fp4x2<0>(out, f[0], f[1], s);
+      out = cvt_fp4x2<1>(out, f[2], f[3], s);
+      if constexpr (EPL == 8) {
+        out = cvt_fp4x2<2>(out, f[4], f[5], s);
+        out = cvt_fp4x2<3>(out, f[6], f[7], s);
+      }
+      if (v < nvec) {
+        if constexpr (EPL == 4) {
+          reinterpret_cast<uint16_t*>(codes)[v] = (uint16_t)out;
+        } else {
+          reinterpret_cast<uint32_t*>(codes)[v] = out;
+        }
+        if ((lane & (LPB - 1)) == 0) scales[v / LPB] = (uint8_t)(e + 127);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4: tensor max |x| (partials per workgroup), then quantize
+// ---------------------------------------------------------------------------
+template <typename TIn, bool CONTIG>
+__global__ __launch_bounds__(QT) void k_absmax(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr, uint32_t nvec,
+                                               uint32_t* __restrict__ partial) {
+  constexpr int EPL = 16 / (int)sizeof(TIn);
+  __shared__ uint32_t red[QT / 64];
+  uint32_t am = 0;
+  for (uint32_t v = blockIdx.x * QT + threadIdx.x; v < nvec; v += gridDim.x * QT) {
+    const TIn* p;
+    if (CONTIG) {
+      p = x + (size_t)v * EPL;
+    } else {
+      uint32_t r = v / vpr, c = v - r * vpr;
+      p = x + (size_t)r * ldx + (size_t)c * EPL;
+    }
+    u32x4 d = *reinterpret_cast<const u32x4*>(p);
+    if constexpr (EPL == 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am = max(am, d[i] & 0x7fffffffu);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) am = max(am, max(d[i] & 0x7fffu, (d[i] >> 16) & 0x7fffu) << 16);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) am = umax_xor(am, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = red[0];
+    for (int i = 1; i < QT / 64; ++i) r = max(r, red[i]);
+    partial[blockIdx.x] = r;
+  }
+}
+
+// Per-tensor scale from the partial maxima: g = fp32(amax / 2688), 2688 being
+// 6 (largest E2M1 state) x 448 (largest E4M3 value), or 1 for an all-zero
+// tensor; the fp32 division is IEEE correctly rounded.
+__device__ __forceinline__ float nv_global_from_partials(const uint32_t* __restrict__ partial, int npart,
+                                                         uint32_t* red) {
+  uint32_t am = 0;
+  for (int i = threadIdx.x; i < npart; i += QT) am = max(am, partial[i]);
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) am = umax_xor(am, m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
+  __syncthreads();
+  uint32_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < QT / 64; ++i) r = max(r, red[i]);
+  return r == 0 ? 1.0f : ffrom(r) / 2688.0f;
+}
+
+template <typename TIn, bool CONTIG>
+__global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr,
+                                                 uint32_t nvec, uint8_t* __restrict__ codes,
+                                                 uint8_t* __restrict__ scales, float* __restrict__ gout,
+                                                 const uint32_t* __restrict__ partial, int npart) {
+  constexpr int EPL = 16 / (int)sizeof(TIn);
+  constexpr int LPB = 16 / EPL;  // lanes per 16-element block (4 or 2)
+  __shared__ uint32_t red[QT / 64];
+  float g;
+  if (partial) {
+    g = nv_global_from_partials(partial, npart, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gout = g;
+  } else {
+    g = *gout;  // static per-tensor scale supplied by the caller
+  }
+  const double six_g = 6.0 * (double)g;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave_global = (blockIdx.x * QT + threadIdx.x) >> 6;
+  const uint32_t nwaves = (gridDim.x * QT) >> 6;
+  for (uint32_t base = wave_global * (64 * QU); base < nvec; base += nwaves * (64 * QU)) {
+    u32x4 d[QU];
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      uint32_t v = base + u * 64 + lane;
+      const TIn* p;
+      if (CONTIG) {
+        p = x + (size_t)v * EPL;
+      } else {
+        uint32_t r = v / vpr, c = v - r * vpr;
+        p = x + (size_t)r * ldx + (size_t)c * EPL;
+      }
+      d[u] = (v < nvec) ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const uint32_t v = base + u * 64 + lane;
+      uint32_t xb[EPL];
+      if constexpr (EPL == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xb[i] = d[u][i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xb[2 * i] = d[u][i] << 16;
+          xb[2 * i + 1] = d[u][i] & 0xffff0000u;
+        }
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) am = max(am, xb[i] & 0x7fffffffu);
+#pragma unroll
+      for (int m = 1; m < LPB; m <<= 1) am = umax_xor(am, m);
+      // s_b = E4M3 nearest to amax / (6 g); unit y = s_b * g is exact in fp64.
+      const uint32_t sc = e4m3_rne_sat((double)ffrom(am) / six_g);
+      const double y = (double)e4m3_to_f32(sc) * (double)g;
+      uint32_t U[7];
+      nv_boundaries(y, U);
+      uint32_t out = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) out |= nv_code(xb[i], U) << (4 * i);
+      if (v < nvec) {
+        if constexpr (EPL == 4) {
+          reinterpret_cast<uint16_t*>(codes)[v] = (uint16_t)out;
+        } else {
+          reinterpret_cast<uint32_t*>(codes)[v] = out;
+        }
+        if ((lane & (LPB - 1)) == 0) scales[v / LPB] = (uint8_t)sc;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: each lane expands one 32-bit word of codes (8 elements).
+// ---------------------------------------------------------------------------
+template <bool NV, bool OUT_BF16, bool CONTIG>
+__global__ __launch_bounds__(QT) void k_dequant(const uint32_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                const float* __restrict__ gptr, uint32_t wpr, uint32_t nwords,
+                                                void* __restrict__ y, int64_t ldy) {
+  const float g = NV ? *gptr : 1.0f;
+  for (uint32_t w = blockIdx.x * QT + threadIdx.x; w < nwords; w += gridDim.x * QT) {
+    const uint32_t c = codes[w];
+    float f[8];
+    if (!NV) {
+      // 8 codes of one 32-element block; E8M0 byte -> power of two.
+      const float s = pow2f((int)scales[w >> 2] - 127);
+      f32x2 t;
+      t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, s, 0); f[0] = t.x; f[1] = t.y;
+      t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, s, 1); f[2] = t.x; f[3] = t.y;
+      t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, s, 2); f[4] = t.x; f[5] = t.y;
+      t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, s, 3); f[6] = t.x; f[7] = t.y;
+    } else {
+      // 8 codes of one 16-element block; fp32(fp32(q * s) * g).
+      const float s = e4m3_to_f32(scales[w >> 1]);
+      f32x2 t;
+      t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0); f[0] = t.x; f[1] = t.y;
+      t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1); f[2] = t.x; f[3] = t.y;
+      t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2); f[4] = t.x; f[5] = t.y;
+      t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3); f[6] = t.x; f[7] = t.y;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[i] = (f[i] * s) * g;
+    }
+    size_t off;  // element offset of the first of the 8 outputs
+    if (CONTIG) {
+      off = (size_t)w * 8;
+    } else {
+      uint32_t r = w / wpr, cw = w - r * wpr;
+      off = (size_t)r * ldy + (size_t)cw * 8;
+    }
+    if (OUT_BF16) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(f[2 * i]) | (f32_to_bf16_rne(f[2 * i + 1]) << 16);
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(y) + off) = o;
+    } else {
+      f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + off);
+      dst[0] = f32x4{f[0], f[1], f[2], f[3]};
+      dst[1] = f32x4{f[4], f[5], f[6], f[7]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+static int grid_for(uint64_t work_items, int per_block) {
+  uint64_t g = (work_items + per_block - 1) / per_block;
+  const uint64_t cap = 256 * 16;  // 16 workgroups per CU is plenty for a grid-stride loop
+  if (g > cap) g = cap;
+  return (int)(g ? g : 1);
+}
+
+hipError_t launch_quant_mx(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, hipStream_t st) {
+  const int epl = xdt_bf16 ? 8 : 4;
+  const uint32_t vpr = (uint32_t)(cols / epl);
+  const uint32_t nvec = (uint32_t)(rows * cols / epl);
+  const bool contig = (ldx == cols);
+  const int grid = grid_for(nvec, QT * QU);
+  if (xdt_bf16) {
+    if (contig)
+      hipLaunchKernelGGL((k_quant_mx<uint16_t, true>), dim3(grid), dim3(QT), 0, st, (const uint16_t*)x, ldx, vpr, nvec, codes, scales);
+    else
+      hipLaunchKernelGGL((k_quant_mx<uint16_t, false>), dim3(grid), dim3(QT), 0, st, (const uint16_t*)x, ldx, vpr, nvec, codes, scales);
+  } else {
+    if (contig)
+      hipLaunchKernelGGL((k_quant_mx<float, true>), dim3(grid), dim3(QT), 0, st, (const float*)x, ldx, vpr, nvec, codes, scales);
+    else
+      hipLaunchKernelGGL((k_quant_mx<float, false>), dim3(grid), dim3(QT), 0, st, (const float*)x, ldx, vpr, nvec, codes, scales);
+  }
+  return hipGetLastError();
+}
+
+int nv_partials_count(int64_t rows, int64_t cols, int xdt_bf16) {
+  const int epl = xdt_bf16 ? 8 : 4;
+  return grid_for((uint64_t)(rows * cols / epl), QT * 4);
+}
+
+hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
+                           uint8_t* scales, float* gscale, bool static_global, uint32_t* partial, hipStream_t st) {
+  const int epl = xdt_bf16 ? 8 : 4;
+  const uint32_t vpr = (uint32_t)(cols / epl);
+  const uint32_t nvec = (uint32_t)(rows * cols / epl);
+  const bool contig = (ldx == cols);
+  int npart = 0;
+  if (!static_global) {
+    npart = nv_partials_count(rows, cols, xdt_bf16);
+#define MX_ABSMAX(T, C) hipLaunchKernelGGL((k_absmax<T, C>), dim3(npart), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, partial)
+    if (xdt_bf16) { if (contig) MX_ABSMAX(uint16_t, true); else MX_ABSMAX(uint16_t, false); }
+    else { if (contig) MX_ABSMAX(float, true); else MX_ABSMAX(float, false); }
+#undef MX_ABSMAX
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int grid = grid_for(nvec, QT * QU);
+  const uint32_t* pp = static_global ? nullptr : partial;
+#define MX_QNV(T, C) hipLaunchKernelGGL((k_quant_nv<T, C>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales, gscale, pp, npart)
+  if (xdt_bf16) { if (contig) MX_QNV(uint16_t, true); else MX_QNV(uint16_t, false); }
+  else { if (contig) MX_QNV(float, true); else MX_QNV(float, false); }
+#undef MX_QNV
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(bool nv, const uint8_t* codes, const uint8_t* scales, const float* gscale, int64_t rows,
+                          int64_t cols, void* y, bool out_bf16, int64_t ldy, hipStream_t st) {
+  const uint32_t wpr = (uint32_t)(cols / 8);
+  const uint32_t nwords = (uint32_t)(rows * cols / 8);
+  const bool contig = (ldy == cols);
+  const int grid = grid_for(nwords, QT * 4);
+#define MX_DQ(NVF, B, C) hipLaunchKernelGGL((k_dequant<NVF, B, C>), dim3(grid), dim3(QT), 0, st, (const uint32_t*)codes, scales, gscale, wpr, nwords, y, ldy)
+  if (nv) {
+    if (out_bf16) { if (contig) MX_DQ(true, true, true); else MX_DQ(true, true, false); }
+    else { if (contig) MX_DQ(true, false, true); else MX_DQ(true, false, false); }
+  } else {
+    if (out_bf16) { if (contig) MX_DQ(false, true, true); else MX_DQ(false, true, false); }
+    else { if (contig) MX_DQ(false, false, true); else MX_DQ(false, false, false); }
+  }
+#undef MX_DQ
+  return hipGetLastError();
+}
+
+}  // namespace mxk

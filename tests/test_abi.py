@@ -1,0 +1,187 @@
+"""C-ABI tests that need no GPU: libmx.so loads, exports every function that
+include/mx.h declares, and rejects invalid arguments on the host with the
+documented status codes before any HIP call (fake, never-dereferenced
+pointers are enough for that)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import microscaling_fp4_quantization_mx_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "mx.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"\b(mx_[a-z_]+)\s*\(", src)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function():
+    L = mx.lib()
+    names = header_functions()
+    assert {"mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemv", "mx_workspace_bytes",
+            "mx_status_string", "mx_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_dynamic_symbols_are_c_abi():
+    out = os.popen(f"nm -D --defined-only {mx.library_path}").read()
+    for n in header_functions():
+        assert re.search(rf"\bT {n}$", out, re.M), n
+
+
+def test_status_strings_and_version():
+    for s in range(-8, 1):
+        assert mx.mx_status_string(s).startswith(mx.STATUS[s])
+    assert "unknown" in mx.mx_status_string(-99)
+    assert mx.mx_version() >= 10000
+
+
+def T(fmt=0, rows=64, cols=256, codes=FAKE, scales=FAKE, g=None):
+    return mx.CMxTensor(fmt, 0, rows, cols, codes, scales, g)
+
+
+def quant(x=FAKE, dt=0, ld=256, t=None, flags=0, ws=None, wsb=0):
+    t = t or T()
+    return mx.lib().mx_quantize(x, dt, ld, ctypes.byref(t), flags, ws, wsb, None)
+
+
+def test_quantize_validation():
+    L = mx.lib()
+    assert L.mx_quantize(FAKE, 0, 256, None, 0, None, 0, None) == -1           # NULL descriptor
+    assert quant(x=None) == -1                                                  # NULL input
+    assert quant(t=T(codes=None)) == -1
+    assert quant(t=T(fmt=7)) == -8                                              # unknown format
+    assert quant(dt=5) == -4                                                    # unknown dtype
+    assert quant(t=T(cols=48)) == -5                                            # cols % 32 != 0
+    assert quant(t=T(fmt=1, cols=40, g=FAKE)) == -5                             # cols % 16 != 0
+    assert quant(ld=100) == -2                                                  # ld < cols
+    assert quant(t=T(rows=-1)) == -2
+    assert quant(x=FAKE + 4) == -3                                              # misaligned input
+    assert quant(ld=257) == -3                                                  # misaligned rows
+    assert quant(t=T(codes=FAKE + 8)) == -3
+    assert quant(flags=1) == -5                                                 # static scale: NVFP4 only
+    assert quant(t=T(fmt=1, g=None)) == -1                                      # NVFP4 needs global scale
+    assert quant(t=T(fmt=1, g=FAKE)) == -7                                      # no workspace
+    assert quant(t=T(fmt=1, g=FAKE), ws=FAKE, wsb=16) == -7                     # too small
+    assert quant(t=T(rows=0)) == 0                                              # empty: no-op
+    assert quant(t=T(cols=0), x=None) == 0
+
+
+def test_workspace_query():
+    L = mx.lib()
+    t = T(fmt=1, g=FAKE)
+    assert L.mx_workspace_bytes(0, ctypes.cast(ctypes.pointer(t), ctypes.c_void_p), 0) >= 4 * 256
+    assert L.mx_workspace_bytes(0, ctypes.cast(ctypes.pointer(t), ctypes.c_void_p), 1) == 0
+    t0 = T()
+    assert L.mx_workspace_bytes(0, ctypes.cast(ctypes.pointer(t0), ctypes.c_void_p), 0) == 0
+    args = mx.CMxGemmArgs()
+    args.M, args.N, args.K = 100, 64, 256
+    need = L.mx_workspace_bytes(1, ctypes.cast(ctypes.pointer(args), ctypes.c_void_p), 0)
+    assert need >= 100 * 256 // 2 + 100 * 256 // 32
+    assert L.mx_workspace_bytes(1, None, 0) == 0
+
+
+def gemm_args(M=64, N=128, K=256, a=True, fmt=0, groups=0, **kw):
+    args = mx.CMxGemmArgs()
+    args.M, args.N, args.K = M, N, K
+    b = T(fmt, N * max(groups, 1), K, g=FAKE if fmt else None)
+    args._keep = [b]
+    args.b = ctypes.pointer(b)
+    if a:
+        at = T(fmt, M, K, g=FAKE if fmt else None)
+        args._keep.append(at)
+        args.a = ctypes.pointer(at)
+    args.groups = groups
+    args.c = FAKE
+    args.c_dtype = 1
+    args.ldc = N
+    for k, v in kw.items():
+        setattr(args, k, v)
+    return args
+
+
+def call_gemm(args):
+    return mx.lib().mx_gemm(ctypes.byref(args), None)
+
+
+def test_gemm_validation():
+    L = mx.lib()
+    assert L.mx_gemm(None, None) == -1
+    a = gemm_args()
+    a.b = None
+    assert call_gemm(a) == -1
+    assert call_gemm(gemm_args(c=None)) == -1
+    assert call_gemm(gemm_args(c=FAKE + 2)) == -3
+    assert call_gemm(gemm_args(ldc=10)) == -2
+    assert call_gemm(gemm_args(c_dtype=9)) == -4
+    assert call_gemm(gemm_args(M=-1)) == -2
+    assert call_gemm(gemm_args(reserved=1)) == -2
+    bad = gemm_args()
+    bad.b.contents.cols = 128                                 # K mismatch
+    assert call_gemm(bad) == -2
+    mism = gemm_args()
+    mism.a.contents.fmt = 1
+    mism.a.contents.global_scale = FAKE
+    assert call_gemm(mism) == -8                              # A NVFP4, B MXFP4
+    assert call_gemm(gemm_args(groups=2)) == -1               # grouped without offsets
+    assert call_gemm(gemm_args(groups=2, fmt=1, group_offsets=FAKE)) == -5
+    assert call_gemm(gemm_args(K=48)) == -5                   # K % 32
+    assert call_gemm(gemm_args(fmt=1, K=48)) == -5            # NVFP4 GEMM needs K % 32 == 0
+    # dynamic activation path
+    d = gemm_args(a=False, a_raw=FAKE, a_raw_dtype=1, lda_raw=256)
+    assert call_gemm(d) == -7                                 # no workspace
+    d = gemm_args(a=False, a_raw=FAKE, a_raw_dtype=1, lda_raw=256, a_codes_out=FAKE)
+    assert call_gemm(d) == -1                                 # codes_out without scales_out
+    d = gemm_args(a=False, a_raw=None, a_raw_dtype=1, lda_raw=256)
+    assert call_gemm(d) == -1
+    d = gemm_args(a=False, a_raw=FAKE, a_raw_dtype=3, lda_raw=256)
+    assert call_gemm(d) == -4
+    d = gemm_args(a=False, fmt=1, a_raw=FAKE, a_raw_dtype=1, lda_raw=256)
+    assert call_gemm(d) == -5                                 # dynamic NVFP4 not provided
+    assert call_gemm(gemm_args(M=0)) == 0                     # empty: no-op
+    assert call_gemm(gemm_args(N=0, ldc=0)) == 0
+
+
+def test_gemv_validation():
+    L = mx.lib()
+    w = T(0, 512, 256)
+
+    def gv(x=FAKE, xdt=1, M=1, ldx=256, w=w, y=FAKE, ydt=1, ldy=512):
+        return L.mx_gemv(x, xdt, M, ldx, ctypes.byref(w) if w is not None else None, y, ydt, ldy, None)
+
+    assert gv(w=None) == -1
+    assert gv(x=None) == -1
+    assert gv(y=None) == -1
+    assert gv(xdt=0) == -4                                    # activations must be bf16
+    assert gv(ydt=0) == -4
+    assert gv(M=17) == -5
+    assert gv(M=-1) == -2
+    assert gv(ldx=100) == -2
+    assert gv(ldx=260) == -3
+    assert gv(ldy=100) == -2
+    assert gv(w=T(1, 512, 256, g=FAKE)) == -5                 # NVFP4 weights not provided
+    assert gv(M=0) == 0
+
+
+def test_dequantize_validation():
+    L = mx.lib()
+    t = T()
+    assert L.mx_dequantize(None, FAKE, 0, 256, None) == -1
+    assert L.mx_dequantize(ctypes.byref(t), None, 0, 256, None) == -1
+    assert L.mx_dequantize(ctypes.byref(t), FAKE, 2, 256, None) == -4
+    assert L.mx_dequantize(ctypes.byref(t), FAKE, 0, 255, None) == -2
+    assert L.mx_dequantize(ctypes.byref(t), FAKE + 4, 0, 256, None) == -3
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(mx, "_LIB", None)
+    monkeypatch.setattr(mx, "library_path", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        mx.lib()

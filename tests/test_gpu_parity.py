@@ -1,0 +1,405 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Codes, scale bytes and per-tensor scales must match bit
+for bit; GEMM / GEMV outputs must lie within 1e-5 * sum_k |a||b| of the
+oracle's fp64-accumulated result (plus one bf16 ulp of the reference value
+for bf16 outputs).  Small cases cover several tiles and ragged tails; the
+full-size workloads run in the launch configuration the benchmark uses and
+are checked on sampled outputs."""
+import numpy as np
+import pytest
+import torch
+
+import microscaling_fp4_quantization_mx_amd as mx
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def announce(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run with -m 'not gpu' on CPU)")
+    mx.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def dev(x, dtype=torch.float32):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dtype).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def bf16_values(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def assert_within(y_gpu, y_ref, tol, what):
+    err = np.abs(y_gpu.astype(np.float64) - y_ref.astype(np.float64))
+    bad = err > tol
+    if bad.any():
+        i = np.argwhere(bad)[0]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside tolerance; first at {tuple(i)}: "
+                             f"gpu={y_gpu[tuple(i)]} ref={y_ref[tuple(i)]} tol={tol[tuple(i)]}")
+    announce(f"{what}: max err / tol = {(err / np.maximum(tol, 1e-300)).max():.3g}")
+
+
+def mx_quant_gpu(x_np, dtype, fmt="mxfp4", ld_pad=0, static_global=None):
+    rows, cols = x_np.shape
+    xt = torch.zeros(rows, cols + ld_pad, dtype=dtype, device=DEV)
+    xt[:, :cols] = dev(x_np, dtype)
+    view = xt[:, :cols]
+    t = mx.mx_quantize(view, fmt=fmt, static_global=static_global)
+    return t
+
+
+# ------------------------------------------------------------------ quantize
+QSHAPES = [(64, 256), (256, 256), (3, 96), (257, 1024), (1, 32), (130, 4128)]
+
+
+@pytest.mark.parametrize("shape", QSHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("ld_pad", [0, 32])
+def test_quantize_mxfp4_bit_exact(shape, dtype, ld_pad):
+    announce(f"quantize mxfp4 shape={shape} dtype={dtype} ld_pad={ld_pad}")
+    rng = np.random.default_rng(shape[0] * 7 + shape[1])
+    x = (rng.standard_normal(shape) * np.exp2(rng.integers(-12, 12, size=(shape[0], 1)))).astype(np.float32)
+    x[:, ::37] *= 60.0
+    if dtype == torch.bfloat16:
+        x = bf16_values(x)
+    t = mx_quant_gpu(x, dtype, ld_pad=ld_pad)
+    rc, rs = O.mxfp4_quantize(x)
+    assert np.array_equal(host(t.scales), rs)
+    assert np.array_equal(host(t.codes), rc)
+
+
+def exhaustive_bf16_blocks():
+    pats = np.arange(1 << 16, dtype=np.uint32)
+    vals = (pats << 16).view(np.float32)
+    vals = vals[np.isfinite(vals)]
+    n = vals.size
+    d = np.arange(n) % 6 - 1
+    mag = np.abs(vals).astype(np.float64)
+    fl = np.floor(np.log2(np.where(mag > 0, mag, 1.0))).astype(np.int64)
+    e_anchor = np.clip(fl + d, -29, 125)
+    anchor = (6.0 * np.exp2(e_anchor.astype(np.float64))).astype(np.float32)
+    x = np.zeros((n, 64), np.float32)
+    x[:, 0] = vals
+    x[:, 32] = vals
+    x[:, 33] = anchor
+    return x
+
+
+def test_quantize_mxfp4_exhaustive_bf16_sweep():
+    """Every finite bf16 bit pattern, alone in a block and in an anchored block
+    (input values kept below 1.5 * 2^127 by construction), bf16 and fp32 input."""
+    x = exhaustive_bf16_blocks()
+    x = x[np.abs(x).max(axis=1) <= 1.5 * 2.0 ** 127]
+    rc, rs = O.mxfp4_quantize(x)
+    for dtype in (torch.bfloat16, torch.float32):
+        announce(f"exhaustive bf16 sweep rows={x.shape[0]} dtype={dtype}")
+        t = mx_quant_gpu(x, dtype)
+        assert np.array_equal(host(t.scales), rs)
+        assert np.array_equal(host(t.codes), rc)
+
+
+def test_quantize_mxfp4_special_values():
+    announce("quantize mxfp4 special values")
+    vals = [0.0, -0.0, 1e-45, -1e-45, 1e-39, 6e-9, 1e-8, 1.1e-8, 1e30, -3e38, 1.5 * 2.0 ** 127]
+    for t_ in [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]:
+        for j in (-20, 0, 9):
+            c = np.float32(t_ * 2.0 ** j)
+            vals += [c, np.nextafter(c, np.float32(0)), np.nextafter(c, np.float32(np.inf))]
+    v = np.array(vals, np.float32)
+    x = np.zeros((len(v), 64), np.float32)
+    x[:, 0] = v
+    x[:, 32] = v
+    x[:, 33] = np.float32(6.0)
+    x[:, 34] = -np.float32(0.0)
+    x = x[np.abs(x).max(axis=1) <= 1.5 * 2.0 ** 127]
+    rc, rs = O.mxfp4_quantize(x)
+    t = mx_quant_gpu(x, torch.float32)
+    assert np.array_equal(host(t.scales), rs)
+    assert np.array_equal(host(t.codes), rc)
+
+
+NVSHAPES = [(64, 256), (3, 48), (257, 1024), (100, 4112)]
+
+
+@pytest.mark.parametrize("shape", NVSHAPES)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_nvfp4_bit_exact(shape, dtype):
+    announce(f"quantize nvfp4 shape={shape} dtype={dtype}")
+    rng = np.random.default_rng(shape[0] * 11 + shape[1])
+    x = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+    x[:, ::29] *= 50.0
+    x[shape[0] // 2, :16] *= np.float32(1e-5)        # tiny block: E4M3 subnormal / zero scale
+    if dtype == torch.bfloat16:
+        x = bf16_values(x)
+    rc, rs, rg = O.nvfp4_quantize(x)
+    for ld_pad in (0, 16):
+        t = mx_quant_gpu(x, dtype, fmt="nvfp4", ld_pad=ld_pad)
+        assert host(t.global_scale)[0] == rg
+        assert np.array_equal(host(t.scales), rs)
+        assert np.array_equal(host(t.codes), rc)
+
+
+def test_quantize_nvfp4_static_global_and_zero_tensor():
+    announce("quantize nvfp4 static global scale / all-zero tensor")
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((40, 160)).astype(np.float32)
+    g = np.float32(0.0031)
+    rc, rs, _ = O.nvfp4_quantize(x, global_scale=g)
+    t = mx_quant_gpu(x, torch.float32, fmt="nvfp4", static_global=float(g))
+    assert host(t.global_scale)[0] == g
+    assert np.array_equal(host(t.scales), rs)
+    assert np.array_equal(host(t.codes), rc)
+    z = np.zeros((8, 64), np.float32)
+    z[3, 5] = -0.0
+    rc, rs, rg = O.nvfp4_quantize(z)
+    t = mx_quant_gpu(z, torch.float32, fmt="nvfp4")
+    assert host(t.global_scale)[0] == rg == 1.0
+    assert np.array_equal(host(t.scales), rs)
+    assert np.array_equal(host(t.codes), rc)
+
+
+# ---------------------------------------------------------------- dequantize
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_dequantize_parity(fmt, odt):
+    announce(f"dequantize fmt={fmt} out={odt}")
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((67, 512)) * np.exp2(rng.integers(-8, 8, size=(67, 1)))).astype(np.float32)
+    t = mx_quant_gpu(x, torch.float32, fmt=fmt)
+    if fmt == "mxfp4":
+        ref = O.dequantize("mxfp4", host(t.codes), host(t.scales))
+    else:
+        ref = O.dequantize("nvfp4", host(t.codes), host(t.scales), host(t.global_scale)[0])
+    if odt == torch.bfloat16:
+        ref = O.round_to_bf16(ref)
+    for ld_pad in (0, 64):
+        out = torch.zeros(67, 512 + ld_pad, dtype=odt, device=DEV)
+        mx.mx_dequantize(t, out=out[:, :512])
+        got = out[:, :512].float().cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+# --------------------------------------------------------------------- GEMM
+def gemm_case(M, N, K, fmt, out_dtype, seed, x_scale=1.0, w_sigma=1.0, outlier=50.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((M, K)).astype(np.float32) * np.float32(x_scale)
+    if K:
+        x[:, rng.choice(K, size=max(1, K // 1000), replace=False)] *= np.float32(outlier)
+    w = (rng.standard_normal((N, K)) * w_sigma).astype(np.float32)
+    a = mx_quant_gpu(x, torch.float32, fmt=fmt)
+    b = mx_quant_gpu(w, torch.float32, fmt=fmt)
+    if fmt == "mxfp4":
+        ra, rsa = O.mxfp4_quantize(x)
+        rb, rsb = O.mxfp4_quantize(w)
+        assert np.array_equal(host(a.codes), ra) and np.array_equal(host(a.scales), rsa)
+        assert np.array_equal(host(b.codes), rb) and np.array_equal(host(b.scales), rsb)
+        ah, bh = O.dequantize("mxfp4", ra, rsa), O.dequantize("mxfp4", rb, rsb)
+    else:
+        ra, rsa, ga = O.nvfp4_quantize(x)
+        rb, rsb, gb = O.nvfp4_quantize(w)
+        assert np.array_equal(host(a.codes), ra) and np.array_equal(host(a.scales), rsa)
+        assert np.array_equal(host(b.codes), rb) and np.array_equal(host(b.scales), rsb)
+        ah, bh = O.dequantize("nvfp4", ra, rsa, ga), O.dequantize("nvfp4", rb, rsb, gb)
+    y = mx.mx_gemm(a, b, out_dtype=out_dtype)
+    o = "bf16" if out_dtype == torch.bfloat16 else "f32"
+    yref = O.gemm(ah, bh, out=o)
+    tol = O.gemm_tolerance(ah, bh, yref, out=o)
+    return host(y.float()), yref, tol, (a, b)
+
+
+GEMM_CASES = [(64, 256, 256), (100, 70, 96), (1, 1, 32), (300, 520, 384), (257, 513, 1056), (512, 256, 4096)]
+
+
+@pytest.mark.parametrize("mnk", GEMM_CASES)
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_gemm_mxfp4_parity(mnk, odt):
+    M, N, K = mnk
+    announce(f"gemm mxfp4 M={M} N={N} K={K} out={odt}")
+    y, yref, tol, _ = gemm_case(M, N, K, "mxfp4", odt, seed=M + N + K)
+    assert_within(y, yref, tol, f"mxfp4 gemm {mnk}")
+
+
+def test_gemm_mxfp4_config_small_workload():
+    """The 64x256x256 workload: A with one outlier channel x50, A and B
+    ~N(0,1), fp32 accumulate and output."""
+    announce("gemm mxfp4 64x256x256 workload")
+    d = W.make(W.C1)
+    a = mx_quant_gpu(d["x"], torch.float32)
+    b = mx_quant_gpu(d["w"], torch.float32)
+    ra, rsa = O.mxfp4_quantize(d["x"])
+    rb, rsb = O.mxfp4_quantize(d["w"])
+    assert np.array_equal(host(a.codes), ra) and np.array_equal(host(a.scales), rsa)
+    assert np.array_equal(host(b.codes), rb) and np.array_equal(host(b.scales), rsb)
+    y = host(mx.mx_gemm(a, b, out_dtype=torch.float32))
+    ah, bh = O.dequantize("mxfp4", ra, rsa), O.dequantize("mxfp4", rb, rsb)
+    yref = O.gemm(ah, bh)
+    assert_within(y, yref, O.gemm_tolerance(ah, bh), "64x256x256 workload")
+
+
+@pytest.mark.parametrize("mnk", [(64, 256, 256), (100, 70, 96), (300, 520, 384), (257, 300, 1056)])
+@pytest.mark.parametrize("odt", [torch.float32, torch.bfloat16])
+def test_gemm_nvfp4_parity(mnk, odt):
+    M, N, K = mnk
+    announce(f"gemm nvfp4 M={M} N={N} K={K} out={odt}")
+    y, yref, tol, _ = gemm_case(M, N, K, "nvfp4", odt, seed=3 * M + N + K, w_sigma=0.02)
+    assert_within(y, yref, tol, f"nvfp4 gemm {mnk}")
+
+
+def test_gemm_deterministic():
+    announce("gemm determinism")
+    _, _, _, (a, b) = gemm_case(300, 520, 384, "mxfp4", torch.bfloat16, seed=9)
+    y1 = mx.mx_gemm(a, b, out_dtype=torch.bfloat16)
+    y2 = mx.mx_gemm(a, b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("offs", [[0, 100, 100, 300], [0, 0, 256, 513], [0, 1, 2, 3]])
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float32])
+def test_grouped_dynamic_gemm(offs, xdt):
+    G, N, K = 3, 96, 288
+    T = offs[-1]
+    announce(f"grouped dynamic gemm offsets={offs} xdt={xdt}")
+    rng = np.random.default_rng(T + N)
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    x[:, 7] *= 40
+    if xdt == torch.bfloat16:
+        x = bf16_values(x)
+    w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+    wq = mx_quant_gpu(w.reshape(G * N, K), torch.float32)
+    wc = host(wq.codes).reshape(G, N, K // 2)
+    ws = host(wq.scales).reshape(G, N, K // 32)
+    yref, ac, as_ = O.grouped_gemm(x, np.array(offs), wc, ws)
+    offsets = torch.tensor(offs, dtype=torch.int32, device=DEV)
+    acodes = torch.empty(T, K // 2, dtype=torch.uint8, device=DEV)
+    ascales = torch.empty(T, K // 32, dtype=torch.uint8, device=DEV)
+    y = mx.mx_gemm(dev(x, xdt), wq, N=N, out_dtype=torch.bfloat16, groups=G, offsets=offsets,
+                   a_codes_out=acodes, a_scales_out=ascales)
+    assert np.array_equal(host(acodes), ac) and np.array_equal(host(ascales), as_)
+    y = host(y.float())
+    tol = np.zeros_like(yref, dtype=np.float64)
+    for g in range(G):
+        r0, r1 = offs[g], offs[g + 1]
+        if r1 > r0:
+            ah = O.dequantize("mxfp4", ac[r0:r1], as_[r0:r1])
+            bh = O.dequantize("mxfp4", wc[g], ws[g])
+            tol[r0:r1] = O.gemm_tolerance(ah, bh, yref[r0:r1], out="bf16")
+    assert_within(y, yref, tol, f"grouped {offs}")
+    # the same call through the workspace (no side outputs)
+    y2 = mx.mx_gemm(dev(x, xdt), wq, N=N, out_dtype=torch.bfloat16, groups=G, offsets=offsets)
+    assert np.array_equal(host(y2.float()), y)
+
+
+# --------------------------------------------------------------------- GEMV
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+@pytest.mark.parametrize("NK", [(300, 4096), (64, 96), (17, 8192)])
+def test_gemv_parity(M, NK):
+    N, K = NK
+    announce(f"gemv M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 1000 + N)
+    x = bf16_values(rng.standard_normal((M, K)).astype(np.float32) * 3)
+    w = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    wq = mx_quant_gpu(w, torch.float32)
+    rc, rs = O.mxfp4_quantize(w)
+    assert np.array_equal(host(wq.codes), rc)
+    y = host(mx.mx_gemv(dev(x, torch.bfloat16), wq).float())
+    yref = O.gemv(x, rc, rs)
+    wh = O.dequantize("mxfp4", rc, rs)
+    assert_within(y, yref, O.gemm_tolerance(x, wh, yref, out="bf16"), f"gemv M={M} N={N} K={K}")
+
+
+# ------------------------------------------------- full-size workloads (sampled)
+def _sample(n, k, seed):
+    return np.sort(np.random.default_rng(seed).choice(n, size=min(n, k), replace=False))
+
+
+def test_full_gemv_8192():
+    d = W.make(W.C2)
+    announce("full W4A16 GEMV N=K=8192, M=1/8/16")
+    wq = mx_quant_gpu(d["w"], torch.float32)
+    rows = _sample(8192, 48, 1)
+    rc, rs = O.mxfp4_quantize(d["w"][rows])
+    assert np.array_equal(host(wq.codes)[rows], rc) and np.array_equal(host(wq.scales)[rows], rs)
+    wh = O.dequantize("mxfp4", rc, rs)
+    for M in W.GEMV_M:
+        x = d["x"][:M]
+        y = host(mx.mx_gemv(dev(x, torch.bfloat16), wq).float())[:, rows]
+        yref = O.gemm(x, wh, out="bf16")
+        assert_within(y, yref, O.gemm_tolerance(x, wh, yref, out="bf16"), f"full gemv M={M}")
+
+
+def test_full_mxfp4_gemm_4096x8192x8192():
+    d = W.make(W.C3)
+    announce("full MXFP4 GEMM 4096x8192x8192")
+    a = mx_quant_gpu(d["x"], torch.float32)
+    b = mx_quant_gpu(d["w"], torch.float32)
+    y = mx.mx_gemm(a, b, out_dtype=torch.bfloat16)
+    rm, rn = _sample(4096, 24, 2), _sample(8192, 96, 3)
+    ra, rsa = O.mxfp4_quantize(d["x"][rm])
+    rb, rsb = O.mxfp4_quantize(d["w"][rn])
+    assert np.array_equal(host(a.codes)[rm], ra) and np.array_equal(host(a.scales)[rm], rsa)
+    assert np.array_equal(host(b.codes)[rn], rb) and np.array_equal(host(b.scales)[rn], rsb)
+    ah, bh = O.dequantize("mxfp4", ra, rsa), O.dequantize("mxfp4", rb, rsb)
+    yref = O.gemm(ah, bh, out="bf16")
+    got = host(y.float())[np.ix_(rm, rn)]
+    assert_within(got, yref, O.gemm_tolerance(ah, bh, yref, out="bf16"), "full mxfp4 gemm")
+
+
+def test_full_nvfp4_gemm_2048x28672x8192():
+    d = W.make(W.C4)
+    announce("full NVFP4 quantize + GEMM 2048x28672x8192")
+    a = mx_quant_gpu(d["x"], torch.float32, fmt="nvfp4")
+    b = mx_quant_gpu(d["w"], torch.float32, fmt="nvfp4")
+    y = mx.mx_gemm(a, b, out_dtype=torch.bfloat16)
+    ga, gb = O.nvfp4_global_scale(d["x"]), O.nvfp4_global_scale(d["w"])
+    assert host(a.global_scale)[0] == ga and host(b.global_scale)[0] == gb
+    rm, rn = _sample(2048, 24, 4), _sample(28672, 96, 5)
+    ra, rsa, _ = O.nvfp4_quantize(d["x"][rm], global_scale=ga)
+    rb, rsb, _ = O.nvfp4_quantize(d["w"][rn], global_scale=gb)
+    assert np.array_equal(host(a.codes)[rm], ra) and np.array_equal(host(a.scales)[rm], rsa)
+    assert np.array_equal(host(b.codes)[rn], rb) and np.array_equal(host(b.scales)[rn], rsb)
+    ah, bh = O.dequantize("nvfp4", ra, rsa, ga), O.dequantize("nvfp4", rb, rsb, gb)
+    yref = O.gemm(ah, bh, out="bf16")
+    got = host(y.float())[np.ix_(rm, rn)]
+    assert_within(got, yref, O.gemm_tolerance(ah, bh, yref, out="bf16"), "full nvfp4 gemm")
+
+
+def test_full_grouped_dynamic_gemm():
+    d = W.make(W.C5)
+    announce("full fused dynamic-quantize grouped GEMM 8x4096x14336, 8192 tokens")
+    G, N, K = 8, 4096, 14336
+    wq = mx_quant_gpu(d["w"].reshape(G * N, K), torch.float32)
+    offs = d["offsets"]
+    offsets = torch.from_numpy(offs).to(DEV)
+    acodes = torch.empty(8192, K // 2, dtype=torch.uint8, device=DEV)
+    ascales = torch.empty(8192, K // 32, dtype=torch.uint8, device=DEV)
+    y = mx.mx_gemm(dev(d["x"], torch.bfloat16), wq, N=N, out_dtype=torch.bfloat16, groups=G, offsets=offsets,
+                   a_codes_out=acodes, a_scales_out=ascales)
+    yh = host(y.float())
+    ach, ash = host(acodes), host(ascales)
+    wch, wsh = host(wq.codes), host(wq.scales)
+    rn = _sample(N, 32, 6)
+    for g in range(G):
+        r0, r1 = int(offs[g]), int(offs[g + 1])
+        rm = r0 + _sample(r1 - r0, 4, 10 + g)
+        ra, rsa = O.mxfp4_quantize(d["x"][rm])
+        assert np.array_equal(ach[rm], ra) and np.array_equal(ash[rm], rsa)
+        rb, rsb = O.mxfp4_quantize(d["w"][g][rn])
+        assert np.array_equal(wch[g * N + rn], rb) and np.array_equal(wsh[g * N + rn], rsb)
+        ah, bh = O.dequantize("mxfp4", ra, rsa), O.dequantize("mxfp4", rb, rsb)
+        yref = O.gemm(ah, bh, out="bf16")
+        assert_within(yh[np.ix_(rm, rn)], yref, O.gemm_tolerance(ah, bh, yref, out="bf16"), f"grouped g={g}")
