@@ -241,6 +241,594 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx(MxGemmPa
     }
 }
 
+// ---------------------------------------------------------------------------
+// Main path (K % 128 == 0): a 4-slot LDS ring filled by direct-to-LDS buffer
+// loads (buffer_load_dwordx4 ... lds), three stages in flight.  Each wave
+// waits only for its own loads of the stage it is about to use
+// (s_waitcnt vmcnt(n) with n = loads issued after that stage), then a bare
+// s_barrier publishes the slot to the whole workgroup; no register staging,
+// so the 256 accumulators stay in AGPRs and the loads never stall the MFMA
+// stream.  Rows past the matrix edge read as zero through the buffer range
+// check (the tile's buffer descriptor covers only its valid rows).
+// ---------------------------------------------------------------------------
+constexpr int RING = 4;
+constexpr int LOADS_PER_STAGE = 10;  // per wave: 4 A chunks, 4 B chunks, 1 A scale, 1 B scale
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ void wait_vm(int n) {
+  // n is one of the three pipeline depths; s_waitcnt needs an immediate.
+  if (n >= 2 * LOADS_PER_STAGE)
+    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  else if (n >= LOADS_PER_STAGE)
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  else
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_ring(MxGemmParams p) {
+  constexpr int NWX = BN / WN;
+  constexpr int NT = (BM / WM) * NWX * 64;
+  constexpr int NW = NT / 64;
+  constexpr int TI = WM / 32, TJ = WN / 32;
+  static_assert(BM == 256 && BN == 256 && NW == 4, "load mapping assumes a 256x256 tile and 4 waves");
+  constexpr int SLOT_A = BM * MX_BKB;             // 16 KiB
+  constexpr int SLOT_B = BN * MX_BKB;
+  constexpr int SLOT = SLOT_A + SLOT_B + 4 * BM + 4 * BN;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[RING * SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wy = wave / NWX, wx = wave % NWX;
+
+  // ---- tile selection (as in the generic kernel)
+  const int tn_count = (p.N + BN - 1) / BN;
+  int g = 0, m_begin = 0, m_end = p.M, tm, tn;
+  {
+    int total;
+    if (p.groups == 0) {
+      total = ((p.M + BM - 1) / BM) * tn_count;
+    } else {
+      total = 0;
+      for (int i = 0; i < p.groups; ++i) {
+        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
+        int rows = o1 > o0 ? o1 - o0 : 0;
+        total += ((rows + BM - 1) / BM) * tn_count;
+      }
+    }
+    const int per_xcd = (total + 7) / 8;
+    const int bid = blockIdx.x;
+    const int local = bid / 8;
+    if (local >= per_xcd) return;
+    const int t = (bid % 8) * per_xcd + local;
+    if (t >= total) return;
+    int tl = t;
+    if (p.groups != 0) {
+      for (int i = 0; i < p.groups; ++i) {
+        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
+        int rows = o1 > o0 ? o1 - o0 : 0;
+        int nt = ((rows + BM - 1) / BM) * tn_count;
+        if (tl < nt) { g = i; m_begin = o0; m_end = o1; break; }
+        tl -= nt;
+      }
+    }
+    const int tm_count = (m_end - m_begin + BM - 1) / BM;
+    const int per_group = GROUP_M * tn_count;
+    const int grp = tl / per_group;
+    const int first_m = grp * GROUP_M;
+    const int gm = min(tm_count - first_m, GROUP_M);
+    const int in_grp = tl % per_group;
+    tm = first_m + in_grp % gm;
+    tn = in_grp / gm;
+  }
+  const int m0 = m_begin + tm * BM;
+  const int n0 = tn * BN;
+  const int KB = p.K / 2, KS = p.K / 32;
+  const int a_rows = min(BM, m_end - m0), b_rows = min(BN, p.N - n0);
+
+  // Buffer descriptors over this tile's valid rows (reads past them return 0).
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a_codes + (size_t)m0 * KB), 0, a_rows * KB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.b_codes + ((size_t)g * p.N + n0) * KB), 0, b_rows * KB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a_scales + (size_t)m0 * KS), 0, a_rows * KS, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.b_scales + ((size_t)g * p.N + n0) * KS), 0, b_rows * KS, 0x00020000);
+
+  // Per-lane byte offsets (stage 0); the stage offset goes in soffset.  LDS
+  // chunk position q = (wave*4 + j)*64 + lane holds row q/4, swizzled chunk
+  // q%4, i.e. global chunk (q%4) ^ swz4(row).
+  int voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int q = (wave * 4 + j) * 64 + lane;
+    const int row = q >> 2, cs = q & 3;
+    voff[j] = row * KB + ((cs ^ swz4(row)) << 4);
+  }
+  const int soff_row = (wave * 64 + lane) * KS;   // scale dword of row wave*64+lane
+
+  // All offsets go in the per-lane voffset, which the raw-buffer range check
+  // covers; soffset stays 0.  A stage past the end gets an offset beyond
+  // every descriptor's range (the host keeps K <= 2^23, so tile ranges stay
+  // below 2^30 bytes) and therefore loads zeros.
+  const int nst = p.K / MX_BK;
+  auto issue = [&](int st) {
+    uint8_t* slot = smem + (st % RING) * SLOT;
+    const bool in = st < nst;
+    const int kb0 = st * MX_BKB;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (wave * 4 + j) * 1024), 16,
+                                               in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + SLOT_A + (wave * 4 + j) * 1024), 16,
+                                               in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(slot + SLOT_A + SLOT_B + wave * 256), 4,
+                                             in ? soff_row + st * 4 : 0x7ffffff0, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(slot + SLOT_A + SLOT_B + 4 * BM + wave * 256), 4,
+                                             in ? soff_row + st * 4 : 0x7ffffff0, 0, 0, 0);
+  };
+
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Prefetch is issued unconditionally: a stage past the end lies outside
+  // the buffer range (soffset beyond num_records) and loads zeros, so every
+  // iteration waits for the same count and the loop body is one basic block.
+  const int nstages = p.K / MX_BK;
+  issue(0);
+  issue(1);
+  issue(2);
+
+  const int lrow = lane & 31;
+  const int khalf = lane >> 5;
+  // LDS byte offsets (within a slot) of this lane's fragments: A row
+  // wy*WM + i*32 + lrow, B row wx*WN + j*32 + lrow, 16-byte chunk kk*2+khalf.
+  int offa[2][TI], offb[2][TJ];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = wy * WM + i * 32 + lrow;
+      offa[kk][i] = row * MX_BKB + (((kk * 2 + khalf) ^ swz4(row)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = wx * WN + j * 32 + lrow;
+      offb[kk][j] = SLOT_A + row * MX_BKB + (((kk * 2 + khalf) ^ swz4(row)) << 4);
+    }
+  }
+  const int offsa = SLOT_A + SLOT_B + (wy * WM + lrow) * 4;
+  const int offsb = SLOT_A + SLOT_B + 4 * BM + (wx * WN + lrow) * 4;
+  const int sshift = 8 * khalf;
+
+  i32x4 fa0[TI], fb0[TJ], fa1[TI], fb1[TJ];
+  uint32_t sa[TI], sb[TJ];
+  auto read_k0 = [&](const uint8_t* slot) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa0[i] = *reinterpret_cast<const i32x4*>(slot + offa[0][i]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fb0[j] = *reinterpret_cast<const i32x4*>(slot + offb[0][j]);
+#pragma unroll
+    for (int i = 0; i < TI; ++i) sa[i] = *reinterpret_cast<const uint32_t*>(slot + offsa + i * 128);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) sb[j] = *reinterpret_cast<const uint32_t*>(slot + offsb + j * 128);
+  };
+  auto read_k1 = [&](const uint8_t* slot) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa1[i] = *reinterpret_cast<const i32x4*>(slot + offa[1][i]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fb1[j] = *reinterpret_cast<const i32x4*>(slot + offb[1][j]);
+  };
+
+  asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  block_barrier();
+  read_k0(smem);
+  for (int s = 0; s < nstages; ++s) {
+    const uint8_t* slot = smem + (s % RING) * SLOT;
+    uint32_t sa_s[TI], sb_s[TJ];
+#pragma unroll
+    for (int i = 0; i < TI; ++i) sa_s[i] = sa[i] >> sshift;
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) sb_s[j] = sb[j] >> sshift;
+    // segment 1: K 0..63 of stage s; read this stage's second-half fragments
+    read_k1(slot);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const i32x8 a8 = {fa0[i][0], fa0[i][1], fa0[i][2], fa0[i][3], 0, 0, 0, 0};
+        const i32x8 b8 = {fb0[j][0], fb0[j][1], fb0[j][2], fb0[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 0, sa_s[i], 0, sb_s[j]);
+      }
+#pragma unroll
+    for (int q = 0; q < TI + TJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - TI - TJ, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // segment 2: stage s+1 is complete in LDS once every wave has seen its
+    // own loads land; then refill the slot stage s-1 used.
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+    block_barrier();
+    issue(s + RING - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    // segment 3: K 64..127 of stage s; read stage s+1's first-half fragments
+    read_k0(smem + ((s + 1) % RING) * SLOT);
+#pragma unroll
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const i32x8 a8 = {fa1[i][0], fa1[i][1], fa1[i][2], fa1[i][3], 0, 0, 0, 0};
+        const i32x8 b8 = {fb1[j][0], fb1[j][1], fb1[j][2], fb1[j][3], 0, 0, 0, 0};
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, acc[i][j], 4, 4, 2, sa_s[i], 2, sb_s[j]);
+      }
+#pragma unroll
+    for (int q = 0; q < TI + TJ + 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - TI - TJ - 4, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue through LDS: each wave stages half of its 128 x 128 fp32
+  // tile (64 rows, row pitch 136 floats so the two half-waves' writes fall
+  // in different banks), then writes whole rows with 8- or 16-byte stores.
+  block_barrier();   // every wave is done reading the ring
+  constexpr int EP_PITCH = WN + 8;
+  float* ep = reinterpret_cast<float*>(smem) + wave * (WM / 2) * EP_PITCH;
+  const bool vec_ok = (p.ldc % 4) == 0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int ii = 0; ii < TI / 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = ii * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+          ep[lr * EP_PITCH + j * 32 + lrow] = acc[half * (TI / 2) + ii][j][r];
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+    const int cl = (lane & 31) * 4;
+    const int col = n0 + wx * WN + cl;
+#pragma unroll 4
+    for (int t = 0; t < WM / 4; ++t) {
+      const int lr = 2 * t + khalf;
+      const int row = m0 + wy * WM + half * (WM / 2) + lr;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&ep[lr * EP_PITCH + cl]);
+      if (row < m_end) {
+        if (p.c_bf16) {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + (size_t)row * p.ldc + col;
+          if (vec_ok && col + 3 < p.N) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2*>(dst) = u32x2{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                                   f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (col + q < p.N) dst[q] = (uint16_t)f32_to_bf16_rne(v[q]);
+          }
+        } else {
+          float* dst = reinterpret_cast<float*>(p.c) + (size_t)row * p.ldc + col;
+          if (vec_ok && col + 3 < p.N) {
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (col + q < p.N) dst[q] = v[q];
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Main path for K % 256 == 0: stages of K = 256 (128 bytes of codes per row),
+// two LDS slots of 68 KiB.  Whole 128-byte row slices per direct-to-LDS load
+// keep every request a full cache line, which roughly doubles the per-CU
+// L2 -> LDS rate over 64-byte slices.  A stage is four K = 64 MFMA segments;
+// each segment reads the next segment's fragments while its 16 MFMAs run, and
+// the refill of the slot just consumed is issued before the last segment, so
+// it has a whole stage of MFMA time to land.
+// ---------------------------------------------------------------------------
+constexpr int BK2 = 256, BKB2 = 128;
+__device__ __forceinline__ int swz8r(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxGemmParams p) {
+  constexpr int NWX = BN / WN;
+  constexpr int NT = (BM / WM) * NWX * 64;
+  constexpr int NW = NT / 64;
+  constexpr int TI = WM / 32, TJ = WN / 32;
+  static_assert(BM == 256 && BN == 256 && NW == 4, "load mapping assumes a 256x256 tile and 4 waves");
+  constexpr int SLOT_A = BM * BKB2;              // 32 KiB
+  constexpr int SLOT_B = BN * BKB2;
+  constexpr int OFF_SA = SLOT_A + SLOT_B;        // 2 x [BM] dwords, then 2 x [BN]
+  constexpr int OFF_SB = OFF_SA + 8 * BM;
+  constexpr int SLOT = OFF_SB + 8 * BN;          // 69632
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wy = wave / NWX, wx = wave % NWX;
+
+  const int tn_count = (p.N + BN - 1) / BN;
+  int g = 0, m_begin = 0, m_end = p.M, tm, tn;
+  {
+    int total;
+    if (p.groups == 0) {
+      total = ((p.M + BM - 1) / BM) * tn_count;
+    } else {
+      total = 0;
+      for (int i = 0; i < p.groups; ++i) {
+        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
+        int rows = o1 > o0 ? o1 - o0 : 0;
+        total += ((rows + BM - 1) / BM) * tn_count;
+      }
+    }
+    const int per_xcd = (total + 7) / 8;
+    const int bid = blockIdx.x;
+    const int local = bid / 8;
+    if (local >= per_xcd) return;
+    const int t = (bid % 8) * per_xcd + local;
+    if (t >= total) return;
+    int tl = t;
+    if (p.groups != 0) {
+      for (int i = 0; i < p.groups; ++i) {
+        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
+        int rows = o1 > o0 ? o1 - o0 : 0;
+        int nt = ((rows + BM - 1) / BM) * tn_count;
+        if (tl < nt) { g = i; m_begin = o0; m_end = o1; break; }
+        tl -= nt;
+      }
+    }
+    const int tm_count = (m_end - m_begin + BM - 1) / BM;
+    const int per_group = GROUP_M * tn_count;
+    const int grp = tl / per_group;
+    const int first_m = grp * GROUP_M;
+    const int gm = min(tm_count - first_m, GROUP_M);
+    const int in_grp = tl % per_group;
+    tm = first_m + in_grp % gm;
+    tn = in_grp / gm;
+  }
+  const int m0 = m_begin + tm * BM;
+  const int n0 = tn * BN;
+  const int KB = p.K / 2, KS = p.K / 32;
+  const int a_rows = min(BM, m_end - m0), b_rows = min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a_codes + (size_t)m0 * KB), 0, a_rows * KB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.b_codes + ((size_t)g * p.N + n0) * KB), 0, b_rows * KB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsa = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a_scales + (size_t)m0 * KS), 0, a_rows * KS, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.b_scales + ((size_t)g * p.N + n0) * KS), 0, b_rows * KS, 0x00020000);
+
+  // LDS 16-byte position q = (wave*8 + j)*64 + lane of a panel holds row q/8,
+  // swizzled chunk q%8, i.e. global chunk (q%8) ^ swz8r(row).
+  int voff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int q = (wave * 8 + j) * 64 + lane;
+    const int row = q >> 3, cs = q & 7;
+    voff[j] = row * KB + ((cs ^ swz8r(row)) << 4);
+  }
+  const int srow = (wave * 64 + lane) * KS;
+  const int nst = p.K / BK2;
+  // All offsets in voffset (range checked); stages past the end load zeros.
+  auto issue = [&](int st) {
+    uint8_t* slot = smem + (st & 1) * SLOT;
+    const bool in = st < nst;
+    const int kb0 = st * BKB2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (wave * 8 + j) * 1024), 16,
+                                               in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + SLOT_A + (wave * 8 + j) * 1024), 16,
+                                               in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(slot + OFF_SA + h * 4 * BM + wave * 256), 4,
+                                               in ? srow + st * 8 + h * 4 : 0x7ffffff0, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(slot + OFF_SB + h * 4 * BN + wave * 256), 4,
+                                               in ? srow + st * 8 + h * 4 : 0x7ffffff0, 0, 0, 0);
+    }
+  };
+
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int lrow = lane & 31;
+  const int khalf = lane >> 5;
+  int offa[4][TI], offb[4][TJ];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) {
+      const int row = wy * WM + i * 32 + lrow;
+      offa[kk][i] = row * BKB2 + (((kk * 2 + khalf) ^ swz8r(row)) << 4);
+    }
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int row = wx * WN + j * 32 + lrow;
+      offb[kk][j] = SLOT_A + row * BKB2 + (((kk * 2 + khalf) ^ swz8r(row)) << 4);
+    }
+  }
+  const int offsa = OFF_SA + (wy * WM + lrow) * 4;
+  const int offsb = OFF_SB + (wx * WN + lrow) * 4;
+  const int sshift = 8 * khalf;
+
+  // All four K = 64 fragment sets of a stage live in registers (F[kk]), so a
+  // slot is fully read two segments into the stage.  Two barriers per stage:
+  // B1 after segment 2 (slot consumed -> refill it with stage s+2) and B2
+  // before segment 4 (stage s+1 landed -> start reading it), which gives the
+  // refill a stage and a half of lead time with two slots.
+  i32x4 fa[4][TI], fb[4][TJ];
+  uint32_t sa[2][TI], sb[2][TJ];   // raw scale dwords (blocks 0-3 / 4-7 of the stage)
+  auto read_frag = [&](int kk, const uint8_t* slot) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) fa[kk][i] = *reinterpret_cast<const i32x4*>(slot + offa[kk][i]);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) fb[kk][j] = *reinterpret_cast<const i32x4*>(slot + offb[kk][j]);
+  };
+  auto read_scales = [&](int h, const uint8_t* slot) {
+#pragma unroll
+    for (int i = 0; i < TI; ++i) sa[h][i] = *reinterpret_cast<const uint32_t*>(slot + offsa + h * 4 * BM + i * 128);
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) sb[h][j] = *reinterpret_cast<const uint32_t*>(slot + offsb + h * 4 * BN + j * 128);
+  };
+  // 16 MFMAs of segment KK: the lane's block is 2*KK + khalf, i.e. byte
+  // 2*(KK%2) + khalf of scale dword KK/2; shifting by 8*khalf leaves it at
+  // byte 0 (opsel 0) or byte 2 (opsel 2).
+#define MX_SEG(KK, OPS)                                                                                 \
+  _Pragma("unroll") for (int i = 0; i < TI; ++i)                                                        \
+  _Pragma("unroll") for (int j = 0; j < TJ; ++j) {                                                      \
+    const i32x8 a8 = {fa[KK][i][0], fa[KK][i][1], fa[KK][i][2], fa[KK][i][3], 0, 0, 0, 0};              \
+    const i32x8 b8 = {fb[KK][j][0], fb[KK][j][1], fb[KK][j][2], fb[KK][j][3], 0, 0, 0, 0};              \
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(                                        \
+        a8, b8, acc[i][j], 4, 4, OPS, sa[(KK) / 2][i] >> sshift, OPS, sb[(KK) / 2][j] >> sshift);       \
+  }
+  // Reads for later segments go out two per MFMA at the front of a segment,
+  // so each has most of the segment (16 x 32 cycles) to land.
+#define MX_INTERLEAVE(NDS)                                              \
+  _Pragma("unroll") for (int q = 0; q < (NDS) / 2; ++q) {               \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  \
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                  \
+  }                                                                     \
+  __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - (NDS) / 2, 0);  \
+  __builtin_amdgcn_sched_barrier(0);
+
+  issue(0);
+  issue(1);
+  asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  block_barrier();
+  read_frag(0, smem);
+  read_scales(0, smem);
+  for (int s = 0; s < nst; ++s) {
+    const uint8_t* cur = smem + (s & 1) * SLOT;
+    const uint8_t* nxt = smem + ((s + 1) & 1) * SLOT;
+    read_frag(1, cur);
+    read_scales(1, cur);
+    read_frag(2, cur);
+    MX_SEG(0, 0)
+    MX_INTERLEAVE(2 * (TI + TJ) + 4)
+    read_frag(3, cur);
+    MX_SEG(1, 2)
+    MX_INTERLEAVE(TI + TJ)
+    // B1: every wave has read all of `cur`; refill it with stage s+2
+    // The 20 refill loads are spread between the segment-3 MFMAs: issued as
+    // one burst they fill the texture-address queue and block the wave (and
+    // with it the MFMA stream) until the queue drains.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    block_barrier();
+    issue(s + 2);
+    MX_SEG(2, 0)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+    }
+#pragma unroll
+    for (int q = 4; q < TI * TJ; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // B2: this wave's loads of stage s+1 have landed (only stage s+2's 20 may
+    // still be in flight); after the barrier every wave's have.
+    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    block_barrier();
+    read_scales(0, nxt);
+    read_frag(0, nxt);
+    MX_SEG(3, 2)
+    MX_INTERLEAVE(TI + TJ + 4)
+  }
+#undef MX_SEG
+#undef MX_INTERLEAVE
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue through LDS: each wave stages half of its 128 x 128 fp32
+  // tile (64 rows, row pitch 136 floats so the two half-waves' writes fall
+  // in different banks), then writes whole rows with 8- or 16-byte stores.
+  block_barrier();   // every wave is done reading the ring
+  constexpr int EP_PITCH = WN + 8;
+  float* ep = reinterpret_cast<float*>(smem) + wave * (WM / 2) * EP_PITCH;
+  const bool vec_ok = (p.ldc % 4) == 0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int ii = 0; ii < TI / 2; ++ii)
+#pragma unroll
+      for (int j = 0; j < TJ; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = ii * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+          ep[lr * EP_PITCH + j * 32 + lrow] = acc[half * (TI / 2) + ii][j][r];
+        }
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+    const int cl = (lane & 31) * 4;
+    const int col = n0 + wx * WN + cl;
+#pragma unroll 4
+    for (int t = 0; t < WM / 4; ++t) {
+      const int lr = 2 * t + khalf;
+      const int row = m0 + wy * WM + half * (WM / 2) + lr;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(&ep[lr * EP_PITCH + cl]);
+      if (row < m_end) {
+        if (p.c_bf16) {
+          uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + (size_t)row * p.ldc + col;
+          if (vec_ok && col + 3 < p.N) {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<u32x2*>(dst) = u32x2{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
+                                                   f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (col + q < p.N) dst[q] = (uint16_t)f32_to_bf16_rne(v[q]);
+          }
+        } else {
+          float* dst = reinterpret_cast<float*>(p.c) + (size_t)row * p.ldc + col;
+          if (vec_ok && col + 3 < p.N) {
+            *reinterpret_cast<f32x4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (col + q < p.N) dst[q] = v[q];
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+  }
+}
+
 // Tile configuration used for every MXFP4 product.
 constexpr int GBM = 256, GBN = 256, GWM = 128, GWN = 128;
 
@@ -257,7 +845,12 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
   int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   constexpr int NT = (GBM / GWM) * (GBN / GWN) * 64;
-  hipLaunchKernelGGL((k_gemm_mx<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
+  if (K % BK2 == 0)
+    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
+  else if (K % MX_BK == 0)
+    hipLaunchKernelGGL((k_gemm_mx_ring<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
+  else
+    hipLaunchKernelGGL((k_gemm_mx<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
   return hipGetLastError();
 }
 

@@ -168,6 +168,7 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
     }
   }
   if (fmt == MX_FMT_NVFP4 && a->K % 32 != 0) return MX_ERR_UNSUPPORTED;
+  if (a->K > (int64_t(1) << 23)) return MX_ERR_UNSUPPORTED;   // tile byte offsets stay below 2^30
   if (a->M == 0 || a->N == 0) return MX_OK;
   hipStream_t s = as_stream(stream);
   if (dynamic && a->K > 0) {
