@@ -6,8 +6,10 @@ One step = quantize the fp32 activations X [4096, 8192] to MXFP4 + quantize
 the fp32 weights W [8192, 8192] to MXFP4 + the W4A4 GEMM (bf16 out).
 value = 2*M*N*K / step time, in TFLOPS.  Inputs are resident in HBM before
 timing; two input sets (804 MB) alternate so that the 256 MB last-level cache
-cannot hold a step's inputs.  Per-kernel durations come from HIP events
-recorded on the stream the kernels run on.
+cannot hold a step's inputs.  The timed steps replay HIP graphs (one per
+input set, checked to reproduce the eager result); per-kernel durations come
+from HIP events around graphs of back-to-back launches of that kernel, on
+the stream they run on.
 
 Secondary measurements (same JSON line, `secondary`): the W4A16 GEMV
 N=K=8192 at M = 1, 8, 16 (GB/s, weights rotated over 16 copies), the NVFP4
@@ -68,30 +70,37 @@ def load_traffic(name, kernel_files):
         return None
 
 
-class EvTimer:
-    """Accumulates durations of regions bracketed by HIP events on a stream."""
+def capture(torch, fn, reps=1):
+    """A HIP graph of `reps` calls of fn (all launches on the capture stream).
+    The step is launch-bound from Python (a few tens of microseconds of host
+    work per call), so timed work replays graphs instead of calling eagerly."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()                                  # eager warm-up call outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    torch.cuda.synchronize()
+    return g
 
-    def __init__(self, torch, stream):
-        self.torch, self.stream, self.pairs = torch, stream, {}
 
-    def region(self, name):
-        torch = self.torch
-        tm = self
-
-        class _R:
-            def __enter__(self_):
-                self_.s = torch.cuda.Event(enable_timing=True)
-                self_.e = torch.cuda.Event(enable_timing=True)
-                self_.s.record(tm.stream)
-
-            def __exit__(self_, *a):
-                self_.e.record(tm.stream)
-                tm.pairs.setdefault(name, []).append((self_.s, self_.e))
-        return _R()
-
-    def mean_ms(self, name):
-        p = self.pairs.get(name, [])
-        return sum(s.elapsed_time(e) for s, e in p) / max(len(p), 1)
+def time_graph(torch, g, reps_in_graph, replays=5):
+    """Average duration of one captured call: HIP events around `replays`
+    replays on the stream the graph runs on."""
+    stream = torch.cuda.current_stream()
+    g.replay()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record(stream)
+    for _ in range(replays):
+        g.replay()
+    e.record(stream)
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / (replays * reps_in_graph)
 
 
 def bench_main(args, torch, mx, W):
@@ -106,35 +115,47 @@ def bench_main(args, torch, mx, W):
         wt = torch.from_numpy(d["w"]).to(dev)
         sets.append((x, wt, mx.empty_quantized(M, K, "mxfp4", dev), mx.empty_quantized(N, K, "mxfp4", dev)))
     c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream(dev)
 
-    def step(i, tm=None):
+    def step(i):
         x, wt, aq, bq = sets[i % 2]
-        if tm is None:
-            mx.mx_quantize(x, out=aq)
-            mx.mx_quantize(wt, out=bq)
-            mx.mx_gemm(aq, bq, out=c)
-            return
-        with tm.region("quant_x"):
-            mx.mx_quantize(x, out=aq)
-        with tm.region("quant_w"):
-            mx.mx_quantize(wt, out=bq)
-        with tm.region("gemm"):
-            mx.mx_gemm(aq, bq, out=c)
+        mx.mx_quantize(x, out=aq)
+        mx.mx_quantize(wt, out=bq)
+        mx.mx_gemm(aq, bq, out=c)
+
+    # one graph per input set; a replay must reproduce the eager result exactly
+    step(0)
+    torch.cuda.synchronize()
+    c_eager = c.clone()
+    graphs = [capture(torch, lambda i=i: step(i)) for i in range(2)]
+    for i in (1, 0, 1, 0):
+        c.zero_()
+        graphs[i].replay()
+        torch.cuda.synchronize()
+    if not torch.equal(c, c_eager):
+        raise RuntimeError("graph replay of the step differs from the eager step")
 
     for i in range(args.warmup):
-        step(i)
+        graphs[i % 2].replay()
     torch.cuda.synchronize()
-    tm = EvTimer(torch, stream)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, tm)
+        graphs[i % 2].replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    del graphs
+
+    # per-kernel durations: events around graphs of back-to-back launches that
+    # alternate between the two input sets (each set's fp32 inputs alone fill
+    # about half of the last-level cache)
+    R = 5
+
+    def alt(fn):
+        return lambda: [fn(*sets[i]) for i in (0, 1)]
+    qx_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(x, out=aq)), R), 2 * R)
+    qw_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(wt, out=bq)), R), 2 * R)
+    g_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_gemm(aq, bq, out=c)), R), 2 * R)
     flops = 2.0 * M * N * K
-    g_ms = tm.mean_ms("gemm")
-    qx_ms, qw_ms = tm.mean_ms("quant_x"), tm.mean_ms("quant_w")
     qx_bytes = M * K * 4 + M * K // 2 + M * K // 32
     qw_bytes = N * K * 4 + N * K // 2 + N * K // 32
     gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * 2
@@ -145,7 +166,8 @@ def bench_main(args, torch, mx, W):
         "ms_per_step": ms_step,
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / PEAK_FP4_TFLOPS, "traffic": traffic,
-                     "kernel": GEMM_KERNEL, "flops_per_launch": flops, "avg_launch_ms": g_ms},
+                     "kernel": GEMM_KERNEL, "flops_per_launch": flops, "algorithmic_bytes_per_launch": gemm_bytes,
+                     "avg_launch_ms": g_ms},
         "kernels": {
             "quantize_x": {"avg_ms": qx_ms, "GB/s": qx_bytes / (qx_ms * 1e-3) / 1e9, "bytes": qx_bytes,
                            "frac_hbm": qx_bytes / (qx_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
@@ -165,25 +187,19 @@ def bench_gemv(args, torch, mx, W):
     dev = torch.device("cuda:0")
     d = W.make(w)
     wt = torch.from_numpy(d["w"]).to(dev)
-    reps = 16   # 16 weight copies x 35.7 MB rotate past the last-level cache
+    reps = 16   # 16 weight copies x 35.7 MB rotate past the 256 MB last-level cache
     ws = [mx.mx_quantize(wt) for _ in range(reps)]
     del wt
     out = {}
-    stream = torch.cuda.current_stream(dev)
     for M in W.GEMV_M:
         x = torch.from_numpy(d["x"][:M]).to(torch.bfloat16).to(dev)
         y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        for i in range(2 * reps):
-            mx.mx_gemv(x, ws[i % reps], out=y)
-        torch.cuda.synchronize()
-        n = max(args.gemv_iters, reps)
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record(stream)
-        for i in range(n):
-            mx.mx_gemv(x, ws[i % reps], out=y)
-        e.record(stream)
-        torch.cuda.synchronize()
-        ms = s.elapsed_time(e) / n
+
+        def batch():
+            for i in range(reps):
+                mx.mx_gemv(x, ws[i], out=y)
+        g = capture(torch, batch, max(1, args.gemv_iters // reps))
+        ms = time_graph(torch, g, reps * max(1, args.gemv_iters // reps))
         byt = N * K // 2 + N * K // 32 + 2 * M * K + 2 * M * N
         gbs = byt / (ms * 1e-3) / 1e9
         out[f"M={M}"] = {"avg_ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": byt,
@@ -201,28 +217,17 @@ def bench_nvfp4(args, torch, mx, W):
     aq = mx.empty_quantized(M, K, "nvfp4", dev)
     bq = mx.empty_quantized(N, K, "nvfp4", dev)
     c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    tm = EvTimer(torch, stream)
-    for it in range(1 + args.side_iters):
-        t = tm if it else None
-        for name, fn in (("quant_x", lambda: mx.mx_quantize(x, "nvfp4", out=aq, workspace=ws)),
-                         ("quant_w", lambda: mx.mx_quantize(wt, "nvfp4", out=bq, workspace=ws)),
-                         ("gemm", lambda: mx.mx_gemm(aq, bq, out=c))):
-            if t is None:
-                fn()
-            else:
-                with t.region(name):
-                    fn()
-    torch.cuda.synchronize()
-    g = tm.mean_ms("gemm")
+    wsp = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    R = max(1, args.side_iters)
+    qx = time_graph(torch, capture(torch, lambda: mx.mx_quantize(x, "nvfp4", out=aq, workspace=wsp), R), R)
+    qw = time_graph(torch, capture(torch, lambda: mx.mx_quantize(wt, "nvfp4", out=bq, workspace=wsp), R), R)
+    g = time_graph(torch, capture(torch, lambda: mx.mx_gemm(aq, bq, out=c), R), R, replays=2)
     flops = 2.0 * M * N * K
-    qw = tm.mean_ms("quant_w")
     qw_bytes = 2 * N * K * 4 + N * K // 2 + N * K // 16 + 4   # amax pass + quantize pass
     return {"gemm_avg_ms": g, "gemm_TFLOPS": flops / (g * 1e-3) / 1e12,
             "gemm_frac_fp16_mfma_peak": flops / (g * 1e-3) / 1e12 / PEAK_F16_TFLOPS,
             "gemm_frac_fp4_peak": flops / (g * 1e-3) / 1e12 / PEAK_FP4_TFLOPS,
-            "quant_x_avg_ms": tm.mean_ms("quant_x"), "quant_w_avg_ms": qw,
+            "quant_x_avg_ms": qx, "quant_w_avg_ms": qw,
             "quant_w_GB/s_two_reads": qw_bytes / (qw * 1e-3) / 1e9}
 
 
@@ -235,18 +240,11 @@ def bench_grouped(args, torch, mx, W):
     x = torch.from_numpy(d["x"]).to(torch.bfloat16).to(dev)
     offs = torch.from_numpy(d["offsets"]).to(dev)
     y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
-    wsz = T * K // 2 + T * K // 32 + 4096
+    wsz = T * K // 2 + T * K // 32 + 4096   # >= mx_workspace_bytes for the dynamic A operand
     wsp = torch.empty(wsz, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-    tm = EvTimer(torch, stream)
-    for it in range(1 + args.side_iters):
-        if it == 0:
-            mx.mx_gemm(x, wq, N=N, out=y, groups=G, offsets=offs, workspace=wsp)
-        else:
-            with tm.region("fused"):
-                mx.mx_gemm(x, wq, N=N, out=y, groups=G, offsets=offs, workspace=wsp)
-    torch.cuda.synchronize()
-    ms = tm.mean_ms("fused")
+    R = max(1, args.side_iters)
+    ms = time_graph(torch, capture(torch, lambda: mx.mx_gemm(x, wq, N=N, out=y, groups=G, offsets=offs,
+                                                             workspace=wsp), R), R, replays=3)
     flops = 2.0 * T * N * K
     return {"avg_ms": ms, "TFLOPS": flops / (ms * 1e-3) / 1e12, "frac_fp4_peak": flops / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS,
             "note": "one mx_gemm call: MXFP4 quantization of the bf16 tokens + grouped W4A4 GEMM"}

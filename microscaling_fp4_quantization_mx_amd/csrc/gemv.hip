@@ -169,6 +169,7 @@ __global__ __launch_bounds__(GV_T) void k_gemv_sk(const uint16_t* __restrict__ x
 // copy, and after the arithmetic (before the buffer is refilled).
 constexpr int GL_T = 512;              // 8 waves
 constexpr int GV_LG_RB = 4;            // weight rows per wave of the large-M kernel
+constexpr int GV_LG_MIN_M = 2;         // smallest M that takes the large-M kernel
 
 template <int VM>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -315,7 +316,7 @@ __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x
 hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st) {
   if (N == 0) return hipSuccess;
-  if (M <= 4) {
+  if (M < GV_LG_MIN_M) {
     constexpr int RB = GV_SK_RB;
     const int grid = (int)((N + RB - 1) / RB);
 #define MX_GVS(MM) case MM: hipLaunchKernelGGL((k_gemv_sk<MM, RB>), dim3(grid), dim3(GV_T), 0, st, (const uint16_t*)x, ldx, wc, ws, (int)N, (int)K, (uint16_t*)y, ldy); break;
@@ -330,7 +331,7 @@ hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc,
   const int grid = (int)((N + 8 * RB - 1) / (8 * RB));
 #define MX_GVL(MM) case MM: hipLaunchKernelGGL((k_gemv_lg<MM, RB>), dim3(grid), dim3(GL_T), 0, st, (const uint16_t*)x, ldx, wc, ws, (int)N, (int)K, (uint16_t*)y, ldy); break;
   switch ((int)M) {
-    MX_GVL(5) MX_GVL(6) MX_GVL(7) MX_GVL(8)
+    MX_GVL(2) MX_GVL(3) MX_GVL(4) MX_GVL(5) MX_GVL(6) MX_GVL(7) MX_GVL(8)
     MX_GVL(9) MX_GVL(10) MX_GVL(11) MX_GVL(12) MX_GVL(13) MX_GVL(14) MX_GVL(15) MX_GVL(16)
     default: return hipErrorInvalidValue;
   }
