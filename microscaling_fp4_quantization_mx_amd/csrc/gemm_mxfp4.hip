@@ -519,8 +519,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_ring(MxG
           uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + (size_t)row * p.ldc + col;
           if (vec_ok && col + 3 < p.N) {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u32x2*>(dst) = u32x2{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                                   f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
           } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -806,8 +805,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
           uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + (size_t)row * p.ldc + col;
           if (vec_ok && col + 3 < p.N) {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u32x2*>(dst) = u32x2{f32_to_bf16_rne(v[0]) | (f32_to_bf16_rne(v[1]) << 16),
-                                                   f32_to_bf16_rne(v[2]) | (f32_to_bf16_rne(v[3]) << 16)};
+            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
           } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)

@@ -29,6 +29,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two floats -> packed bf16 pair (lo in bits 0-15), round to nearest even, in
+// one v_cvt_pk_bf16_f32.  Identical to f32_to_bf16_rne for every non-NaN
+// input (a NaN comes out as a quiet NaN).
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t b = __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &b, 4);
+  return u;
+}
+
 // E8M0 block exponent of an MXFP4 block from the bit pattern of its max |x|:
 // the smallest e with max <= 6 * 2^e, floored at -29 (the 1e-8 guard of the
 // pages' emulation: ceil(log2(1e-8 / 6)) = -29).  For a normal max with

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(QT) void k_dequant(const uint32_t* __restrict__ cod
     if (OUT_BF16) {
       u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16_rne(f[2 * i]) | (f32_to_bf16_rne(f[2 * i + 1]) << 16);
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2_rne(f[2 * i], f[2 * i + 1]);
       *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(y) + off) = o;
     } else {
       f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + off);
