@@ -254,8 +254,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx(MxGemmPa
 constexpr int RING = 4;
 constexpr int LOADS_PER_STAGE = 10;  // per wave: 4 A chunks, 4 B chunks, 1 A scale, 1 B scale
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 __device__ __forceinline__ void wait_vm(int n) {
   // n is one of the three pipeline depths; s_waitcnt needs an immediate.
   if (n >= 2 * LOADS_PER_STAGE)
@@ -264,11 +262,6 @@ __device__ __forceinline__ void wait_vm(int n) {
     asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
   else
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
 }
 
 template <int BM, int BN, int WM, int WN>
@@ -551,7 +544,6 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_ring(MxG
 // it has a whole stage of MFMA time to land.
 // ---------------------------------------------------------------------------
 constexpr int BK2 = 256, BKB2 = 128;
-__device__ __forceinline__ int swz8r(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxGemmParams p) {

@@ -23,8 +23,6 @@
 
 namespace mxk {
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
 constexpr int GV_T = 256;              // 4 waves
 constexpr int GV_WIN = 64 * 32;        // K elements per window (64 lanes x 1 block)
 constexpr int GV_SK_RB = 4;            // weight rows per workgroup of the small-M kernel
@@ -179,11 +177,6 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x70 | 0xf00);
 }
 
-__device__ __forceinline__ void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int M, int RB>
 __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,

@@ -115,6 +115,20 @@ __device__ __forceinline__ uint32_t cvt_fp4x2(uint32_t old, float a, float b, fl
 }
 
 // wave64 reductions via cross-lane xor shuffles.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Workgroup barrier without the implicit wait for outstanding loads that
+// __syncthreads() carries (callers issue the counted s_waitcnt they need).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row: the 32
+// lanes that read one chunk column of 32 consecutive rows hit distinct banks.
+__device__ __forceinline__ int swz8r(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
+
 __device__ __forceinline__ uint32_t umax_xor(uint32_t v, int mask) {
   return max(v, (uint32_t)__shfl_xor((int)v, mask, 64));
 }
