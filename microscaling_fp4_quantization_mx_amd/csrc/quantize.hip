@@ -29,6 +29,16 @@ constexpr int QU = 4;      // vectors per lane per iteration (loads in flight)
 // Vector v of the tensor: flat index v in [0, rows * cols / EPL).  With a
 // contiguous tensor (ld == cols) its elements sit at x + v * EPL; otherwise
 // row = v / vpr.
+// max over the LPB lanes of a block (aligned groups of 2, 4 or 8 lanes) with
+// DPP lane swaps inside each row of 16 lanes: no LDS round trip
+template <int LPB>
+__device__ __forceinline__ uint32_t block_umax(uint32_t v) {
+  if constexpr (LPB >= 2) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // lane ^ 1
+  if constexpr (LPB >= 4) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // lane ^ 2
+  if constexpr (LPB >= 8) v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // 8-lane mirror
+  return v;
+}
+
 template <typename TIn, bool CONTIG>
 __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr,
                                                  uint32_t nvec, uint8_t* __restrict__ codes,
@@ -38,8 +48,8 @@ __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int6
   const int lane = threadIdx.x & 63;
   const uint32_t wave_global = (blockIdx.x * QT + threadIdx.x) >> 6;
   const uint32_t nwaves = (gridDim.x * QT) >> 6;
-  for (uint32_t base = wave_global * (64 * QU); base < nvec; base += nwaves * (64 * QU)) {
-    u32x4 d[QU];
+  const uint32_t stride = nwaves * (64 * QU);
+  auto load = [&](u32x4 (&d)[QU], uint32_t base) {
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
       uint32_t v = base + u * 64 + lane;
@@ -52,6 +62,14 @@ __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int6
       }
       d[u] = (v < nvec) ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
     }
+  };
+  // the next iteration's vectors are in flight while this one is converted
+  u32x4 d[QU], dn[QU];
+  uint32_t base = wave_global * (64 * QU);
+  if (base < nvec) load(d, base);
+  for (; base < nvec; base += stride) {
+    const uint32_t nb = base + stride;
+    if (nb < nvec) load(dn, nb);
 #pragma unroll
     for (int u = 0; u < QU; ++u) {
       const uint32_t v = base + u * 64 + lane;
@@ -69,8 +87,7 @@ __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int6
       uint32_t am = 0;
 #pragma unroll
       for (int i = 0; i < EPL; ++i) am = max(am, fbits(f[i]) & 0x7fffffffu);
-#pragma unroll
-      for (int m = 1; m < LPB; m <<= 1) am = umax_xor(am, m);
+      am = block_umax<LPB>(am);
       const int e = mx_block_exp(am);
       const float s = pow2f(e);
       uint32_t out = 0;
@@ -89,6 +106,8 @@ __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int6
         if ((lane & (LPB - 1)) == 0) scales[v / LPB] = (uint8_t)(e + 127);
       }
     }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) d[u] = dn[u];
   }
 }
 
