@@ -13,8 +13,10 @@ the stream they run on.
 
 Secondary measurements (same JSON line, `secondary`): the W4A16 GEMV
 N=K=8192 at M = 1, 8, 16 (GB/s, weights rotated over 16 copies), the NVFP4
-quantize + GEMM 2048x28672x8192 and the fused dynamic-quantize grouped GEMM
-(8 experts, N=4096, K=14336, 8192 tokens).
+quantize + GEMM 2048x28672x8192, the fused dynamic-quantize grouped GEMM
+(8 experts, N=4096, K=14336, 8192 tokens) and the routed expert layer
+around it (4096 tokens, top-2: route, gathered quantize, grouped GEMM,
+combine).
 
 cpu_baseline: the CPU oracle (numpy, fp64) on a bounded sub-problem of the
 same step, timed on this host.
@@ -250,6 +252,32 @@ def bench_grouped(args, torch, mx, W):
             "note": "one mx_gemm call: MXFP4 quantization of the bf16 tokens + grouped W4A4 GEMM"}
 
 
+def bench_moe(args, torch, mx, W):
+    """Routed expert layer: route (top-2 of 8) + gathered MXFP4 quantize of the
+    bf16 tokens + grouped W4A4 GEMM (bf16 y) + weighted combine, one graph."""
+    w = W.MOE
+    T, G, N, K, k = w.M, w.experts, w.N, w.K, W.MOE_TOPK
+    dev = torch.device("cuda:0")
+    d = W.make(w)
+    ids, tw = W.topk_routing(T, G, k)
+    wq = mx.mx_quantize(torch.from_numpy(d["w"].reshape(G * N, K)).to(dev))
+    x = torch.from_numpy(d["x"]).to(torch.bfloat16).to(dev)
+    idt, twt = torch.from_numpy(ids).to(dev), torch.from_numpy(tw).to(dev)
+    P = T * k
+    bufs = {"offsets": torch.empty(G + 1, dtype=torch.int32, device=dev),
+            "dest_row": torch.empty(P, dtype=torch.int32, device=dev),
+            "src_token": torch.empty(P, dtype=torch.int32, device=dev),
+            "route_ws": torch.empty(4096, dtype=torch.uint8, device=dev),
+            "aq": mx.empty_quantized(P, K, "mxfp4", dev),
+            "y": torch.empty(P, N, dtype=torch.bfloat16, device=dev),
+            "out": torch.empty(T, N, dtype=torch.bfloat16, device=dev)}
+    R = max(1, args.side_iters)
+    ms = time_graph(torch, capture(torch, lambda: mx.moe_forward(x, idt, twt, wq, G, N, bufs=bufs), R), R, replays=3)
+    flops = 2.0 * P * N * K
+    return {"avg_ms": ms, "TFLOPS": flops / (ms * 1e-3) / 1e12, "frac_fp4_peak": flops / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS,
+            "note": f"{T} tokens, top-{k} of {G} experts, N={N}, K={K}: route + gathered quantize + grouped GEMM + combine"}
+
+
 def cpu_baseline(d):
     """The oracle, as it stands, on a bounded sub-problem of the same step:
     X rows 0..1023 and W rows 0..4095 (both quantized) and their GEMM."""
@@ -328,6 +356,9 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: fused dynamic-quantize grouped GEMM")
         sec["grouped_8x4096x14336_T8192"] = bench_grouped(args, torch, mx, W)
+        torch.cuda.empty_cache()
+        log("secondary: routed expert layer (top-2)")
+        sec["moe_top2_8x4096x14336_T4096"] = bench_moe(args, torch, mx, W)
         torch.cuda.empty_cache()
         out["secondary"] = sec
         if not args.no_cpu:

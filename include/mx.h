@@ -70,7 +70,7 @@ enum {
 };
 
 /* mx_workspace_bytes operations */
-enum { MX_OP_QUANTIZE = 0, MX_OP_GEMM = 1 };
+enum { MX_OP_QUANTIZE = 0, MX_OP_GEMM = 1, MX_OP_MOE_ROUTE = 2 };
 
 typedef struct mx_tensor {
   int32_t fmt;            /* MX_FMT_MXFP4 or MX_FMT_NVFP4 */
@@ -165,8 +165,57 @@ int mx_gemm(const mx_gemm_args *args, void *stream);
 int mx_gemv(const void *x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_tensor *w,
             void *y, int32_t y_dtype, int64_t ld_y, void *stream);
 
+/*
+ * Routed mixture-of-experts layers around the grouped GEMM.  Expert weights
+ * are where block-scaled FP4 pays most ("NVFP4 Architecture", section
+ * "Strategic Recommendations: Adopting NVFP4 in 2026"); grouped GEMM and TopK
+ * belong to an MXFP4 serving stack ("MXFP4" card, section "Core Facts").
+ * A layer with top-k routing runs
+ *   mx_moe_route      (token, slot) pairs -> expert-sorted rows
+ *   mx_quantize_rows  the routed tokens' activations, in that order, to MXFP4
+ *   mx_gemm           grouped W4A4 over offsets[] (groups = experts)
+ *   mx_moe_combine    out[t] = sum_s weight[t, s] * y[dest_row[t, s]]
+ *
+ * mx_moe_route -- stable counting sort of the pairs by expert.
+ *   topk_ids   device int32 [tokens, topk], expert of pair (t, s)
+ *   offsets    device int32 [experts + 1] out: offsets[g] = number of pairs
+ *              with a valid expert id below g (offsets[experts] = all valid)
+ *   dest_row   device int32 [tokens * topk] out: row of pair (t, s) in the
+ *              sorted order; -1 for an id outside [0, experts) (such pairs
+ *              are dropped)
+ *   src_token  device int32 [tokens * topk] out: token of sorted row r for
+ *              r < offsets[experts] (entries beyond are not written)
+ *   workspace  device, >= mx_workspace_bytes(MX_OP_MOE_ROUTE, &experts) bytes
+ * Pairs of one expert keep their flat order t * topk + s, so the result is
+ * unique.  1 <= topk, 1 <= experts <= 65536, tokens * topk < 2^31.
+ */
+int mx_moe_route(const int32_t *topk_ids, int64_t tokens, int32_t topk, int32_t experts,
+                 int32_t *offsets, int32_t *dest_row, int32_t *src_token,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * mx_quantize_rows -- MXFP4 quantization (exactly as mx_quantize) of gathered
+ * rows: output row r is input row row_index[r] of x (device int32
+ * [out->rows]); an index outside [0, x_rows) gives an all-zero row (scale
+ * byte 98, +0 codes).  x is [x_rows, out->cols] with pitch ld_x elements.
+ */
+int mx_quantize_rows(const void *x, int32_t x_dtype, int64_t ld_x, int64_t x_rows,
+                     const int32_t *row_index, const mx_tensor *out, void *stream);
+
+/*
+ * mx_moe_combine -- out[t, n] = sum_{s < topk} weights[t, s] * y[dest_row[t, s], n]
+ * with fp32 accumulation in slot order (fused multiply-add); a pair whose row
+ * is outside [0, y_rows) adds nothing.  y is [y_rows, N] (f32 or bf16, pitch
+ * ld_y), out is [tokens, N] (f32 or bf16 round-to-nearest-even, pitch
+ * ld_out), weights device fp32 [tokens, topk].  Requires N % 8 == 0.
+ */
+int mx_moe_combine(const void *y, int32_t y_dtype, int64_t ld_y, int64_t y_rows,
+                   const int32_t *dest_row, const float *weights, int64_t tokens, int32_t topk,
+                   int64_t N, void *out, int32_t out_dtype, int64_t ld_out, void *stream);
+
 /* Scratch bytes that op needs: desc is an mx_tensor* (MX_OP_QUANTIZE, with
-   flags as in mx_quantize) or an mx_gemm_args* (MX_OP_GEMM). */
+   flags as in mx_quantize), an mx_gemm_args* (MX_OP_GEMM) or a pointer to
+   the int32 expert count (MX_OP_MOE_ROUTE). */
 size_t mx_workspace_bytes(int32_t op, const void *desc, int32_t flags);
 
 /* Static, never-NULL description of a status code. */

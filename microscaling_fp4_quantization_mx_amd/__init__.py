@@ -17,7 +17,8 @@ __all__ = [
     "MXError", "MXTensor", "lib", "library_path", "MX_FMT_MXFP4", "MX_FMT_NVFP4", "MX_DT_F32", "MX_DT_BF16",
     "MX_QUANT_STATIC_GLOBAL", "MX_OP_QUANTIZE", "MX_OP_GEMM", "STATUS", "CMxTensor", "CMxGemmArgs",
     "empty_quantized", "mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemv", "mx_workspace_bytes",
-    "mx_status_string", "mx_version",
+    "mx_status_string", "mx_version", "MX_OP_MOE_ROUTE", "mx_moe_route", "mx_quantize_rows", "mx_moe_combine",
+    "moe_forward",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -26,7 +27,7 @@ library_path = os.path.join(_PKG, "libmx.so")
 MX_FMT_MXFP4, MX_FMT_NVFP4 = 0, 1
 MX_DT_F32, MX_DT_BF16 = 0, 1
 MX_QUANT_DEFAULT, MX_QUANT_STATIC_GLOBAL = 0, 1
-MX_OP_QUANTIZE, MX_OP_GEMM = 0, 1
+MX_OP_QUANTIZE, MX_OP_GEMM, MX_OP_MOE_ROUTE = 0, 1, 2
 STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_ALIGN", -4: "MX_ERR_DTYPE",
           -5: "MX_ERR_UNSUPPORTED", -6: "MX_ERR_HIP", -7: "MX_ERR_WORKSPACE", -8: "MX_ERR_FORMAT"}
 _FMT = {"mxfp4": MX_FMT_MXFP4, "nvfp4": MX_FMT_NVFP4}
@@ -75,6 +76,12 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm.restype = ctypes.c_int
         L.mx_gemv.argtypes = [vp, i32, i64, i64, ctypes.POINTER(CMxTensor), vp, i32, i64, vp]
         L.mx_gemv.restype = ctypes.c_int
+        L.mx_moe_route.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, sz, vp]
+        L.mx_moe_route.restype = ctypes.c_int
+        L.mx_quantize_rows.argtypes = [vp, i32, i64, i64, vp, ctypes.POINTER(CMxTensor), vp]
+        L.mx_quantize_rows.restype = ctypes.c_int
+        L.mx_moe_combine.argtypes = [vp, i32, i64, i64, vp, vp, i64, i32, i64, vp, i32, i64, vp]
+        L.mx_moe_combine.restype = ctypes.c_int
         L.mx_workspace_bytes.argtypes = [i32, vp, i32]
         L.mx_workspace_bytes.restype = sz
         L.mx_status_string.argtypes = [ctypes.c_int]
@@ -238,3 +245,70 @@ def mx_gemv(x, w: MXTensor, out=None):
     _check(lib().mx_gemv(x.data_ptr(), _dt(x), M, x.stride(0), ctypes.byref(d), out.data_ptr(), _dt(out),
                          out.stride(0), _stream(torch, x.device)), "mx_gemv")
     return out
+
+
+def mx_moe_route(topk_ids, experts: int, offsets=None, dest_row=None, src_token=None, workspace=None):
+    """Stable expert-sorted order of the (token, slot) pairs of an int32 CUDA
+    tensor topk_ids [tokens, topk].  Returns (offsets [experts+1],
+    dest_row [tokens*topk], src_token [tokens*topk]), int32 CUDA tensors."""
+    import torch
+    assert topk_ids.dim() == 2 and topk_ids.dtype == torch.int32 and topk_ids.is_contiguous()
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    if offsets is None:
+        offsets = torch.empty(experts + 1, dtype=torch.int32, device=dev)
+    if dest_row is None:
+        dest_row = torch.empty(T * k, dtype=torch.int32, device=dev)
+    if src_token is None:
+        src_token = torch.empty(T * k, dtype=torch.int32, device=dev)
+    e = ctypes.c_int32(experts)
+    need = int(lib().mx_workspace_bytes(MX_OP_MOE_ROUTE, ctypes.cast(ctypes.pointer(e), ctypes.c_void_p), 0))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _check(lib().mx_moe_route(topk_ids.data_ptr(), T, k, experts, offsets.data_ptr(), dest_row.data_ptr(),
+                              src_token.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream(torch, dev)),
+           "mx_moe_route")
+    return offsets, dest_row, src_token
+
+
+def mx_quantize_rows(x, row_index, out: MXTensor | None = None) -> MXTensor:
+    """MXFP4 quantization of the rows x[row_index[r]] (int32 CUDA tensor; an
+    index outside [0, x.shape[0]) gives a zero row)."""
+    import torch
+    assert x.dim() == 2 and x.stride(1) == 1 and row_index.dtype == torch.int32
+    R = row_index.numel()
+    if out is None:
+        out = empty_quantized(R, x.shape[1], "mxfp4", x.device)
+    d = out.desc()
+    _check(lib().mx_quantize_rows(x.data_ptr(), _dt(x), x.stride(0), x.shape[0], row_index.data_ptr(),
+                                  ctypes.byref(d), _stream(torch, x.device)), "mx_quantize_rows")
+    return out
+
+
+def mx_moe_combine(y, dest_row, weights, tokens: int, topk: int, out=None, out_dtype=None):
+    """out[t] = sum_s weights[t, s] * y[dest_row[t, s]] (fp32 accumulation)."""
+    import torch
+    out_dtype = out_dtype or torch.bfloat16
+    N = y.shape[1]
+    if out is None:
+        out = torch.empty(tokens, N, dtype=out_dtype, device=y.device)
+    _check(lib().mx_moe_combine(y.data_ptr(), _dt(y), y.stride(0), y.shape[0], dest_row.data_ptr(),
+                                weights.data_ptr(), tokens, topk, N, out.data_ptr(), _dt(out), out.stride(0),
+                                _stream(torch, y.device)), "mx_moe_combine")
+    return out
+
+
+def moe_forward(x, topk_ids, topk_weights, w: MXTensor, experts: int, N: int, y_dtype=None, out_dtype=None,
+                bufs: dict | None = None):
+    """A routed W4A4 expert layer: mx_moe_route, mx_quantize_rows, grouped
+    mx_gemm, mx_moe_combine, in that order on the current stream.  `bufs`
+    (optional) holds preallocated intermediates keyed by name."""
+    import torch
+    y_dtype = y_dtype or torch.bfloat16
+    T, k = topk_ids.shape
+    b = bufs if bufs is not None else {}
+    offsets, dest_row, src_token = mx_moe_route(topk_ids, experts, b.get("offsets"), b.get("dest_row"),
+                                                b.get("src_token"), b.get("route_ws"))
+    aq = mx_quantize_rows(x, src_token, b.get("aq"))
+    y = mx_gemm(aq, w, N=N, out=b.get("y"), out_dtype=y_dtype, groups=experts, offsets=offsets)
+    return mx_moe_combine(y, dest_row, topk_weights, T, k, out=b.get("out"), out_dtype=out_dtype)

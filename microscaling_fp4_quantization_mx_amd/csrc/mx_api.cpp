@@ -12,9 +12,12 @@ namespace {
 
 constexpr int64_t kMaxElems = int64_t(1) << 33;   // rows * cols limit (32-bit vector indices)
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxPairs = (int64_t(1) << 31) - 1;   // routed (token, slot) pairs: int32 row indices
+constexpr int32_t kMaxExperts = 1 << 16;
 constexpr size_t kNvPartialBytes = 4096 * sizeof(uint32_t);
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 inline int block_of(int32_t fmt) { return fmt == MX_FMT_MXFP4 ? 32 : 16; }
 inline size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 inline int esize(int32_t dt) { return dt == MX_DT_F32 ? 4 : 2; }
@@ -82,6 +85,10 @@ size_t mx_workspace_bytes(int32_t op, const void* desc, int32_t flags) {
     const mx_gemm_args* a = static_cast<const mx_gemm_args*>(desc);
     if (!a->a && !(a->a_codes_out && a->a_scales_out) && a->M > 0 && a->K > 0) return dyn_a_bytes(a->M, a->K);
     return 0;
+  }
+  if (op == MX_OP_MOE_ROUTE) {
+    const int32_t experts = *static_cast<const int32_t*>(desc);
+    return experts > 0 ? round256((size_t)experts * 4) : 0;
   }
   return 0;
 }
@@ -182,6 +189,52 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
                                           a->K, a->groups, a->group_offsets, s));
   return hip_status(mxk::launch_gemm_nv(a_codes, a_scales, a_global, a->b->codes, a->b->scales, a->b->global_scale,
                                         a->c, cbf, a->ldc, a->M, a->N, a->K, s));
+}
+
+int mx_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t experts, int32_t* offsets,
+                 int32_t* dest_row, int32_t* src_token, void* workspace, size_t workspace_bytes, void* stream) {
+  if (tokens < 0 || topk < 1 || experts < 1 || experts > kMaxExperts) return MX_ERR_SHAPE;
+  if (tokens > kMaxPairs / topk) return MX_ERR_SHAPE;
+  const int64_t npairs = tokens * topk;
+  if (!offsets) return MX_ERR_NULL;
+  if (npairs > 0 && (!topk_ids || !dest_row || !src_token)) return MX_ERR_NULL;
+  if (!al4(offsets) || (npairs > 0 && (!al4(topk_ids) || !al4(dest_row) || !al4(src_token)))) return MX_ERR_ALIGN;
+  if (!workspace || workspace_bytes < (size_t)experts * 4 || !al4(workspace)) return MX_ERR_WORKSPACE;
+  return hip_status(mxk::launch_moe_route(topk_ids, npairs, topk, experts, offsets, dest_row, src_token,
+                                          static_cast<int32_t*>(workspace), as_stream(stream)));
+}
+
+int mx_quantize_rows(const void* x, int32_t x_dtype, int64_t ld_x, int64_t x_rows, const int32_t* row_index,
+                     const mx_tensor* out, void* stream) {
+  int st = check_tensor(out);
+  if (st) return st;
+  if (out->fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
+  if (x_rows < 0) return MX_ERR_SHAPE;
+  st = check_dense_input(x, x_dtype, ld_x, x_rows, out->cols);
+  if (st) return st;
+  if (out->rows == 0 || out->cols == 0) return MX_OK;
+  if (!row_index) return MX_ERR_NULL;
+  if (!al4(row_index)) return MX_ERR_ALIGN;
+  if (x_rows > 0 && !x) return MX_ERR_NULL;
+  return hip_status(mxk::launch_quant_mx(x, x_dtype == MX_DT_BF16, ld_x, out->rows, out->cols, out->codes, out->scales,
+                                         as_stream(stream), row_index, x_rows));
+}
+
+int mx_moe_combine(const void* y, int32_t y_dtype, int64_t ld_y, int64_t y_rows, const int32_t* dest_row,
+                   const float* weights, int64_t tokens, int32_t topk, int64_t N, void* out, int32_t out_dtype,
+                   int64_t ld_out, void* stream) {
+  if (tokens < 0 || topk < 1 || N < 0 || y_rows < 0 || N > kMaxDim) return MX_ERR_SHAPE;
+  if (tokens > kMaxPairs / topk) return MX_ERR_SHAPE;
+  if (N % 8 != 0) return MX_ERR_UNSUPPORTED;
+  int st = check_dense_input(y, y_dtype, ld_y, y_rows, N);
+  if (st) return st;
+  st = check_dense_input(out, out_dtype, ld_out, tokens, N);
+  if (st) return st;
+  if (tokens == 0 || N == 0) return MX_OK;
+  if (!dest_row || !weights) return MX_ERR_NULL;
+  if (!al4(dest_row) || !al4(weights)) return MX_ERR_ALIGN;
+  return hip_status(mxk::launch_moe_combine(y, y_dtype == MX_DT_BF16, ld_y, y_rows, dest_row, weights, tokens, topk, N,
+                                            out, out_dtype == MX_DT_BF16, ld_out, as_stream(stream)));
 }
 
 int mx_gemv(const void* x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_tensor* w, void* y, int32_t y_dtype,

@@ -4,8 +4,10 @@
 #include <stdint.h>
 
 namespace mxk {
+// gidx != nullptr: output row r quantizes input row gidx[r] (zero row if the
+// index is outside [0, x_rows)).
 hipError_t launch_quant_mx(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
-                           uint8_t* scales, hipStream_t st);
+                           uint8_t* scales, hipStream_t st, const int32_t* gidx = nullptr, int64_t x_rows = 0);
 int nv_partials_count(int64_t rows, int64_t cols, int xdt_bf16);
 hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* gscale, bool static_global, uint32_t* partial, hipStream_t st);
@@ -19,4 +21,9 @@ hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const
                           int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st);
 hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st);
+hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int experts, int32_t* offsets,
+                            int32_t* dest_row, int32_t* src_token, int32_t* cnt, hipStream_t st);
+hipError_t launch_moe_combine(const void* y, int y_bf16, int64_t ldy, int64_t y_rows, const int32_t* dest_row,
+                              const float* w, int64_t tokens, int topk, int64_t N, void* out, int o_bf16, int64_t ldo,
+                              hipStream_t st);
 }  // namespace mxk

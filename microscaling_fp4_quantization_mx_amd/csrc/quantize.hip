@@ -39,10 +39,13 @@ __device__ __forceinline__ uint32_t block_umax(uint32_t v) {
   return v;
 }
 
-template <typename TIn, bool CONTIG>
+// MODE 0: contiguous rows; 1: rows ld apart; 2: output row r is input row
+// gidx[r] (an index outside [0, x_rows) gives a zero row).
+template <typename TIn, int MODE>
 __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr,
                                                  uint32_t nvec, uint8_t* __restrict__ codes,
-                                                 uint8_t* __restrict__ scales) {
+                                                 uint8_t* __restrict__ scales, const int32_t* __restrict__ gidx,
+                                                 int64_t x_rows) {
   constexpr int EPL = 16 / (int)sizeof(TIn);  // elements per vector
   constexpr int LPB = 32 / EPL;               // lanes per 32-element block
   const int lane = threadIdx.x & 63;
@@ -54,13 +57,19 @@ __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int6
     for (int u = 0; u < QU; ++u) {
       uint32_t v = base + u * 64 + lane;
       const TIn* p;
-      if (CONTIG) {
+      bool ok = v < nvec;
+      if (MODE == 0) {
         p = x + (size_t)v * EPL;
       } else {
         uint32_t r = v / vpr, c = v - r * vpr;
-        p = x + (size_t)r * ldx + (size_t)c * EPL;
+        int64_t src = r;
+        if (MODE == 2) {
+          src = ok ? (int64_t)gidx[r] : 0;
+          ok = ok && src >= 0 && src < x_rows;
+        }
+        p = x + (size_t)(ok ? src : 0) * ldx + (size_t)c * EPL;
       }
-      d[u] = (v < nvec) ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+      d[u] = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
     }
   };
   // the next iteration's vectors are in flight while this one is converted
@@ -298,23 +307,19 @@ static int grid_for(uint64_t work_items, int per_block) {
 }
 
 hipError_t launch_quant_mx(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
-                           uint8_t* scales, hipStream_t st) {
+                           uint8_t* scales, hipStream_t st, const int32_t* gidx, int64_t x_rows) {
   const int epl = xdt_bf16 ? 8 : 4;
   const uint32_t vpr = (uint32_t)(cols / epl);
   const uint32_t nvec = (uint32_t)(rows * cols / epl);
-  const bool contig = (ldx == cols);
+  const int mode = gidx ? 2 : (ldx == cols ? 0 : 1);
   const int grid = grid_for(nvec, QT * QU);
+#define MX_QMX(T, MODE) hipLaunchKernelGGL((k_quant_mx<T, MODE>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales, gidx, x_rows)
   if (xdt_bf16) {
-    if (contig)
-      hipLaunchKernelGGL((k_quant_mx<uint16_t, true>), dim3(grid), dim3(QT), 0, st, (const uint16_t*)x, ldx, vpr, nvec, codes, scales);
-    else
-      hipLaunchKernelGGL((k_quant_mx<uint16_t, false>), dim3(grid), dim3(QT), 0, st, (const uint16_t*)x, ldx, vpr, nvec, codes, scales);
+    if (mode == 0) MX_QMX(uint16_t, 0); else if (mode == 1) MX_QMX(uint16_t, 1); else MX_QMX(uint16_t, 2);
   } else {
-    if (contig)
-      hipLaunchKernelGGL((k_quant_mx<float, true>), dim3(grid), dim3(QT), 0, st, (const float*)x, ldx, vpr, nvec, codes, scales);
-    else
-      hipLaunchKernelGGL((k_quant_mx<float, false>), dim3(grid), dim3(QT), 0, st, (const float*)x, ldx, vpr, nvec, codes, scales);
+    if (mode == 0) MX_QMX(float, 0); else if (mode == 1) MX_QMX(float, 1); else MX_QMX(float, 2);
   }
+#undef MX_QMX
   return hipGetLastError();
 }
 

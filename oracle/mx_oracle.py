@@ -21,7 +21,7 @@ __all__ = [
     "mx_block_exponent", "mxfp4_quantize", "nvfp4_global_scale",
     "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize",
     "round_to_bf16", "gemm", "gemm_tolerance", "gemv", "grouped_gemm",
-    "naive_per_tensor_fp4", "storage_bytes",
+    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward",
 ]
 
 # Table "The Complete Discrete State Mapping of E2M1" ("NVFP4 Architecture",
@@ -366,6 +366,74 @@ def grouped_gemm(x: np.ndarray, offsets: np.ndarray, w_packed: np.ndarray, w_sca
         w_hat = dequantize("mxfp4", w_packed[g], w_scales[g])
         y[r0:r1] = gemm(a_hat, w_hat, out="bf16")
     return y, a_codes, a_scales
+
+
+def moe_route(topk_ids: np.ndarray, experts: int):
+    """Expert-sorted order of top-k routed (token, slot) pairs.  Routed expert
+    layers are where block-scaled FP4 gains most ("NVFP4 Architecture", section
+    "Strategic Recommendations: Adopting NVFP4 in 2026"; TopK and grouped GEMM
+    in the "MXFP4" card, section "Core Facts").  Reading: a stable sort by
+    expert id -- the pairs of one expert keep their flat order t * topk + s;
+    pairs whose id is outside [0, experts) are dropped (row -1).
+    Returns (offsets [experts+1], dest_row [T*topk], src_token [offsets[-1]])."""
+    ids = np.asarray(topk_ids, np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    dest = np.full(T * k, -1, np.int64)
+    offsets = np.zeros(experts + 1, np.int64)
+    src = []
+    row = 0
+    for g in range(experts):
+        offsets[g] = row
+        for p in range(T * k):          # flat order = stable
+            if flat[p] == g:
+                dest[p] = row
+                src.append(p // k)
+                row += 1
+    offsets[experts] = row
+    return offsets.astype(np.int32), dest.astype(np.int32), np.asarray(src, np.int32)
+
+
+def moe_combine(y: np.ndarray, dest_row: np.ndarray, weights: np.ndarray, tokens: int, topk: int) -> np.ndarray:
+    """out[t] = sum_s w[t, s] * y[dest_row[t, s]], summed in fp64 and rounded
+    once to fp32; pairs with row -1 add nothing."""
+    y = np.asarray(y, np.float64)
+    w = np.asarray(weights, np.float64).reshape(tokens, topk)
+    d = np.asarray(dest_row).reshape(tokens, topk)
+    out = np.zeros((tokens, y.shape[1]), np.float64)
+    for t in range(tokens):
+        for s in range(topk):
+            if 0 <= d[t, s] < y.shape[0]:
+                out[t] += w[t, s] * y[d[t, s]]
+    return out.astype(np.float32)
+
+
+def moe_forward(x: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w_packed: np.ndarray,
+                w_scales: np.ndarray, y_out: str = "bf16", out: str = "bf16"):
+    """A routed W4A4 expert layer: route, quantize each routed token's
+    activations to MXFP4 (in sorted order), multiply by its expert's MXFP4
+    weights (fp64 sums rounded to fp32, then to y_out), combine with the
+    routing weights.  x fp32 values [T, K]; w_packed [G, N, K/2]; w_scales
+    [G, N, K/32].  Returns (out [T, N], dict of the intermediates)."""
+    x = np.asarray(x, np.float32)
+    T, K = x.shape
+    G, N = w_packed.shape[0], w_packed.shape[1]
+    k = topk_ids.shape[1]
+    offsets, dest, src = moe_route(topk_ids, G)
+    xs = x[src] if len(src) else np.zeros((0, K), np.float32)
+    y, a_codes, a_scales = grouped_gemm(xs, offsets, w_packed, w_scales)
+    if y_out == "f32":
+        y = np.zeros((len(src), N), np.float32)
+        for g in range(G):
+            r0, r1 = int(offsets[g]), int(offsets[g + 1])
+            if r1 > r0:
+                y[r0:r1] = gemm(dequantize("mxfp4", a_codes[r0:r1], a_scales[r0:r1]),
+                                dequantize("mxfp4", w_packed[g], w_scales[g]), out="f32")
+    o = moe_combine(y, dest, topk_w, T, k)
+    if out == "bf16":
+        o = round_to_bf16(o)
+    return o, {"offsets": offsets, "dest_row": dest, "src_token": src, "y": y,
+               "a_codes": a_codes, "a_scales": a_scales}
 
 
 def naive_per_tensor_fp4(x: np.ndarray) -> np.ndarray:

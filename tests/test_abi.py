@@ -185,3 +185,34 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(mx, "library_path", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         mx.lib()
+
+
+def test_moe_validation():
+    L = mx.lib()
+    ws = FAKE
+    # mx_moe_route(ids, tokens, topk, experts, offsets, dest_row, src_token, ws, ws_bytes, stream)
+    assert L.mx_moe_route(FAKE, 10, 0, 8, FAKE, FAKE, FAKE, ws, 4096, None) == -2        # topk < 1
+    assert L.mx_moe_route(FAKE, 10, 2, 0, FAKE, FAKE, FAKE, ws, 4096, None) == -2        # experts < 1
+    assert L.mx_moe_route(FAKE, -1, 2, 8, FAKE, FAKE, FAKE, ws, 4096, None) == -2        # tokens < 0
+    assert L.mx_moe_route(FAKE, 1 << 30, 4, 8, FAKE, FAKE, FAKE, ws, 4096, None) == -2   # pairs >= 2^31
+    assert L.mx_moe_route(None, 10, 2, 8, FAKE, FAKE, FAKE, ws, 4096, None) == -1
+    assert L.mx_moe_route(FAKE, 10, 2, 8, None, FAKE, FAKE, ws, 4096, None) == -1
+    assert L.mx_moe_route(FAKE + 2, 10, 2, 8, FAKE, FAKE, FAKE, ws, 4096, None) == -3    # misaligned ids
+    assert L.mx_moe_route(FAKE, 10, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == -7         # no workspace
+    assert L.mx_moe_route(FAKE, 10, 2, 8, FAKE, FAKE, FAKE, ws, 16, None) == -7          # too small
+    e = ctypes.c_int32(300)
+    need = L.mx_workspace_bytes(mx.MX_OP_MOE_ROUTE, ctypes.cast(ctypes.pointer(e), ctypes.c_void_p), 0)
+    assert need >= 1200 and need % 256 == 0
+    # mx_quantize_rows(x, dtype, ld, x_rows, row_index, out, stream)
+    t = T(rows=16, cols=256)
+    assert L.mx_quantize_rows(FAKE, 0, 256, 10, None, ctypes.byref(t), None) == -1
+    assert L.mx_quantize_rows(FAKE, 0, 256, -1, FAKE, ctypes.byref(t), None) == -2
+    assert L.mx_quantize_rows(FAKE, 0, 100, 10, FAKE, ctypes.byref(t), None) == -2       # ld < cols
+    nv = T(fmt=1, rows=16, cols=256, g=FAKE)
+    assert L.mx_quantize_rows(FAKE, 0, 256, 10, FAKE, ctypes.byref(nv), None) == -5      # MXFP4 only
+    # mx_moe_combine(y, ydt, ldy, y_rows, dest, w, tokens, topk, N, out, odt, ldo, stream)
+    assert L.mx_moe_combine(FAKE, 1, 64, 10, FAKE, FAKE, 5, 2, 60, FAKE, 1, 64, None) == -5   # N % 8
+    assert L.mx_moe_combine(FAKE, 1, 64, 10, FAKE, FAKE, 5, 0, 64, FAKE, 1, 64, None) == -2   # topk < 1
+    assert L.mx_moe_combine(FAKE, 1, 64, 10, None, FAKE, 5, 2, 64, FAKE, 1, 64, None) == -1
+    assert L.mx_moe_combine(FAKE, 7, 64, 10, FAKE, FAKE, 5, 2, 64, FAKE, 1, 64, None) == -4   # dtype
+    assert L.mx_moe_combine(FAKE, 1, 60, 10, FAKE, FAKE, 5, 2, 56, FAKE, 1, 64, None) == -3   # row pitch

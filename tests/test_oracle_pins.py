@@ -544,3 +544,53 @@ def test_tolerance_covers_bf16_rounding():
     y = np.array([[3.0]], np.float32)
     tol = O.gemm_tolerance(a, b, y, out="bf16")
     assert np.isclose(tol[0, 0], 4e-5 + 2.0 ** -6)
+
+
+# ------------------------------------------------------ routed expert layers
+def test_moe_route_is_a_stable_sort_by_expert():
+    """The oracle's per-expert scan against Python's sort of (expert, flat
+    index) keys; invalid ids (outside [0, experts)) are dropped."""
+    rng = np.random.default_rng(31)
+    for T, k, G in [(0, 2, 3), (1, 1, 1), (7, 2, 4), (40, 3, 5), (25, 2, 8)]:
+        ids = rng.integers(-1, G + 1, size=(T, k)).astype(np.int32)   # includes -1 and G (invalid)
+        offs, dest, src = O.moe_route(ids, G)
+        keys = sorted((int(e), p) for p, e in enumerate(ids.reshape(-1)) if 0 <= e < G)
+        want_dest = np.full(T * k, -1)
+        for r, (e, p) in enumerate(keys):
+            want_dest[p] = r
+        assert np.array_equal(dest, want_dest)
+        assert np.array_equal(src, [p // k for _, p in keys])
+        assert offs[0] == 0 and offs[-1] == len(keys) and np.all(np.diff(offs) >= 0)
+        for g in range(G):
+            assert offs[g + 1] - offs[g] == sum(1 for e, _ in keys if e == g)
+
+
+def test_moe_forward_equals_direct_per_token_sum():
+    """Route + sorted grouped product + combine against the definition taken
+    token by token: out[t] = sum_s w[t,s] * (Q(x_t) . W_hat_{e(t,s)}^T), with
+    exact rational dot products (y kept in fp32 on the oracle side)."""
+    rng = np.random.default_rng(32)
+    T, K, N, G, k = 5, 64, 3, 3, 2
+    x = rng.standard_normal((T, K)).astype(np.float32)
+    w = (rng.standard_normal((G, N, K)) * 0.05).astype(np.float32)
+    ids = np.array([[0, 2], [2, 1], [1, 1], [-1, 0], [2, 0]], np.int32)   # a repeated and an invalid slot
+    tw = rng.random((T, k)).astype(np.float32)
+    wc = np.stack([O.mxfp4_quantize(w[g])[0] for g in range(G)])
+    ws = np.stack([O.mxfp4_quantize(w[g])[1] for g in range(G)])
+    out, inter = O.moe_forward(x, ids, tw, wc, ws, y_out="f32", out="f32")
+    for t in range(T):
+        c, s = O.mxfp4_quantize(x[t:t + 1])
+        a = O.dequantize("mxfp4", c, s)
+        for n in range(N):
+            exact = Fraction(0)
+            bound = Fraction(0)
+            for j in range(k):
+                e = int(ids[t, j])
+                if not 0 <= e < G:
+                    continue
+                b = O.dequantize("mxfp4", wc[e][n:n + 1], ws[e][n:n + 1])
+                d = _exact_dot_rows(a, b)[0][0]
+                exact += Fraction(float(tw[t, j])) * d
+                bound += abs(Fraction(float(tw[t, j]))) * (abs(d) + 1)
+            # y rounded to fp32, the combine rounded to fp32: two fp32 roundings
+            assert abs(Fraction(float(out[t, n])) - exact) <= bound * Fraction(1, 2 ** 22)

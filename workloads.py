@@ -20,7 +20,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
-W_ID, X_ID, COUNTS_ID, OUTLIER_COL_ID, OUTLIER_MUL_ID = 1, 2, 3, 4, 5
+W_ID, X_ID, COUNTS_ID, OUTLIER_COL_ID, OUTLIER_MUL_ID, ROUTER_ID = 1, 2, 3, 4, 5, 6
 
 
 def _rng(tensor_id: int, seed: int = 0) -> np.random.Generator:
@@ -70,6 +70,19 @@ def expert_offsets(tokens: int, experts: int, seed: int = 0) -> np.ndarray:
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
 
 
+def topk_routing(tokens: int, experts: int, topk: int, seed: int = 0):
+    """Top-k routing of a seeded router: logits ~ N(0, 1) [tokens, experts]
+    (tensor id 6); each token takes its topk largest logits (distinct
+    experts, largest first) with weights softmax over those topk logits.
+    Returns (ids int32 [tokens, topk], weights fp32 [tokens, topk])."""
+    logits = _rng(ROUTER_ID, seed).standard_normal(size=(tokens, experts), dtype=np.float32)
+    ids = np.argsort(-logits, axis=1, kind="stable")[:, :topk].astype(np.int32)
+    top = np.take_along_axis(logits, ids.astype(np.int64), axis=1).astype(np.float64)
+    e = np.exp(top - top.max(axis=1, keepdims=True))
+    w = (e / e.sum(axis=1, keepdims=True)).astype(np.float32)
+    return ids, w
+
+
 @dataclass(frozen=True)
 class Workload:
     name: str
@@ -92,6 +105,11 @@ C4 = Workload("nvfp4_quant_w4a4_gemm_2048x28672x8192", 2048, 28672, 8192, "nvfp4
 C5 = Workload("moe_dynquant_grouped_gemm_8x4096x14336_T8192", 8192, 4096, 14336, "mxfp4", "bf16", "bf16",
               "uniform", experts=8)
 GEMV_M = (1, 8, 16)
+# Routed expert layer around C5's grouped product: 4096 tokens, top-2 of 8
+# experts (8192 routed rows, the size of C5), same expert shapes.
+MOE = Workload("moe_top2_route_quant_grouped_combine_8x4096x14336_T4096", 4096, 4096, 14336, "mxfp4", "bf16",
+               "bf16", "uniform", experts=8)
+MOE_TOPK = 2
 
 
 def make(w: Workload, seed: int = 0, rows: int | None = None):
