@@ -278,6 +278,28 @@ def bench_moe(args, torch, mx, W):
             "note": f"{T} tokens, top-{k} of {G} experts, N={N}, K={K}: route + gathered quantize + grouped GEMM + combine"}
 
 
+def bench_rmsnorm(args, torch, mx, W):
+    """RMSNorm fused with MXFP4 (and static-scale NVFP4) quantization of bf16
+    tokens [8192, 14336] (the grouped workload's activations); two inputs
+    alternate so the last-level cache cannot hold them."""
+    w = W.C5
+    T, K = w.M, w.K
+    dev = torch.device("cuda:0")
+    d = W.make(w)
+    xs = [torch.from_numpy(d["x"]).to(torch.bfloat16).to(dev) for _ in range(2)]
+    gamma = torch.ones(K, dtype=torch.float32, device=dev)
+    res = {}
+    for fmt, k, sg in (("mxfp4", 32, None), ("nvfp4", 16, 0.01)):
+        outs = [mx.empty_quantized(T, K, fmt, dev) for _ in range(2)]
+        R = max(1, args.side_iters)
+        ms = time_graph(torch, capture(torch, lambda: [mx.mx_rmsnorm_quantize(xs[i], gamma, 1e-6, fmt, outs[i], sg)
+                                                       for i in (0, 1)], R), 2 * R)
+        byt = T * K * 2 + K * 4 + T * K // 2 + T * K // k
+        res[fmt] = {"avg_ms": ms, "GB/s": byt / (ms * 1e-3) / 1e9, "frac_hbm": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                    "bytes": byt}
+    return res
+
+
 def cpu_baseline(d):
     """The oracle, as it stands, on a bounded sub-problem of the same step:
     X rows 0..1023 and W rows 0..4095 (both quantized) and their GEMM."""
@@ -356,6 +378,9 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: fused dynamic-quantize grouped GEMM")
         sec["grouped_8x4096x14336_T8192"] = bench_grouped(args, torch, mx, W)
+        torch.cuda.empty_cache()
+        log("secondary: fused RMSNorm + FP4 quantize")
+        sec["rmsnorm_quantize_8192x14336_bf16"] = bench_rmsnorm(args, torch, mx, W)
         torch.cuda.empty_cache()
         log("secondary: routed expert layer (top-2)")
         sec["moe_top2_8x4096x14336_T4096"] = bench_moe(args, torch, mx, W)

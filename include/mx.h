@@ -213,6 +213,29 @@ int mx_moe_combine(const void *y, int32_t y_dtype, int64_t ld_y, int64_t y_rows,
                    const int32_t *dest_row, const float *weights, int64_t tokens, int32_t topk,
                    int64_t N, void *out, int32_t out_dtype, int64_t ld_out, void *stream);
 
+/*
+ * mx_rmsnorm_quantize -- RMSNorm fused with the FP4 quantization of its
+ * output, so the normalized activations never round-trip through HBM
+ * (dynamic re-quantization is the overhead "NVFP4 Architecture" names in
+ * section "The Problem"; RMSNorm belongs to an MXFP4 serving stack, "MXFP4"
+ * card, section "Core Facts").  Per row of x (bf16 [out->rows, out->cols],
+ * pitch ld_x):
+ *   s   = fp32 sum of x_k^2: thread t of 256 adds the squares of the
+ *         32-element chunks t, t+256, ... in element order, then the 256
+ *         partials are added as a pairwise tree over thread index (per 64,
+ *         then (w0 + w1) + (w2 + w3));
+ *   r   = fp32(1 / sqrt(s / K + eps)) evaluated in fp64;
+ *   y_k = fp32(fp32(x_k * r) * gamma_k)   (gamma fp32 or bf16 [K]);
+ * and y is quantized exactly as mx_quantize quantizes fp32 input: MXFP4
+ * (flags 0) or NVFP4 with the caller's per-tensor scale *out->global_scale
+ * (flags MX_QUANT_STATIC_GLOBAL: no tensor-wide max pass).
+ * Requires K % 32 == 0 and K <= 32768 (else MX_ERR_UNSUPPORTED) and eps > 0
+ * (so an all-zero row stays finite; else MX_ERR_SHAPE).
+ */
+int mx_rmsnorm_quantize(const void *x, int32_t x_dtype, int64_t ld_x, const void *gamma,
+                        int32_t gamma_dtype, float eps, const mx_tensor *out, int32_t flags,
+                        void *stream);
+
 /* Scratch bytes that op needs: desc is an mx_tensor* (MX_OP_QUANTIZE, with
    flags as in mx_quantize), an mx_gemm_args* (MX_OP_GEMM) or a pointer to
    the int32 expert count (MX_OP_MOE_ROUTE). */

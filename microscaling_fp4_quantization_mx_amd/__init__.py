@@ -18,7 +18,7 @@ __all__ = [
     "MX_QUANT_STATIC_GLOBAL", "MX_OP_QUANTIZE", "MX_OP_GEMM", "STATUS", "CMxTensor", "CMxGemmArgs",
     "empty_quantized", "mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemv", "mx_workspace_bytes",
     "mx_status_string", "mx_version", "MX_OP_MOE_ROUTE", "mx_moe_route", "mx_quantize_rows", "mx_moe_combine",
-    "moe_forward",
+    "moe_forward", "mx_rmsnorm_quantize",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +82,8 @@ def lib() -> ctypes.CDLL:
         L.mx_quantize_rows.restype = ctypes.c_int
         L.mx_moe_combine.argtypes = [vp, i32, i64, i64, vp, vp, i64, i32, i64, vp, i32, i64, vp]
         L.mx_moe_combine.restype = ctypes.c_int
+        L.mx_rmsnorm_quantize.argtypes = [vp, i32, i64, vp, i32, ctypes.c_float, ctypes.POINTER(CMxTensor), i32, vp]
+        L.mx_rmsnorm_quantize.restype = ctypes.c_int
         L.mx_workspace_bytes.argtypes = [i32, vp, i32]
         L.mx_workspace_bytes.restype = sz
         L.mx_status_string.argtypes = [ctypes.c_int]
@@ -312,3 +314,22 @@ def moe_forward(x, topk_ids, topk_weights, w: MXTensor, experts: int, N: int, y_
     aq = mx_quantize_rows(x, src_token, b.get("aq"))
     y = mx_gemm(aq, w, N=N, out=b.get("y"), out_dtype=y_dtype, groups=experts, offsets=offsets)
     return mx_moe_combine(y, dest_row, topk_weights, T, k, out=b.get("out"), out_dtype=out_dtype)
+
+
+def mx_rmsnorm_quantize(x, gamma, eps: float = 1e-6, fmt="mxfp4", out: MXTensor | None = None,
+                        static_global=None) -> MXTensor:
+    """RMSNorm of bf16 rows (gamma fp32/bf16 [K]) quantized in the same kernel
+    to MXFP4, or to NVFP4 with the given static per-tensor scale."""
+    import torch
+    assert x.dim() == 2 and x.stride(1) == 1 and gamma.is_contiguous()
+    rows, cols = x.shape
+    if out is None:
+        out = empty_quantized(rows, cols, fmt, x.device)
+    flags = MX_QUANT_DEFAULT
+    if static_global is not None:
+        out.global_scale.fill_(float(static_global))
+        flags = MX_QUANT_STATIC_GLOBAL
+    d = out.desc()
+    _check(lib().mx_rmsnorm_quantize(x.data_ptr(), _dt(x), x.stride(0), gamma.data_ptr(), _dt(gamma), float(eps),
+                                     ctypes.byref(d), flags, _stream(torch, x.device)), "mx_rmsnorm_quantize")
+    return out

@@ -16,14 +16,15 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmx.so")
-SOURCES = ["quantize.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemv.hip", "moe.hip", "mx_api.cpp"]
+SOURCES = ["quantize.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemv.hip", "moe.hip", "norm_quant.hip", "mx_api.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code (the compiler
 # would otherwise form v_pk_* fp32 ops from scalar and float2 arithmetic).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
-          "-Wno-unused-command-line-argument"]
+# Only the C entry points of include/mx.h are exported (mx_api.cpp marks them).
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", f"--offload-arch={ARCH}", "-I",
+          os.path.join(ROOT, "include"), "-Wno-unused-command-line-argument"]
 
 
 def hipcc() -> str:

@@ -14,6 +14,7 @@ constexpr int64_t kMaxElems = int64_t(1) << 33;   // rows * cols limit (32-bit v
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
 constexpr int64_t kMaxPairs = (int64_t(1) << 31) - 1;   // routed (token, slot) pairs: int32 row indices
 constexpr int32_t kMaxExperts = 1 << 16;
+constexpr int64_t kMaxNormCols = 256 * 32 * 4;   // fused RMSNorm: a row stays in one workgroup's registers
 constexpr size_t kNvPartialBytes = 4096 * sizeof(uint32_t);
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -55,6 +56,7 @@ size_t dyn_a_bytes(int64_t M, int64_t K) { return round256((size_t)(M * K / 2)) 
 
 }  // namespace
 
+#pragma GCC visibility push(default)
 extern "C" {
 
 const char* mx_status_string(int status) {
@@ -237,6 +239,25 @@ int mx_moe_combine(const void* y, int32_t y_dtype, int64_t ld_y, int64_t y_rows,
                                             out, out_dtype == MX_DT_BF16, ld_out, as_stream(stream)));
 }
 
+int mx_rmsnorm_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const void* gamma, int32_t gamma_dtype,
+                        float eps, const mx_tensor* out, int32_t flags, void* stream) {
+  int st = check_tensor(out);
+  if (st) return st;
+  if (x_dtype != MX_DT_BF16 || !dtype_ok(gamma_dtype)) return MX_ERR_DTYPE;
+  if (!(eps > 0.0f) || eps > 3.0e38f) return MX_ERR_SHAPE;   // eps > 0 keeps an all-zero row finite
+  if (out->fmt == MX_FMT_MXFP4 && flags != MX_QUANT_DEFAULT) return MX_ERR_UNSUPPORTED;
+  if (out->fmt == MX_FMT_NVFP4 && flags != MX_QUANT_STATIC_GLOBAL) return MX_ERR_UNSUPPORTED;
+  if (out->cols % 32 != 0 || out->cols > kMaxNormCols) return MX_ERR_UNSUPPORTED;
+  st = check_dense_input(x, x_dtype, ld_x, out->rows, out->cols);
+  if (st) return st;
+  if (out->rows == 0 || out->cols == 0) return MX_OK;
+  if (!gamma) return MX_ERR_NULL;
+  if (!al16(gamma)) return MX_ERR_ALIGN;
+  return hip_status(mxk::launch_rmsnorm_quant(x, ld_x, out->rows, out->cols, gamma, gamma_dtype == MX_DT_BF16, eps,
+                                              out->fmt == MX_FMT_NVFP4, out->codes, out->scales, out->global_scale,
+                                              as_stream(stream)));
+}
+
 int mx_gemv(const void* x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_tensor* w, void* y, int32_t y_dtype,
             int64_t ld_y, void* stream) {
   int st = check_tensor(w);
@@ -256,3 +277,4 @@ int mx_gemv(const void* x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_te
 }
 
 }  // extern "C"
+#pragma GCC visibility pop

@@ -26,4 +26,7 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int ex
 hipError_t launch_moe_combine(const void* y, int y_bf16, int64_t ldy, int64_t y_rows, const int32_t* dest_row,
                               const float* w, int64_t tokens, int topk, int64_t N, void* out, int o_bf16, int64_t ldo,
                               hipStream_t st);
+hipError_t launch_rmsnorm_quant(const void* x, int64_t ldx, int64_t rows, int64_t K, const void* gamma, int g_bf16,
+                                float eps, bool nv, uint8_t* codes, uint8_t* scales, const float* gscale,
+                                hipStream_t st);
 }  // namespace mxk

@@ -12,6 +12,8 @@ Conventions shared with the library's public format (a format, not code):
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 __all__ = [
@@ -21,7 +23,7 @@ __all__ = [
     "mx_block_exponent", "mxfp4_quantize", "nvfp4_global_scale",
     "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize",
     "round_to_bf16", "gemm", "gemm_tolerance", "gemv", "grouped_gemm",
-    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward",
+    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward", "rmsnorm_values", "rmsnorm_quantize",
 ]
 
 # Table "The Complete Discrete State Mapping of E2M1" ("NVFP4 Architecture",
@@ -434,6 +436,54 @@ def moe_forward(x: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w_packe
         o = round_to_bf16(o)
     return o, {"offsets": offsets, "dest_row": dest, "src_token": src, "y": y,
                "a_codes": a_codes, "a_scales": a_scales}
+
+
+def rmsnorm_values(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of bf16-valued rows, in the fixed fp32 order this library
+    defines so that the quantized result is reproducible (RMSNorm appears on
+    the pages only as an operation of an MXFP4 serving stack, "MXFP4" card,
+    section "Core Facts"; its order of summation is therefore a reading):
+      s = sum of x_k^2 in fp32: partial p_t over the 32-element chunks
+          t, t+256, t+512, ... in element order (t = 0..255), then a
+          pairwise tree over t within groups of 64, then (g0+g1)+(g2+g3);
+      r = fp32(1 / sqrt(s / K + eps)) computed in fp64;
+      y = fp32(fp32(x * r) * gamma)."""
+    x = np.asarray(x, np.float32)
+    gamma = np.asarray(gamma, np.float32)
+    R, K = x.shape
+    nch = K // 32
+    # part[:, t] accumulates, in order, the squares of chunks t, t+256, ...
+    part = np.zeros((R, 256), np.float32)
+    for j in range((nch + 255) // 256):
+        for e in range(32):
+            t = np.arange(256)
+            c = t + 256 * j
+            ok = c < nch
+            sq = np.zeros((R, 256), np.float32)
+            sq[:, ok] = x[:, c[ok] * 32 + e] * x[:, c[ok] * 32 + e]
+            part = (part + sq).astype(np.float32)
+    groups = []
+    for w in range(4):
+        q = part[:, 64 * w:64 * (w + 1)]
+        while q.shape[1] > 1:
+            q = (q[:, 0::2] + q[:, 1::2]).astype(np.float32)
+        groups.append(q[:, 0])
+    s = ((groups[0] + groups[1]).astype(np.float32) + (groups[2] + groups[3]).astype(np.float32)).astype(np.float32)
+    y = np.empty_like(x)
+    for i in range(R):
+        r = np.float32(1.0 / math.sqrt(float(s[i]) / K + float(eps)))
+        y[i] = ((x[i] * r).astype(np.float32) * gamma).astype(np.float32)
+    return y
+
+
+def rmsnorm_quantize(x: np.ndarray, gamma: np.ndarray, eps: float, fmt: str = "mxfp4", global_scale=None):
+    """RMSNorm (rmsnorm_values) followed by block quantization of its fp32
+    output: MXFP4, or NVFP4 with a given static per-tensor scale."""
+    y = rmsnorm_values(x, gamma, eps)
+    if fmt == "mxfp4":
+        return mxfp4_quantize(y)
+    c, s, _ = nvfp4_quantize(y, global_scale=global_scale)
+    return c, s
 
 
 def naive_per_tensor_fp4(x: np.ndarray) -> np.ndarray:

@@ -216,3 +216,18 @@ def test_moe_validation():
     assert L.mx_moe_combine(FAKE, 1, 64, 10, None, FAKE, 5, 2, 64, FAKE, 1, 64, None) == -1
     assert L.mx_moe_combine(FAKE, 7, 64, 10, FAKE, FAKE, 5, 2, 64, FAKE, 1, 64, None) == -4   # dtype
     assert L.mx_moe_combine(FAKE, 1, 60, 10, FAKE, FAKE, 5, 2, 56, FAKE, 1, 64, None) == -3   # row pitch
+
+
+def test_rmsnorm_quantize_validation():
+    L = mx.lib()
+    t = T(rows=16, cols=256)
+    f = ctypes.c_float
+    assert L.mx_rmsnorm_quantize(FAKE, 0, 256, FAKE, 0, f(1e-6), ctypes.byref(t), 0, None) == -4   # x must be bf16
+    assert L.mx_rmsnorm_quantize(FAKE, 1, 256, FAKE, 9, f(1e-6), ctypes.byref(t), 0, None) == -4   # gamma dtype
+    assert L.mx_rmsnorm_quantize(FAKE, 1, 256, FAKE, 0, f(0.0), ctypes.byref(t), 0, None) == -2    # eps > 0
+    assert L.mx_rmsnorm_quantize(FAKE, 1, 256, None, 0, f(1e-6), ctypes.byref(t), 0, None) == -1
+    assert L.mx_rmsnorm_quantize(FAKE, 1, 256, FAKE, 0, f(1e-6), ctypes.byref(t), 1, None) == -5   # MXFP4: no flags
+    nv = T(fmt=1, rows=16, cols=256, g=FAKE)
+    assert L.mx_rmsnorm_quantize(FAKE, 1, 256, FAKE, 0, f(1e-6), ctypes.byref(nv), 0, None) == -5  # NVFP4: static only
+    big = T(rows=2, cols=32768 + 32)
+    assert L.mx_rmsnorm_quantize(FAKE, 1, 32800, FAKE, 0, f(1e-6), ctypes.byref(big), 0, None) == -5

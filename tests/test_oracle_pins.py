@@ -594,3 +594,48 @@ def test_moe_forward_equals_direct_per_token_sum():
                 bound += abs(Fraction(float(tw[t, j]))) * (abs(d) + 1)
             # y rounded to fp32, the combine rounded to fp32: two fp32 roundings
             assert abs(Fraction(float(out[t, n])) - exact) <= bound * Fraction(1, 2 ** 22)
+
+
+# ------------------------------------------------------- fused RMSNorm + FP4
+def test_rmsnorm_values_close_to_fp64_definition():
+    """The fixed-order fp32 normalization against RMSNorm in fp64: the sum of
+    K squares in fp32 (at most 4*32 sequential adds then 8 tree levels) is
+    within (136) * 2^-24 relative, so y is within a few hundred fp32 ulps."""
+    rng = np.random.default_rng(41)
+    for K in (32, 256, 8192 + 64, 14336):
+        x = torch.from_numpy((rng.standard_normal((3, K)) * rng.uniform(0.1, 40, (3, 1))).astype(np.float32)).to(
+            torch.bfloat16).float().numpy()
+        gamma = rng.uniform(0.5, 2.0, K).astype(np.float32)
+        y = O.rmsnorm_values(x, gamma, 1e-6)
+        x64 = x.astype(np.float64)
+        y64 = x64 / np.sqrt((x64 * x64).mean(axis=1, keepdims=True) + 1e-6) * gamma
+        assert np.all(np.abs(y - y64) <= np.abs(y64) * 200 * 2.0 ** -24 + 1e-30)
+
+
+def test_rmsnorm_sum_order_special_cases():
+    # constant rows: every partial is exact, so s = K c^2 exactly
+    K = 512
+    x = np.full((2, K), 0.75, np.float32)
+    x[1] = -3.0
+    y = O.rmsnorm_values(x, np.ones(K, np.float32), 0.0)
+    assert np.all(np.abs(y - np.sign(x)) <= 2.0 ** -23)
+    # zero row: r = 1/sqrt(eps), y = 0 with x's sign; codes are signed zeros
+    z = np.zeros((1, 64), np.float32)
+    z[0, 5] = -0.0
+    c, s = O.rmsnorm_quantize(z, np.ones(64, np.float32), 1e-5)
+    assert np.all(O.unpack_codes(c)[0, [i for i in range(64) if i != 5]] == 0)
+    assert O.unpack_codes(c)[0, 5] == 8 and np.all(s == 98)
+
+
+def test_rmsnorm_quantize_is_quantize_of_values():
+    rng = np.random.default_rng(42)
+    x = torch.from_numpy(rng.standard_normal((4, 1024)).astype(np.float32) * 5).to(torch.bfloat16).float().numpy()
+    gamma = rng.uniform(-2, 2, 1024).astype(np.float32)
+    y = O.rmsnorm_values(x, gamma, 1e-6)
+    c1, s1 = O.rmsnorm_quantize(x, gamma, 1e-6)
+    c2, s2 = O.mxfp4_quantize(y)
+    assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
+    g = np.float32(0.01)
+    c3, s3 = O.rmsnorm_quantize(x, gamma, 1e-6, "nvfp4", global_scale=g)
+    c4, s4, _ = O.nvfp4_quantize(y, global_scale=g)
+    assert np.array_equal(c3, c4) and np.array_equal(s3, s4)
