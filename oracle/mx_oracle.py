@@ -23,7 +23,7 @@ __all__ = [
     "mx_block_exponent", "mxfp4_quantize", "nvfp4_global_scale",
     "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize",
     "round_to_bf16", "gemm", "gemm_tolerance", "gemv", "grouped_gemm",
-    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward", "rmsnorm_values", "rmsnorm_quantize",
+    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward", "rmsnorm_values", "rmsnorm_quantize", "MX_ELEMENT_FORMATS", "element_bits", "element_positive_values", "element_nearest_code", "mx_block_exponent_fmt", "pack_elements", "unpack_elements", "mx_quantize_fmt", "dequantize_fmt",
 ]
 
 # Table "The Complete Discrete State Mapping of E2M1" ("NVFP4 Architecture",
@@ -368,6 +368,133 @@ def grouped_gemm(x: np.ndarray, offsets: np.ndarray, w_packed: np.ndarray, w_sca
         w_hat = dequantize("mxfp4", w_packed[g], w_scales[g])
         y[r0:r1] = gemm(a_hat, w_hat, out="bf16")
     return y, a_codes, a_scales
+
+
+# ---------------------------------------------------------------------------
+# The wider members of the MX family: MXFP8 (E4M3, E5M2) and MXFP6 (E2M3,
+# E3M2) elements with the same 32-element blocks and E8M0 scales ("MXFP4"
+# card, section "Core Facts": MXFP8/MXFP4 scaled GEMM; "How Microscaling FP4
+# (MXFP4)...", section "The Representation Dilemma: E2M1 vs. E3M0" for the
+# element/exponent trade-off).  Reading: the pages' scale rule carries over
+# with the format's largest finite value Emax in place of 6 -- e is the
+# smallest integer with amax <= Emax * 2^e (amax >= fp32(1e-8) as in the
+# emulation) -- and elements round to nearest, ties to the even code.
+# ---------------------------------------------------------------------------
+MX_ELEMENT_FORMATS = {
+    # name: (exponent bits, mantissa bits, bias, largest finite value)
+    "mxfp8_e4m3": (4, 3, 7, 448.0),
+    "mxfp8_e5m2": (5, 2, 15, 57344.0),
+    "mxfp6_e2m3": (2, 3, 1, 7.5),
+    "mxfp6_e3m2": (3, 2, 3, 28.0),
+    "mxfp4": (2, 1, 1, 6.0),
+}
+
+
+def element_bits(fmt: str) -> int:
+    E, M, _, _ = MX_ELEMENT_FORMATS[fmt]
+    return 1 + E + M
+
+
+def element_positive_values(fmt: str) -> np.ndarray:
+    """Values of the non-negative finite codes 0, 1, 2, ... of a minifloat
+    (sign bit clear), from the fields: exponent field 0 is subnormal
+    (m / 2^M * 2^(1-bias)), otherwise (1 + m / 2^M) * 2^(e - bias); codes
+    above Emax (E4M3's NaN, E5M2's infinities and NaNs) are excluded."""
+    E, M, bias, emax = MX_ELEMENT_FORMATS[fmt]
+    vals = []
+    for code in range(1 << (E + M)):
+        e, m = code >> M, code & ((1 << M) - 1)
+        v = (m / 2.0 ** M) * 2.0 ** (1 - bias) if e == 0 else (1 + m / 2.0 ** M) * 2.0 ** (e - bias)
+        if v > emax:
+            break
+        vals.append(v)
+    return np.array(vals, np.float64)
+
+
+def element_nearest_code(v: np.ndarray, fmt: str) -> np.ndarray:
+    """Code of the non-negative value nearest to v >= 0 (exact fp64 inputs),
+    ties to the even code, v above Emax saturating to Emax."""
+    table = element_positive_values(fmt)
+    v = np.asarray(v, np.float64)
+    d = np.abs(v[..., None] - table)
+    idx = np.argmin(d, axis=-1)
+    tie = (idx % 2 == 1) & (idx + 1 < len(table))
+    nxt = np.minimum(idx + 1, len(table) - 1)
+    tie &= np.take_along_axis(d, nxt[..., None], -1)[..., 0] == np.take_along_axis(d, idx[..., None], -1)[..., 0]
+    return np.where(tie, nxt, idx).astype(np.int64)
+
+
+def mx_block_exponent_fmt(amax: np.ndarray, fmt: str) -> np.ndarray:
+    """Smallest integer e with amax <= Emax * 2^e, amax first raised to
+    fp32(1e-8); exact (a correction loop around the fp64 log2 estimate)."""
+    emax = MX_ELEMENT_FORMATS[fmt][3]
+    a = np.maximum(np.asarray(amax, np.float64), float(np.float32(1e-8)))
+    e = np.ceil(np.log2(a / emax)).astype(np.int64)
+    e = np.where(emax * np.exp2(e.astype(np.float64)) < a, e + 1, e)
+    e = np.where(emax * np.exp2((e - 1).astype(np.float64)) >= a, e - 1, e)
+    return e
+
+
+def pack_elements(codes: np.ndarray, bits: int) -> np.ndarray:
+    """[R, K] codes of `bits` bits -> [R, K*bits/8] bytes, element i at bits
+    [bits*i, bits*i + bits) of the row's little-endian bit stream."""
+    codes = np.asarray(codes, np.uint64)
+    R, K = codes.shape
+    if bits == 8:
+        return codes.astype(np.uint8)
+    if bits == 4:
+        return pack_codes(codes.astype(np.uint8))
+    assert bits == 6 and K % 4 == 0
+    g = codes.reshape(R, K // 4, 4)
+    word = g[..., 0] | (g[..., 1] << 6) | (g[..., 2] << 12) | (g[..., 3] << 18)
+    out = np.stack([(word >> (8 * b)) & 0xFF for b in range(3)], axis=-1)
+    return out.reshape(R, K * 3 // 4).astype(np.uint8)
+
+
+def unpack_elements(packed: np.ndarray, bits: int) -> np.ndarray:
+    packed = np.asarray(packed, np.uint8)
+    R = packed.shape[0]
+    if bits == 8:
+        return packed.astype(np.int64)
+    if bits == 4:
+        return unpack_codes(packed).astype(np.int64)
+    g = packed.reshape(R, -1, 3).astype(np.uint64)
+    word = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)
+    out = np.stack([(word >> (6 * i)) & 0x3F for i in range(4)], axis=-1)
+    return out.reshape(R, -1).astype(np.int64)
+
+
+def mx_quantize_fmt(x: np.ndarray, fmt: str):
+    """MX quantization of a row-major [R, K] fp32 tensor (K % 32 == 0) with
+    elements of `fmt`: per 32-element block the E8M0 byte e + 127 and each
+    element the code nearest to x / 2^e (sign bit = x's sign).
+    Returns (packed codes [R, K*bits/8], scale bytes [R, K/32])."""
+    x = np.asarray(x, np.float32)
+    R, K = x.shape
+    bits = element_bits(fmt)
+    xb = x.reshape(R, K // 32, 32).astype(np.float64)
+    amax = np.abs(xb).max(axis=-1)
+    e = mx_block_exponent_fmt(amax, fmt)
+    mag = np.abs(xb) * np.exp2(-e.astype(np.float64))[..., None]
+    idx = element_nearest_code(mag, fmt)
+    sign = np.signbit(x.reshape(R, K // 32, 32)).astype(np.int64)
+    codes = idx | (sign << (bits - 1))
+    return pack_elements(codes.reshape(R, K), bits), (e + 127).astype(np.uint8)
+
+
+def dequantize_fmt(fmt: str, packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """x_hat = value(code) * 2^(E - 127) for the MX element formats (exact in
+    fp32 for every format and scale the quantizer emits)."""
+    bits = element_bits(fmt)
+    codes = unpack_elements(packed, bits)
+    R, K = codes.shape
+    E, M, bias, _ = MX_ELEMENT_FORMATS[fmt]
+    mag_code = codes & ((1 << (bits - 1)) - 1)
+    e, m = mag_code >> M, mag_code & ((1 << M) - 1)
+    mag = np.where(e == 0, m / 2.0 ** M * 2.0 ** (1 - bias), (1 + m / 2.0 ** M) * np.exp2((e - bias).astype(np.float64)))
+    val = np.where((codes >> (bits - 1)) & 1, -mag, mag)
+    s = np.exp2(np.asarray(scales, np.float64) - 127.0)
+    return (val.reshape(R, K // 32, 32) * s[..., None]).reshape(R, K).astype(np.float32)
 
 
 def moe_route(topk_ids: np.ndarray, experts: int):

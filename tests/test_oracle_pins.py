@@ -639,3 +639,165 @@ def test_rmsnorm_quantize_is_quantize_of_values():
     c3, s3 = O.rmsnorm_quantize(x, gamma, 1e-6, "nvfp4", global_scale=g)
     c4, s4, _ = O.nvfp4_quantize(y, global_scale=g)
     assert np.array_equal(c3, c4) and np.array_equal(s3, s4)
+
+
+# ------------------------------------------------ MXFP8 / MXFP6 element formats
+# Closed-form value sets of the wider MX elements, written from the field
+# definitions (sign, exponent with bias, mantissa; exponent field 0 subnormal).
+def _closed_form_values(fmt):
+    if fmt == "mxfp6_e2m3":        # bias 1: subnormals k/8, then steps 1/8, 1/4, 1/2
+        return ([Fraction(k, 8) for k in range(16)] + [2 + Fraction(k, 4) for k in range(8)]
+                + [4 + Fraction(k, 2) for k in range(8)])
+    if fmt == "mxfp6_e3m2":        # bias 3: subnormals k/16, normals 2^(e-3)(1 + m/4)
+        return [Fraction(k, 16) for k in range(4)] + [Fraction(2) ** (e - 3) * (1 + Fraction(m, 4))
+                                                       for e in range(1, 8) for m in range(4)]
+    raise KeyError(fmt)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp6_e2m3", "mxfp6_e3m2"])
+def test_fp6_value_tables_closed_form(fmt):
+    ref = _closed_form_values(fmt)
+    got = O.element_positive_values(fmt)
+    assert len(got) == 32 and [Fraction(float(v)) for v in got] == ref
+    assert float(ref[-1]) == O.MX_ELEMENT_FORMATS[fmt][3]
+
+
+@pytest.mark.parametrize("fmt,dt,n", [("mxfp8_e4m3", torch.float8_e4m3fn, 127),
+                                      ("mxfp8_e5m2", torch.float8_e5m2, 124)])
+def test_fp8_value_tables_match_torch(fmt, dt, n):
+    codes = torch.arange(n, dtype=torch.uint8).view(dt).float().double().numpy()
+    got = O.element_positive_values(fmt)
+    assert len(got) == n and np.array_equal(got, codes)
+
+
+def _bf_exponent(amax: Fraction, emax: Fraction) -> int:
+    """Smallest integer e with amax <= emax * 2^e, by stepping."""
+    e = 0
+    while amax > emax * Fraction(2) ** e:
+        e += 1
+    while amax <= emax * Fraction(2) ** (e - 1):
+        e -= 1
+    return e
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8_e4m3", "mxfp8_e5m2", "mxfp6_e2m3", "mxfp6_e3m2", "mxfp4"])
+def test_fmt_block_exponent_bruteforce(fmt):
+    emax = Fraction(O.MX_ELEMENT_FORMATS[fmt][3])
+    floor_amax = Fraction(float(np.float32(1e-8)))
+    rng = np.random.default_rng(11)
+    am = np.concatenate([np.exp2(rng.uniform(-40, 40, 300)).astype(np.float32),
+                         np.float32(float(emax)) * np.exp2(np.arange(-5, 6)).astype(np.float32),
+                         np.nextafter(np.float32(float(emax)), np.float32(np.inf)) * np.float32([1, 2, 0.5]),
+                         np.float32([0.0, 1e-12, 1e-8])])
+    got = O.mx_block_exponent_fmt(am, fmt)
+    for a, e in zip(am, got):
+        assert e == _bf_exponent(max(Fraction(float(a)), floor_amax), emax), (fmt, a)
+    # the floor: -27 minus the exponent of Emax (the 1e-8 guard)
+    p = int(np.floor(np.log2(float(emax))))
+    assert O.mx_block_exponent_fmt(np.float32([0.0]), fmt)[0] == -27 - p
+
+
+@pytest.mark.parametrize("fmt,dt", [("mxfp8_e4m3", torch.float8_e4m3fn), ("mxfp8_e5m2", torch.float8_e5m2)])
+def test_fp8_quantize_matches_torch_cast(fmt, dt):
+    """Elements: torch's round-to-nearest-even float8 cast of x / 2^e, with e
+    from the brute-force exponent search."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((6, 128)) * np.exp2(rng.integers(-20, 20, (6, 1)))).astype(np.float32)
+    x[0, :32] = 0.0
+    x[1, 5] = -x[1, 5] * 1e4
+    codes, scales = O.mx_quantize_fmt(x, fmt)
+    emax = Fraction(O.MX_ELEMENT_FORMATS[fmt][3])
+    fl = Fraction(float(np.float32(1e-8)))
+    e = np.array([[_bf_exponent(max(Fraction(float(np.abs(b).max())), fl), emax) for b in row.reshape(-1, 32)]
+                  for row in x])
+    assert np.array_equal(scales, (e + 127).astype(np.uint8))
+    scaled = (x.reshape(6, 4, 32).astype(np.float64) * np.exp2(-e.astype(np.float64))[..., None]).reshape(6, 128)
+    ref = torch.from_numpy(scaled).float().to(dt).view(torch.uint8).numpy()
+    assert np.array_equal(codes, ref)
+
+
+def _bf_nearest_fr(v: Fraction, table) -> int:
+    best, bd = None, None
+    for i, t in enumerate(table):
+        d = abs(v - t)
+        if bd is None or d < bd or (d == bd and i % 2 == 0):
+            best, bd = i, d
+    return best
+
+
+@pytest.mark.parametrize("fmt", ["mxfp6_e2m3", "mxfp6_e3m2"])
+def test_fp6_quantize_bruteforce(fmt):
+    """Exact rational brute force over the closed-form table, including
+    values placed exactly half-way between neighbouring states."""
+    table = _closed_form_values(fmt)
+    emax = table[-1]
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 64)).astype(np.float32)
+    x[0, :32] = np.float32([float(t) for t in table])                     # every state exactly
+    mids = [(table[i] + table[i + 1]) / 2 for i in range(31)]
+    x[1, :31] = np.float32([float(m) for m in mids]) * np.where(np.arange(31) % 2, -1, 1)
+    x[1, 31] = float(emax)
+    codes, scales = O.mx_quantize_fmt(x, fmt)
+    un = O.unpack_elements(codes, 6)
+    fl = Fraction(float(np.float32(1e-8)))
+    for r in range(4):
+        for b in range(2):
+            blk = [Fraction(float(v)) for v in x[r, 32 * b:32 * b + 32]]
+            e = _bf_exponent(max(max(abs(v) for v in blk), fl), emax)
+            assert scales[r, b] == e + 127
+            for i, v in enumerate(blk):
+                idx = _bf_nearest_fr(abs(v) / Fraction(2) ** e, table)
+                sign = 1 if float(x[r, 32 * b + i]) < 0 or (v == 0 and np.signbit(x[r, 32 * b + i])) else 0
+                assert un[r, 32 * b + i] == idx | (sign << 5), (r, b, i)
+
+
+def test_fp6_packing_bitstream():
+    """Element i of a row occupies bits [6i, 6i + 6) of the row read as one
+    little-endian integer."""
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 64, (3, 64))
+    packed = O.pack_elements(codes, 6)
+    assert packed.shape == (3, 48)
+    for r in range(3):
+        big = int.from_bytes(bytes(packed[r]), "little")
+        assert [(big >> (6 * i)) & 63 for i in range(64)] == list(codes[r])
+    assert np.array_equal(O.unpack_elements(packed, 6), codes)
+
+
+def test_fmt_mxfp4_equals_pinned_mxfp4():
+    rng = np.random.default_rng(21)
+    x = (rng.standard_normal((8, 256)) * np.exp2(rng.integers(-30, 30, (8, 1)))).astype(np.float32)
+    x[2, :32] = 0.0
+    x[3, 40] = 1e30
+    c0, s0 = O.mxfp4_quantize(x)
+    c1, s1 = O.mx_quantize_fmt(x, "mxfp4")
+    assert np.array_equal(c0, c1) and np.array_equal(s0, s1)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8_e4m3", "mxfp8_e5m2", "mxfp6_e2m3", "mxfp6_e3m2"])
+def test_fmt_dequant_exact_and_idempotent(fmt):
+    """value(code) * 2^(E-127) against the Fraction decode of the fields, and
+    quantize(dequantize(q)) reproduces the reconstruction exactly."""
+    E, M, bias, _ = O.MX_ELEMENT_FORMATS[fmt]
+    bits = 1 + E + M
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((5, 96)).astype(np.float32) * 3
+    codes, scales = O.mx_quantize_fmt(x, fmt)
+    y = O.dequantize_fmt(fmt, codes, scales)
+    un = O.unpack_elements(codes, bits)
+    for r in range(5):
+        for k in range(96):
+            c = int(un[r, k])
+            mag = c & ((1 << (bits - 1)) - 1)
+            e, m = mag >> M, mag & ((1 << M) - 1)
+            v = (Fraction(m, 2 ** M) * Fraction(2) ** (1 - bias) if e == 0
+                 else (1 + Fraction(m, 2 ** M)) * Fraction(2) ** (e - bias))
+            v = -v if c >> (bits - 1) else v
+            assert Fraction(float(y[r, k])) == v * Fraction(2) ** (int(scales[r, k // 32]) - 127)
+    # re-quantizing the reconstruction is lossless; a block whose max rounded
+    # down onto Emax/2 may take the next smaller scale, never another one
+    c2, s2 = O.mx_quantize_fmt(y, fmt)
+    d = scales.astype(int) - s2.astype(int)
+    assert set(np.unique(d)) <= {0, 1}
+    assert np.array_equal(O.dequantize_fmt(fmt, c2, s2), y)
+    assert np.array_equal(c2[d.repeat(96 * bits // 8 // 3, 1) == 0], codes[d.repeat(96 * bits // 8 // 3, 1) == 0])
