@@ -1,6 +1,7 @@
 /*
  * mx.h -- C ABI of libmx: block-scaled 4-bit floating-point quantization
- * (MXFP4, NVFP4) and the matrix products that consume it, for AMD gfx950.
+ * (MXFP4, NVFP4; also the wider MX elements MXFP8 and MXFP6) and the matrix
+ * products that consume it, for AMD gfx950.
  *
  * Formats (sources are the web pages this library implements):
  *   E2M1 element: 1 sign, 2 exponent (bias 1), 1 mantissa bit; states
@@ -16,10 +17,19 @@
  *     of NVFP4"), one FP8 E4M3 scale byte per block and one fp32 scale per
  *     tensor (dual-level scaling, "NVFP4 Architecture", section "1. The
  *     Dual-Level Mathematical Formulation").
+ *   MXFP8 / MXFP6: the same 32-element blocks and E8M0 scales with 8-bit
+ *     (E4M3 bias 7, largest 448; E5M2 bias 15, largest 57344) or 6-bit (E2M3
+ *     bias 1, largest 7.5; E3M2 bias 3, largest 28) elements (the MX family
+ *     of the "MXFP4" card, section "Core Facts": MXFP8/MXFP4 scaled GEMM; the
+ *     exponent/mantissa trade-off of "How Microscaling FP4 (MXFP4)...",
+ *     section "The Representation Dilemma").
  *
  * Memory layout of a quantized [rows, cols] tensor (blocks run along cols):
- *   codes  uint8 [rows, cols/2], row pitch cols/2 bytes; element 2j of a row
- *          in the low nibble of byte j, element 2j+1 in the high nibble.
+ *   codes  uint8 [rows, cols*b/8] for b-bit elements (b = 4, 6 or 8), rows
+ *          packed back to back; element i of a row occupies bits
+ *          [b*i, b*i + b) of the row read as one little-endian bit string
+ *          (4-bit: element 2j in the low nibble of byte j, 2j+1 in the high
+ *          nibble; 8-bit: one byte per element).
  *   scales uint8 [rows, cols/k], row pitch cols/k bytes (k = 32 or 16).
  *   global_scale  fp32[1] (NVFP4 only).
  *
@@ -58,7 +68,14 @@ typedef enum mx_status {
   MX_ERR_FORMAT = -8        /* unknown format or mismatched operand formats */
 } mx_status;
 
-enum { MX_FMT_MXFP4 = 0, MX_FMT_NVFP4 = 1 };
+enum {
+  MX_FMT_MXFP4 = 0,       /* E2M1 elements, 32-element blocks, E8M0 scales */
+  MX_FMT_NVFP4 = 1,       /* E2M1, 16-element blocks, E4M3 scales, fp32 tensor scale */
+  MX_FMT_MXFP8_E4M3 = 2,  /* 8-bit E4M3 elements, 32-element blocks, E8M0 scales */
+  MX_FMT_MXFP8_E5M2 = 3,  /* 8-bit E5M2 */
+  MX_FMT_MXFP6_E2M3 = 4,  /* 6-bit E2M3 */
+  MX_FMT_MXFP6_E3M2 = 5   /* 6-bit E3M2 */
+};
 enum { MX_DT_F32 = 0, MX_DT_BF16 = 1 };
 
 /* mx_quantize flags */
@@ -73,10 +90,10 @@ enum {
 enum { MX_OP_QUANTIZE = 0, MX_OP_GEMM = 1, MX_OP_MOE_ROUTE = 2 };
 
 typedef struct mx_tensor {
-  int32_t fmt;            /* MX_FMT_MXFP4 or MX_FMT_NVFP4 */
+  int32_t fmt;            /* MX_FMT_* */
   int32_t reserved;       /* must be 0 */
   int64_t rows, cols;     /* logical shape; cols is the blocked (K) axis */
-  uint8_t *codes;         /* device [rows, cols/2] */
+  uint8_t *codes;         /* device [rows, cols*b/8] (b = element bits) */
   uint8_t *scales;        /* device [rows, cols/k] */
   float *global_scale;    /* device fp32[1]; NVFP4 only, NULL for MXFP4 */
 } mx_tensor;
@@ -95,6 +112,11 @@ typedef struct mx_tensor {
  * byte nearest to m/(6g) (ties to even, saturating at 448); elements take the
  * E2M1 state nearest to x/(s*g), saturating at +-6.  The computed g is written
  * to *out->global_scale.
+ * MXFP8 / MXFP6: as MXFP4 with the element format's largest value Emax in
+ * place of 6: e = smallest integer with max(m, fp32(1e-8)) <= Emax*2^e, scale
+ * byte e + 127, each element the code nearest to x/2^e (ties to the even
+ * code; the rule keeps |x|/2^e <= Emax, so nothing saturates and no NaN or
+ * infinity code is produced).
  *   x          device, x_dtype (MX_DT_F32 / MX_DT_BF16), row pitch ld_x elems
  *   out        descriptor of the destination (device buffers caller-owned)
  *   workspace  device scratch of mx_workspace_bytes(MX_OP_QUANTIZE, out)
@@ -108,7 +130,8 @@ int mx_quantize(const void *x, int32_t x_dtype, int64_t ld_x, const mx_tensor *o
 /*
  * mx_dequantize -- x_hat = q * S_block * S_global ("NVFP4 Architecture",
  * section "1. The Dual-Level Mathematical Formulation", reconstruction
- * equation).  MXFP4: q * 2^(E-127) (exact in fp32).  NVFP4:
+ * equation).  MXFP4, MXFP8, MXFP6: q * 2^(E-127) (exact in fp32 for every
+ * scale the quantizer emits; otherwise rounded to nearest fp32).  NVFP4:
  * fp32(fp32(q * s) * g).  bf16 output is the round-to-nearest-even of that
  * fp32 value.  y is device [in->rows, in->cols] with row pitch ld_y elements.
  */
@@ -132,6 +155,12 @@ int mx_dequantize(const mx_tensor *in, void *y, int32_t y_dtype, int64_t ld_y, v
  * into the workspace, then multiplied.
  * c_dtype is MX_DT_F32 or MX_DT_BF16 (round-to-nearest-even), row pitch ldc.
  * Requires K % 32 == 0 (MXFP4) or K % 16 == 0 (NVFP4).
+ * MX element pairs beyond MXFP4 x MXFP4 (A and B each MXFP4, MXFP8 E4M3/E5M2
+ * or MXFP6 E2M3/E3M2, mixed pairs allowed, e.g. FP8 activations x FP4
+ * weights): C = sum_b 2^(eA+eB) sum_{k in b} qA qB with fp32 accumulation;
+ * dense, pre-quantized A only (MX_ERR_UNSUPPORTED for grouped or dynamic
+ * calls), K % 128 == 0 and K <= 2^22 (else MX_ERR_UNSUPPORTED).  NVFP4 pairs
+ * only with NVFP4 (else MX_ERR_FORMAT).
  */
 typedef struct mx_gemm_args {
   int64_t M, N, K;

@@ -18,20 +18,31 @@ __all__ = [
     "MX_QUANT_STATIC_GLOBAL", "MX_OP_QUANTIZE", "MX_OP_GEMM", "STATUS", "CMxTensor", "CMxGemmArgs",
     "empty_quantized", "mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemv", "mx_workspace_bytes",
     "mx_status_string", "mx_version", "MX_OP_MOE_ROUTE", "mx_moe_route", "mx_quantize_rows", "mx_moe_combine",
-    "moe_forward", "mx_rmsnorm_quantize",
+    "moe_forward", "mx_rmsnorm_quantize", "MX_FMT_MXFP8_E4M3", "MX_FMT_MXFP8_E5M2", "MX_FMT_MXFP6_E2M3",
+    "MX_FMT_MXFP6_E3M2", "element_bits",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "libmx.so")
 
 MX_FMT_MXFP4, MX_FMT_NVFP4 = 0, 1
+MX_FMT_MXFP8_E4M3, MX_FMT_MXFP8_E5M2, MX_FMT_MXFP6_E2M3, MX_FMT_MXFP6_E3M2 = 2, 3, 4, 5
 MX_DT_F32, MX_DT_BF16 = 0, 1
 MX_QUANT_DEFAULT, MX_QUANT_STATIC_GLOBAL = 0, 1
 MX_OP_QUANTIZE, MX_OP_GEMM, MX_OP_MOE_ROUTE = 0, 1, 2
 STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_ALIGN", -4: "MX_ERR_DTYPE",
           -5: "MX_ERR_UNSUPPORTED", -6: "MX_ERR_HIP", -7: "MX_ERR_WORKSPACE", -8: "MX_ERR_FORMAT"}
-_FMT = {"mxfp4": MX_FMT_MXFP4, "nvfp4": MX_FMT_NVFP4}
-_BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_NVFP4: 16}
+_FMT = {"mxfp4": MX_FMT_MXFP4, "nvfp4": MX_FMT_NVFP4, "mxfp8_e4m3": MX_FMT_MXFP8_E4M3,
+        "mxfp8_e5m2": MX_FMT_MXFP8_E5M2, "mxfp6_e2m3": MX_FMT_MXFP6_E2M3, "mxfp6_e3m2": MX_FMT_MXFP6_E3M2}
+_BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_NVFP4: 16, MX_FMT_MXFP8_E4M3: 32, MX_FMT_MXFP8_E5M2: 32,
+          MX_FMT_MXFP6_E2M3: 32, MX_FMT_MXFP6_E3M2: 32}
+_BITS = {MX_FMT_MXFP4: 4, MX_FMT_NVFP4: 4, MX_FMT_MXFP8_E4M3: 8, MX_FMT_MXFP8_E5M2: 8,
+         MX_FMT_MXFP6_E2M3: 6, MX_FMT_MXFP6_E3M2: 6}
+
+
+def element_bits(fmt) -> int:
+    """Bits per element code of a format (name or MX_FMT_* value)."""
+    return _BITS[_FMT[fmt] if isinstance(fmt, str) else fmt]
 
 
 class MXError(RuntimeError):
@@ -127,7 +138,7 @@ class MXTensor:
     fmt: int
     rows: int
     cols: int
-    codes: object          # uint8 [rows, cols/2]
+    codes: object          # uint8 [rows, cols * bits / 8]
     scales: object         # uint8 [rows, cols/k]
     global_scale: object = None   # float32 [1] (NVFP4)
 
@@ -146,7 +157,7 @@ def empty_quantized(rows: int, cols: int, fmt="mxfp4", device="cuda", lead=()) -
     import torch
     f = _FMT[fmt] if isinstance(fmt, str) else fmt
     k = _BLOCK[f]
-    codes = torch.empty(rows, cols // 2, dtype=torch.uint8, device=device)
+    codes = torch.empty(rows, cols * _BITS[f] // 8, dtype=torch.uint8, device=device)
     scales = torch.empty(rows, cols // k, dtype=torch.uint8, device=device)
     g = torch.ones(1, dtype=torch.float32, device=device) if f == MX_FMT_NVFP4 else None
     return MXTensor(f, rows, cols, codes, scales, g)

@@ -169,13 +169,6 @@ constexpr int GL_T = 512;              // 8 waves
 constexpr int GV_LG_RB = 4;            // weight rows per wave of the large-M kernel
 constexpr int GV_LG_MIN_M = 2;         // smallest M that takes the large-M kernel
 
-template <int VM>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  // s_waitcnt encoding for gfx9: vmcnt in [3:0] and [15:14]; expcnt and
-  // lgkmcnt at their maxima (no wait)
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x70 | 0xf00);
-}
 
 
 template <int M, int RB>

@@ -19,7 +19,13 @@ constexpr size_t kNvPartialBytes = 4096 * sizeof(uint32_t);
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-inline int block_of(int32_t fmt) { return fmt == MX_FMT_MXFP4 ? 32 : 16; }
+inline int block_of(int32_t fmt) { return fmt == MX_FMT_NVFP4 ? 16 : 32; }
+inline bool fmt_known(int32_t fmt) { return fmt >= MX_FMT_MXFP4 && fmt <= MX_FMT_MXFP6_E3M2; }
+// MXFP8 / MXFP6 (every MX element format but E2M1)
+inline bool fmt_wide(int32_t fmt) { return fmt >= MX_FMT_MXFP8_E4M3 && fmt <= MX_FMT_MXFP6_E3M2; }
+// element-format code of the block-scaled MFMA: E4M3 0, E5M2 1, E2M3 2, E3M2 3, E2M1 4
+inline int mfma_fmt(int32_t fmt) { return fmt == MX_FMT_MXFP4 ? 4 : fmt - MX_FMT_MXFP8_E4M3; }
+
 inline size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 inline int esize(int32_t dt) { return dt == MX_DT_F32 ? 4 : 2; }
 inline bool dtype_ok(int32_t dt) { return dt == MX_DT_F32 || dt == MX_DT_BF16; }
@@ -27,7 +33,7 @@ inline bool dtype_ok(int32_t dt) { return dt == MX_DT_F32 || dt == MX_DT_BF16; }
 // Descriptor checks common to every entry point.
 int check_tensor(const mx_tensor* t) {
   if (!t) return MX_ERR_NULL;
-  if (t->fmt != MX_FMT_MXFP4 && t->fmt != MX_FMT_NVFP4) return MX_ERR_FORMAT;
+  if (!fmt_known(t->fmt)) return MX_ERR_FORMAT;
   if (t->reserved != 0) return MX_ERR_SHAPE;
   if (t->rows < 0 || t->cols < 0 || t->rows > kMaxDim || t->cols > kMaxDim) return MX_ERR_SHAPE;
   if (t->rows > 0 && t->cols > 0 && t->rows > kMaxElems / t->cols) return MX_ERR_SHAPE;
@@ -100,7 +106,7 @@ int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* o
   int st = check_tensor(out);
   if (st) return st;
   if (flags != MX_QUANT_DEFAULT && flags != MX_QUANT_STATIC_GLOBAL) return MX_ERR_UNSUPPORTED;
-  if (out->fmt == MX_FMT_MXFP4 && flags != MX_QUANT_DEFAULT) return MX_ERR_UNSUPPORTED;
+  if (out->fmt != MX_FMT_NVFP4 && flags != MX_QUANT_DEFAULT) return MX_ERR_UNSUPPORTED;
   st = check_dense_input(x, x_dtype, ld_x, out->rows, out->cols);
   if (st) return st;
   const bool dyn_nv = out->fmt == MX_FMT_NVFP4 && !(flags & MX_QUANT_STATIC_GLOBAL);
@@ -110,6 +116,9 @@ int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* o
   hipError_t e;
   if (out->fmt == MX_FMT_MXFP4) {
     e = mxk::launch_quant_mx(x, bf, ld_x, out->rows, out->cols, out->codes, out->scales, as_stream(stream));
+  } else if (fmt_wide(out->fmt)) {
+    e = mxk::launch_quant_wide(mfma_fmt(out->fmt), x, bf, ld_x, out->rows, out->cols, out->codes, out->scales,
+                               as_stream(stream));
   } else {
     e = mxk::launch_quant_nv(x, bf, ld_x, out->rows, out->cols, out->codes, out->scales, out->global_scale, !dyn_nv,
                              static_cast<uint32_t*>(workspace), as_stream(stream));
@@ -123,6 +132,9 @@ int mx_dequantize(const mx_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, v
   st = check_dense_input(y, y_dtype, ld_y, in->rows, in->cols);
   if (st) return st;
   if (in->rows == 0 || in->cols == 0) return MX_OK;
+  if (fmt_wide(in->fmt))
+    return hip_status(mxk::launch_dequant_wide(mfma_fmt(in->fmt), in->codes, in->scales, in->rows, in->cols, y,
+                                               y_dtype == MX_DT_BF16, ld_y, as_stream(stream)));
   return hip_status(mxk::launch_dequant(in->fmt == MX_FMT_NVFP4, in->codes, in->scales, in->global_scale, in->rows,
                                         in->cols, y, y_dtype == MX_DT_BF16, ld_y, as_stream(stream)));
 }
@@ -143,6 +155,26 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
     if (!a->group_offsets) return MX_ERR_NULL;
     if (fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
   }
+  // MX element pairs other than E2M1 x E2M1 (MXFP8 / MXFP6, mixed pairs)
+  if (a->a && (fmt_wide(fmt) || fmt_wide(a->a->fmt))) {
+    st = check_tensor(a->a);
+    if (st) return st;
+    if (a->a->fmt == MX_FMT_NVFP4 || fmt == MX_FMT_NVFP4) return MX_ERR_FORMAT;
+    if (a->groups != 0) return MX_ERR_UNSUPPORTED;
+    if (a->a->rows != a->M || a->a->cols != a->K) return MX_ERR_SHAPE;
+    if (!dtype_ok(a->c_dtype)) return MX_ERR_DTYPE;
+    if (a->ldc < a->N) return MX_ERR_SHAPE;
+    if (a->M > 0 && a->N > 0) {
+      if (!a->c) return MX_ERR_NULL;
+      if (!al16(a->c)) return MX_ERR_ALIGN;
+    }
+    if (a->K % 128 != 0 || a->K > (int64_t(1) << 22)) return MX_ERR_UNSUPPORTED;
+    if (a->M == 0 || a->N == 0) return MX_OK;
+    return hip_status(mxk::launch_gemm_mxw(mfma_fmt(a->a->fmt), mfma_fmt(fmt), a->a->codes, a->a->scales,
+                                           a->b->codes, a->b->scales, a->c, a->c_dtype == MX_DT_BF16, a->ldc,
+                                           a->M, a->N, a->K, as_stream(stream)));
+  }
+  if (fmt_wide(fmt)) return MX_ERR_UNSUPPORTED;   // dynamic activation quantization is MXFP4 only
   if (!dtype_ok(a->c_dtype)) return MX_ERR_DTYPE;
   if (a->ldc < a->N) return MX_ERR_SHAPE;
   if (a->M > 0 && a->N > 0) {
@@ -245,6 +277,7 @@ int mx_rmsnorm_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const void
   if (st) return st;
   if (x_dtype != MX_DT_BF16 || !dtype_ok(gamma_dtype)) return MX_ERR_DTYPE;
   if (!(eps > 0.0f) || eps > 3.0e38f) return MX_ERR_SHAPE;   // eps > 0 keeps an all-zero row finite
+  if (out->fmt != MX_FMT_MXFP4 && out->fmt != MX_FMT_NVFP4) return MX_ERR_UNSUPPORTED;
   if (out->fmt == MX_FMT_MXFP4 && flags != MX_QUANT_DEFAULT) return MX_ERR_UNSUPPORTED;
   if (out->fmt == MX_FMT_NVFP4 && flags != MX_QUANT_STATIC_GLOBAL) return MX_ERR_UNSUPPORTED;
   if (out->cols % 32 != 0 || out->cols > kMaxNormCols) return MX_ERR_UNSUPPORTED;

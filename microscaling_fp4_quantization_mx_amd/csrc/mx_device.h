@@ -129,6 +129,16 @@ __device__ __forceinline__ void block_barrier() {
 // lanes that read one chunk column of 32 consecutive rows hit distinct banks.
 __device__ __forceinline__ int swz8r(int row) { return ((row >> 1) & 7) ^ ((row & 1) << 2); }
 
+// Wait until at most VM of this wave's vector-memory operations (including
+// direct-to-LDS loads) are outstanding.
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  // s_waitcnt encoding for gfx9: vmcnt in [3:0] and [15:14]; expcnt and
+  // lgkmcnt at their maxima (no wait)
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | 0x70 | 0xf00);
+}
+
 __device__ __forceinline__ uint32_t umax_xor(uint32_t v, int mask) {
   return max(v, (uint32_t)__shfl_xor((int)v, mask, 64));
 }

@@ -19,6 +19,15 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
 hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_global, void* c, int c_bf16,
                           int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st);
+// Wider MX elements; fmt is the block-scaled MFMA's element code (E4M3 0,
+// E5M2 1, E2M3 2, E3M2 3; the GEMM also takes E2M1 4).
+hipError_t launch_quant_wide(int fmt, const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols,
+                             uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_dequant_wide(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, void* y,
+                               bool out_bf16, int64_t ldy, hipStream_t st);
+hipError_t launch_gemm_mxw(int fa, int fb, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                           const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                           hipStream_t st);
 hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st);
 hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int experts, int32_t* offsets,

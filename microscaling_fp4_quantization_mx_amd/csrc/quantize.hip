@@ -297,6 +297,205 @@ __global__ __launch_bounds__(QT) void k_dequant(const uint32_t* __restrict__ cod
 }
 
 // ---------------------------------------------------------------------------
+// Wider MX elements: MXFP8 (E4M3, E5M2) and MXFP6 (E2M3, E3M2), same 32-element
+// blocks and E8M0 scales.  The block exponent is the smallest e with
+// max|x| <= Emax * 2^e (max|x| raised to 1e-8 first); for Emax = (1 + fE) 2^p
+// and max|x| = (1 + f) 2^(F-127) that is F - 127 - p + [f > fE], floored at
+// -27 - p (fp32(1e-8) has biased exponent 100 and a mantissa below every
+// fE).  Elements: |x| * 2^-e (exact in fp32) rounded to nearest-even in
+// software -- below the smallest normal 2^(1-bias) the subnormal step count
+// rint(v * 2^(bias-1+M)), else the fp32 mantissa rounded to M bits with the
+// carry running into the exponent field.  The scale rule keeps v <= Emax, so
+// nothing saturates and no NaN code (E4M3 0x7F) or infinity (E5M2) arises.
+// ---------------------------------------------------------------------------
+template <int F>
+struct WideFmt;
+template <> struct WideFmt<0> { static constexpr int E = 4, M = 3, BIAS = 7, P = 8; static constexpr uint32_t FE = 0x600000u; };
+template <> struct WideFmt<1> { static constexpr int E = 5, M = 2, BIAS = 15, P = 15; static constexpr uint32_t FE = 0x600000u; };
+template <> struct WideFmt<2> { static constexpr int E = 2, M = 3, BIAS = 1, P = 2; static constexpr uint32_t FE = 0x700000u; };
+template <> struct WideFmt<3> { static constexpr int E = 3, M = 2, BIAS = 3, P = 4; static constexpr uint32_t FE = 0x600000u; };
+
+template <int F>
+__device__ __forceinline__ int wide_block_exp(uint32_t amax_bits) {
+  using T = WideFmt<F>;
+  const int e = (int)(amax_bits >> 23) - 127 - T::P + ((amax_bits & 0x7fffffu) > T::FE ? 1 : 0);
+  return e < -27 - T::P ? -27 - T::P : e;
+}
+
+// Code of x (sign from x's bit pattern) for the block scale factor inv = 2^-e.
+template <int F>
+__device__ __forceinline__ uint32_t wide_encode(uint32_t xbits, float inv) {
+  using T = WideFmt<F>;
+  constexpr int BITS = 1 + T::E + T::M;
+  const float v = ffrom(xbits & 0x7fffffffu) * inv;
+  const uint32_t u = fbits(v);
+  const uint32_t sub = (uint32_t)__builtin_rintf(v * pow2f(T::BIAS - 1 + T::M));
+  uint32_t t = u >> (23 - T::M);
+  const uint32_t rem = u & ((1u << (23 - T::M)) - 1u), half = 1u << (22 - T::M);
+  t += (rem > half || (rem == half && (t & 1u))) ? 1u : 0u;
+  const uint32_t nrm = t - ((uint32_t)(127 - T::BIAS) << T::M);
+  const uint32_t mag = u < ((uint32_t)(128 - T::BIAS) << 23) ? sub : nrm;
+  return mag | ((xbits >> 31) << (BITS - 1));
+}
+
+template <typename TIn, int F, bool CONTIG>
+__global__ __launch_bounds__(QT) void k_quant_wide(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr, uint32_t nvec,
+                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  constexpr int EPL = 16 / (int)sizeof(TIn);
+  constexpr int LPB = 32 / EPL;
+  constexpr int BITS = 1 + WideFmt<F>::E + WideFmt<F>::M;
+  const int lane = threadIdx.x & 63;
+  const uint32_t wave_global = (blockIdx.x * QT + threadIdx.x) >> 6;
+  const uint32_t nwaves = (gridDim.x * QT) >> 6;
+  const uint32_t stride = nwaves * (64 * QU);
+  auto load = [&](u32x4 (&d)[QU], uint32_t base) {
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const uint32_t v = base + u * 64 + lane;
+      const TIn* p;
+      if (CONTIG) {
+        p = x + (size_t)v * EPL;
+      } else {
+        const uint32_t r = v / vpr, c = v - r * vpr;
+        p = x + (size_t)r * ldx + (size_t)c * EPL;
+      }
+      d[u] = v < nvec ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+    }
+  };
+  u32x4 d[QU], dn[QU];
+  uint32_t base = wave_global * (64 * QU);
+  if (base < nvec) load(d, base);
+  for (; base < nvec; base += stride) {
+    const uint32_t nb = base + stride;
+    if (nb < nvec) load(dn, nb);
+#pragma unroll
+    for (int u = 0; u < QU; ++u) {
+      const uint32_t v = base + u * 64 + lane;
+      uint32_t xb[EPL];
+      if constexpr (EPL == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xb[i] = d[u][i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xb[2 * i] = d[u][i] << 16;
+          xb[2 * i + 1] = d[u][i] & 0xffff0000u;
+        }
+      }
+      uint32_t am = 0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) am = max(am, xb[i] & 0x7fffffffu);
+      am = block_umax<LPB>(am);
+      const int e = wide_block_exp<F>(am);
+      const float inv = pow2f(-e);
+      uint32_t c[EPL];
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) c[i] = wide_encode<F>(xb[i], inv);
+      if (v < nvec) {
+        if constexpr (BITS == 8) {
+          uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+          if constexpr (EPL == 4) {
+            reinterpret_cast<uint32_t*>(codes)[v] = w0;
+          } else {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            const uint32_t w1 = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+            reinterpret_cast<u32x2*>(codes)[v] = u32x2{w0, w1};
+          }
+        } else {
+          // 6-bit fields, element i at bits [6i, 6i + 6) of the lane's bytes
+          const uint32_t lo = c[0] | (c[1] << 6) | (c[2] << 12) | (c[3] << 18);   // 24 bits
+          if constexpr (EPL == 4) {
+            uint8_t* dst = codes + (size_t)v * 3;       // 3 bytes; 2-byte aligned when v is even
+            if ((v & 1u) == 0) {
+              *reinterpret_cast<uint16_t*>(dst) = (uint16_t)lo;
+              dst[2] = (uint8_t)(lo >> 16);
+            } else {
+              dst[0] = (uint8_t)lo;
+              *reinterpret_cast<uint16_t*>(dst + 1) = (uint16_t)(lo >> 8);
+            }
+          } else {
+            const uint32_t hi = c[4] | (c[5] << 6) | (c[6] << 12) | (c[7] << 18);
+            const uint32_t w0 = lo | (hi << 24), w1 = hi >> 8;                     // 48 bits
+            uint8_t* dst = codes + (size_t)v * 6;       // 6 bytes; 4-byte aligned when v is even
+            if ((v & 1u) == 0) {
+              *reinterpret_cast<uint32_t*>(dst) = w0;
+              *reinterpret_cast<uint16_t*>(dst + 4) = (uint16_t)w1;
+            } else {
+              *reinterpret_cast<uint16_t*>(dst) = (uint16_t)w0;
+              *reinterpret_cast<uint32_t*>(dst + 2) = (w0 >> 16) | (w1 << 16);
+            }
+          }
+        }
+        if ((lane & (LPB - 1)) == 0) scales[v / LPB] = (uint8_t)(e + 127);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < QU; ++u) d[u] = dn[u];
+  }
+}
+
+// value(code) * 2^(E-127): each lane expands 16 elements (half a block).
+template <int F>
+__device__ __forceinline__ float wide_decode(uint32_t code) {
+  using T = WideFmt<F>;
+  constexpr int BITS = 1 + T::E + T::M;
+  const uint32_t mag = code & ((1u << (BITS - 1)) - 1u);
+  const uint32_t e = mag >> T::M, m = mag & ((1u << T::M) - 1u);
+  const float sub = (float)m * pow2f(1 - T::BIAS - T::M);
+  const float nrm = ffrom(((e + 127u - T::BIAS) << 23) | (m << (23 - T::M)));
+  const float v = e == 0 ? sub : nrm;
+  return (code >> (BITS - 1)) ? -v : v;
+}
+
+template <int F, bool OUT_BF16, bool CONTIG>
+__global__ __launch_bounds__(QT) void k_dequant_wide(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                     uint32_t hpr, uint32_t nhalf, void* __restrict__ y, int64_t ldy) {
+  constexpr int BITS = 1 + WideFmt<F>::E + WideFmt<F>::M;
+  for (uint32_t h = blockIdx.x * QT + threadIdx.x; h < nhalf; h += gridDim.x * QT) {
+    uint32_t c[16];
+    if constexpr (BITS == 8) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(codes + (size_t)h * 16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] = (w[i >> 2] >> (8 * (i & 3))) & 0xffu;
+    } else {
+      // 12 bytes = 96 bits: field i at bits [6i, 6i + 6)
+      const uint32_t* src = reinterpret_cast<const uint32_t*>(codes + (size_t)h * 12);
+      const uint64_t lo = (uint64_t)src[0] | ((uint64_t)src[1] << 32);
+      const uint32_t w2 = src[2];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int b = 6 * i;
+        if (b + 6 <= 64) c[i] = (uint32_t)(lo >> b) & 63u;
+        else if (b >= 64) c[i] = (w2 >> (b - 64)) & 63u;
+        else c[i] = ((uint32_t)(lo >> b) | (w2 << (64 - b))) & 63u;
+      }
+    }
+    const int sexp = (int)scales[h >> 1] - 127;
+    float f[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) f[i] = __builtin_ldexpf(wide_decode<F>(c[i]), sexp);
+    size_t off;
+    if (CONTIG) {
+      off = (size_t)h * 16;
+    } else {
+      const uint32_t r = h / hpr, ch = h - r * hpr;
+      off = (size_t)r * ldy + (size_t)ch * 16;
+    }
+    if (OUT_BF16) {
+      u32x4* dst = reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(y) + off);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        dst[q] = u32x4{pack_bf16x2_rne(f[8 * q + 0], f[8 * q + 1]), pack_bf16x2_rne(f[8 * q + 2], f[8 * q + 3]),
+                       pack_bf16x2_rne(f[8 * q + 4], f[8 * q + 5]), pack_bf16x2_rne(f[8 * q + 6], f[8 * q + 7])};
+    } else {
+      f32x4* dst = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(y) + off);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[q] = f32x4{f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]};
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
 static int grid_for(uint64_t work_items, int per_block) {
@@ -368,6 +567,51 @@ hipError_t launch_dequant(bool nv, const uint8_t* codes, const uint8_t* scales, 
     else { if (contig) MX_DQ(false, false, true); else MX_DQ(false, false, false); }
   }
 #undef MX_DQ
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_wide(int fmt, const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols,
+                             uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  const int epl = xdt_bf16 ? 8 : 4;
+  const uint32_t vpr = (uint32_t)(cols / epl);
+  const uint32_t nvec = (uint32_t)(rows * cols / epl);
+  const bool contig = ldx == cols;
+  const int grid = grid_for(nvec, QT * QU);
+#define MX_QW3(T, F, C) hipLaunchKernelGGL((k_quant_wide<T, F, C>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales)
+#define MX_QW2(T, F) if (contig) MX_QW3(T, F, true); else MX_QW3(T, F, false)
+#define MX_QW(F) if (xdt_bf16) { MX_QW2(uint16_t, F); } else { MX_QW2(float, F); }
+  switch (fmt) {
+    case 0: MX_QW(0); break;
+    case 1: MX_QW(1); break;
+    case 2: MX_QW(2); break;
+    case 3: MX_QW(3); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MX_QW
+#undef MX_QW2
+#undef MX_QW3
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_wide(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, void* y,
+                               bool out_bf16, int64_t ldy, hipStream_t st) {
+  const uint32_t hpr = (uint32_t)(cols / 16);
+  const uint32_t nhalf = (uint32_t)(rows * cols / 16);
+  const bool contig = ldy == cols;
+  const int grid = grid_for(nhalf, QT * 4);
+#define MX_DW3(F, B, C) hipLaunchKernelGGL((k_dequant_wide<F, B, C>), dim3(grid), dim3(QT), 0, st, codes, scales, hpr, nhalf, y, ldy)
+#define MX_DW2(F, B) if (contig) MX_DW3(F, B, true); else MX_DW3(F, B, false)
+#define MX_DW(F) if (out_bf16) { MX_DW2(F, true); } else { MX_DW2(F, false); }
+  switch (fmt) {
+    case 0: MX_DW(0); break;
+    case 1: MX_DW(1); break;
+    case 2: MX_DW(2); break;
+    case 3: MX_DW(3); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MX_DW
+#undef MX_DW2
+#undef MX_DW3
   return hipGetLastError();
 }
 

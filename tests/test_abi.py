@@ -231,3 +231,39 @@ def test_rmsnorm_quantize_validation():
     assert L.mx_rmsnorm_quantize(FAKE, 1, 256, FAKE, 0, f(1e-6), ctypes.byref(nv), 0, None) == -5  # NVFP4: static only
     big = T(rows=2, cols=32768 + 32)
     assert L.mx_rmsnorm_quantize(FAKE, 1, 32800, FAKE, 0, f(1e-6), ctypes.byref(big), 0, None) == -5
+
+
+def test_wide_format_validation():
+    """MXFP8 / MXFP6 descriptors: quantize and dequantize accept them, the
+    GEMM takes any MX pair (dense, pre-quantized A, K % 128 == 0) and every
+    other entry point reports them unsupported."""
+    L = mx.lib()
+    for f in (2, 3, 4, 5):
+        assert quant(t=T(fmt=f, cols=48)) == -5                            # cols % 32
+        assert quant(t=T(fmt=f), flags=1) == -5                            # no static-scale flag
+        assert quant(t=T(fmt=f, rows=0)) == 0
+        assert L.mx_dequantize(ctypes.byref(T(fmt=f)), FAKE + 4, 0, 256, None) == -3
+    # mixed pair A MXFP8 E4M3 x B MXFP4, then the reverse
+    g = gemm_args(K=256)
+    g.a.contents.fmt = 2
+    g.c = None
+    assert call_gemm(g) == -1                                              # validation reaches the wide path
+    g = gemm_args(K=192)
+    g.a.contents.fmt = 2
+    assert call_gemm(g) == -5                                              # K % 128
+    g = gemm_args(K=256, fmt=4)
+    g.a.contents.fmt = 1
+    g.a.contents.global_scale = FAKE
+    assert call_gemm(g) == -8                                              # NVFP4 x MXFP6
+    g = gemm_args(K=256, fmt=3, groups=2, group_offsets=FAKE)
+    assert call_gemm(g) == -5                                              # grouped wide not provided
+    g = gemm_args(K=256, fmt=5, a=False, a_raw=FAKE, a_raw_dtype=1, lda_raw=256)
+    assert call_gemm(g) == -5                                              # dynamic path: MXFP4 only
+    g = gemm_args(K=1 << 23, fmt=2)
+    g.a.contents.rows = 1
+    assert call_gemm(gemm_args(M=0, fmt=2)) == 0
+    w = T(3, 512, 256)
+    assert L.mx_gemv(FAKE, 1, 1, 256, ctypes.byref(w), FAKE, 1, 512, None) == -5
+    t = T(fmt=4, rows=16, cols=256)
+    assert L.mx_rmsnorm_quantize(FAKE, 1, 256, FAKE, 0, ctypes.c_float(1e-6), ctypes.byref(t), 0, None) == -5
+    assert L.mx_quantize_rows(FAKE, 0, 256, 10, FAKE, ctypes.byref(t), None) == -5

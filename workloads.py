@@ -110,6 +110,11 @@ GEMV_M = (1, 8, 16)
 MOE = Workload("moe_top2_route_quant_grouped_combine_8x4096x14336_T4096", 4096, 4096, 14336, "mxfp4", "bf16",
                "bf16", "uniform", experts=8)
 MOE_TOPK = 2
+# Wider MX elements on C3's product shape: activations and weights in
+# (A format, B format) pairs -- FP8 activations with FP4 weights (W4A8), FP8 x
+# FP8 and FP6 x FP6 -- from the same activation and weight recipes.
+WIDE = Workload("mx_wide_gemm_4096x8192x8192", 4096, 8192, 8192, "mxfp8_e4m3", "bf16", "bf16", "uniform")
+WIDE_PAIRS = (("mxfp8_e4m3", "mxfp4"), ("mxfp8_e4m3", "mxfp8_e4m3"), ("mxfp6_e2m3", "mxfp6_e2m3"))
 
 
 def make(w: Workload, seed: int = 0, rows: int | None = None):
