@@ -14,9 +14,10 @@ the stream they run on.
 Secondary measurements (same JSON line, `secondary`): the W4A16 GEMV
 N=K=8192 at M = 1, 8, 16 (GB/s, weights rotated over 16 copies), the NVFP4
 quantize + GEMM 2048x28672x8192, the fused dynamic-quantize grouped GEMM
-(8 experts, N=4096, K=14336, 8192 tokens) and the routed expert layer
+(8 experts, N=4096, K=14336, 8192 tokens), the routed expert layer
 around it (4096 tokens, top-2: route, gathered quantize, grouped GEMM,
-combine).
+combine), the fused RMSNorm + quantize, and MXFP8 / MXFP6 products on the
+4096x8192x8192 shape (FP8 x FP4, FP8 x FP8, FP6 x FP6).
 
 cpu_baseline: the CPU oracle (numpy, fp64) on a bounded sub-problem of the
 same step, timed on this host.
@@ -36,6 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MXFP4 W4A4 GEMM TFLOPS + W4A16 GEMV GB/s on 1 MI355X, % of roofline"
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 GEMM_KERNEL = "k_gemm_mx"
 PROFILES = os.path.join(ROOT, "profiles")
@@ -233,6 +235,34 @@ def bench_nvfp4(args, torch, mx, W):
             "quant_w_GB/s_two_reads": qw_bytes / (qw * 1e-3) / 1e9}
 
 
+def bench_wide(args, torch, mx, W):
+    """MXFP8 / MXFP6 pairs on the 4096 x 8192 x 8192 product: quantize the bf16
+    activations and fp32 weights to the pair's formats, then the GEMM."""
+    w = W.WIDE
+    M, N, K = w.M, w.N, w.K
+    dev = torch.device("cuda:0")
+    d = W.make(w)
+    x = torch.from_numpy(d["x"]).to(torch.bfloat16).to(dev)
+    wt = torch.from_numpy(d["w"]).to(dev)
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    R = max(1, args.side_iters)
+    res = {}
+    for fa, fb in W.WIDE_PAIRS:
+        aq = mx.empty_quantized(M, K, fa, dev)
+        bq = mx.empty_quantized(N, K, fb, dev)
+        qx = time_graph(torch, capture(torch, lambda: mx.mx_quantize(x, fa, out=aq), R), R)
+        mx.mx_quantize(wt, fb, out=bq)
+        g = time_graph(torch, capture(torch, lambda: mx.mx_gemm(aq, bq, out=c), R), R, replays=2)
+        flops = 2.0 * M * N * K
+        tf = flops / (g * 1e-3) / 1e12
+        peak = PEAK_FP8_TFLOPS if "mxfp8" in (fa + fb) else PEAK_FP4_TFLOPS
+        qbytes = M * K * 2 + M * K * mx.element_bits(fa) // 8 + M * K // 32
+        res[f"{fa}_x_{fb}"] = {"gemm_avg_ms": g, "gemm_TFLOPS": tf, "gemm_peak_TFLOPS": peak, "gemm_frac": tf / peak,
+                               "quant_x_bf16_avg_ms": qx, "quant_x_GB/s": qbytes / (qx * 1e-3) / 1e9}
+        del aq, bq
+    return res
+
+
 def bench_grouped(args, torch, mx, W):
     w = W.C5
     G, N, K, T = w.experts, w.N, w.K, w.M
@@ -375,6 +405,9 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: NVFP4 quantize + GEMM")
         sec["nvfp4_2048x28672x8192"] = bench_nvfp4(args, torch, mx, W)
+        torch.cuda.empty_cache()
+        log("secondary: MXFP8 / MXFP6 GEMM pairs")
+        sec["mx_wide_gemm_4096x8192x8192"] = bench_wide(args, torch, mx, W)
         torch.cuda.empty_cache()
         log("secondary: fused dynamic-quantize grouped GEMM")
         sec["grouped_8x4096x14336_T8192"] = bench_grouped(args, torch, mx, W)
