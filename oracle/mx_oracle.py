@@ -23,7 +23,7 @@ __all__ = [
     "mx_block_exponent", "mxfp4_quantize", "nvfp4_global_scale",
     "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize",
     "round_to_bf16", "gemm", "gemm_tolerance", "gemv", "grouped_gemm",
-    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward", "rmsnorm_values", "rmsnorm_quantize", "MX_ELEMENT_FORMATS", "element_bits", "element_positive_values", "element_nearest_code", "mx_block_exponent_fmt", "pack_elements", "unpack_elements", "mx_quantize_fmt", "dequantize_fmt",
+    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward", "rmsnorm_values", "rmsnorm_quantize", "MX_ELEMENT_FORMATS", "element_bits", "element_positive_values", "element_nearest_code", "mx_block_exponent_fmt", "pack_elements", "unpack_elements", "mx_quantize_fmt", "dequantize_fmt", "mx_quantize_variant", "dequantize_variant", "naive_per_tensor_quantize", "dequantize_naive", "reconstruction_snr_db",
 ]
 
 # Table "The Complete Discrete State Mapping of E2M1" ("NVFP4 Architecture",
@@ -495,6 +495,112 @@ def dequantize_fmt(fmt: str, packed: np.ndarray, scales: np.ndarray) -> np.ndarr
     val = np.where((codes >> (bits - 1)) & 1, -mag, mag)
     s = np.exp2(np.asarray(scales, np.float64) - 127.0)
     return (val.reshape(R, K // 32, 32) * s[..., None]).reshape(R, K).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Variants of the pages' emulation surface ("NVFP4 Architecture", sections
+# "1. The Dual-Level Mathematical Formulation" and "End-to-End
+# Implementation"): any block length (the emulation defaults to 16 with an
+# E8M0 scale), an optional per-tensor scale S_global inside the power-of-two
+# block scale, the OCP floor rule as an alternative exponent rule, and rows
+# whose length is not a multiple of the block (zero-padded, as the emulation
+# pads its flattened tensor).
+# ---------------------------------------------------------------------------
+def _emax_exponent(fmt: str) -> int:
+    """floor(log2 Emax): 2 for E2M1 and E2M3, 8 for E4M3, 15 for E5M2, 4 for E3M2."""
+    return int(math.floor(math.log2(MX_ELEMENT_FORMATS[fmt][3])))
+
+
+def mx_quantize_variant(x: np.ndarray, fmt: str = "mxfp4", block: int = 32, rule: str = "ceil",
+                        global_scale=None):
+    """Block quantization with E8M0 scales, generalised.
+
+    Rows are zero-padded to Kp = ceil(K / block) * block (READING: blocks stay
+    inside a row, the emulation's zero padding applied per row; the padding
+    leaves max|x| unchanged and its codes are +0).  With g = global_scale
+    (fp32; 1 when None) and Emax the element format's largest value:
+      rule "ceil"  (the pages): e = smallest integer with max(m, 1e-8) <= Emax * g * 2^e;
+      rule "floor" (OCP, READING: offered as an option only, g must be 1):
+                   e = floor(log2 max(m, 1e-8)) - floor(log2 Emax); elements
+                   beyond Emax then saturate to +-Emax.
+    Elements: the code nearest to x / (g * 2^e) (ties to the even code), the
+    input's sign kept.  Returns (packed codes [R, Kp * bits / 8], E8M0 bytes
+    [R, Kp / block])."""
+    x = np.asarray(x, np.float32)
+    R, K = x.shape
+    Kp = -(-K // block) * block
+    xp = np.zeros((R, Kp), np.float32)
+    xp[:, :K] = x
+    g = 1.0 if global_scale is None else float(np.float32(global_scale))
+    bits = element_bits(fmt)
+    emax = MX_ELEMENT_FORMATS[fmt][3]
+    xb = xp.astype(np.float64).reshape(R, Kp // block, block)
+    m = np.maximum(np.abs(xb).max(axis=-1), float(np.float32(1e-8)))
+    if rule == "ceil":
+        lim = emax * g
+        e = np.ceil(np.log2(m / lim)).astype(np.int64)
+        for _ in range(2):   # exact: products of Emax, g and 2^e are exact in fp64
+            e = np.where(lim * np.exp2(e.astype(np.float64)) < m, e + 1, e)
+            e = np.where(lim * np.exp2((e - 1).astype(np.float64)) >= m, e - 1, e)
+    elif rule == "floor":
+        if g != 1.0:
+            raise ValueError("the floor rule has no per-tensor scale")
+        e = np.floor(np.log2(m)).astype(np.int64)
+        e = np.where(np.exp2(e.astype(np.float64)) > m, e - 1, e)
+        e = np.where(np.exp2((e + 1).astype(np.float64)) <= m, e + 1, e)
+        e = e - _emax_exponent(fmt)
+    else:
+        raise ValueError(rule)
+    unit = g * np.exp2(e.astype(np.float64))
+    # nearest code: compare |x| with the exact midpoints between codes times
+    # the unit (fp64 products of an fp32 g, a power of two and a short midpoint)
+    table = element_positive_values(fmt)
+    mids = (table[:-1] + table[1:]) / 2
+    above = np.abs(xb)[..., None] > mids * unit[..., None, None]
+    at = np.abs(xb)[..., None] == mids * unit[..., None, None]
+    idx = above.sum(-1) + (at & (np.arange(len(mids)) % 2 == 1)).sum(-1)   # ties go to the even code
+    sign = np.signbit(xp).reshape(xb.shape).astype(np.int64)
+    codes = idx.astype(np.int64) | (sign << (bits - 1))
+    return pack_elements(codes.reshape(R, Kp), bits), (e + 127).astype(np.uint8)
+
+
+def dequantize_variant(fmt: str, packed: np.ndarray, scales: np.ndarray, K: int, global_scale=None) -> np.ndarray:
+    """x_hat = fp32(fp32(value(code) * 2^(E-127)) * g) for the first K columns."""
+    y = dequantize_fmt(fmt, packed, scales) if fmt != "mxfp4" else None
+    if fmt == "mxfp4":
+        codes = unpack_codes(packed)
+        R, Kp = codes.shape
+        s = np.repeat(e8m0_decode(scales), Kp // np.asarray(scales).shape[1], axis=1)
+        y = (e2m1_decode(codes) * s).astype(np.float32)
+    if global_scale is not None:
+        y = (y * np.float32(global_scale)).astype(np.float32)
+    return y[:, :K]
+
+
+def naive_per_tensor_quantize(x: np.ndarray):
+    """The pages' naive per-tensor FP4 in stored form: one fp32 scale
+    s = fp32(max(max|x|, 1e-8) / 6) for the whole tensor (READING: the
+    emulation computes it in the tensor's fp32), every element the E2M1 state
+    nearest to x / s with the input's sign.  Returns (packed codes [R, K/2]
+    (K even), s as np.float32)."""
+    x = np.asarray(x, np.float32)
+    s = np.float32(max(np.float32(np.abs(x).max()) if x.size else np.float32(0), np.float32(1e-8))) / np.float32(6.0)
+    idx = nearest_state_index(np.abs(x.astype(np.float64)), np.full(x.shape, float(s)))
+    codes = (idx | (np.signbit(x).astype(np.int64) << 3)).astype(np.uint8)
+    return pack_codes(codes), np.float32(s)
+
+
+def dequantize_naive(packed: np.ndarray, s) -> np.ndarray:
+    return (e2m1_decode(unpack_codes(packed)) * np.float64(np.float32(s))).astype(np.float32)
+
+
+def reconstruction_snr_db(x: np.ndarray, x_hat: np.ndarray) -> float:
+    """10 log10(sum x^2 / sum (x - x_hat)^2) in fp64: the accuracy measure of
+    the pages' emulation demo (MSE against the original, reported as SNR)."""
+    x = np.asarray(x, np.float64)
+    d = x - np.asarray(x_hat, np.float64)
+    num, den = float(np.sum(x * x)), float(np.sum(d * d))
+    return float("inf") if den == 0 else 10.0 * math.log10(num / den)
 
 
 def moe_route(topk_ids: np.ndarray, experts: int):

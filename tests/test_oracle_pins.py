@@ -801,3 +801,131 @@ def test_fmt_dequant_exact_and_idempotent(fmt):
     assert set(np.unique(d)) <= {0, 1}
     assert np.array_equal(O.dequantize_fmt(fmt, c2, s2), y)
     assert np.array_equal(c2[d.repeat(96 * bits // 8 // 3, 1) == 0], codes[d.repeat(96 * bits // 8 // 3, 1) == 0])
+
+
+# ------------------------------------------- emulation variants (k, rule, S_global, tails)
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8_e4m3", "mxfp6_e2m3"])
+def test_variant_default_equals_pinned_quantizers(fmt):
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((6, 128)) * np.exp2(rng.integers(-10, 10, (6, 1)))).astype(np.float32)
+    x[0, 3] *= 300
+    c, s = O.mx_quantize_variant(x, fmt, 32, "ceil")
+    c2, s2 = O.mx_quantize_fmt(x, fmt)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+    if fmt == "mxfp4":   # the emulation's default block of 16 (pinned against the page emulation)
+        c, s = O.mx_quantize_variant(x, fmt, 16, "ceil")
+        c2, s2 = O.mxfp4_quantize(x, block=16)
+        assert np.array_equal(c, c2) and np.array_equal(s, s2)
+
+
+def _bf_floor_exponent(m: Fraction) -> int:
+    e = 0
+    while Fraction(2) ** e > m:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= m:
+        e += 1
+    return e
+
+
+@pytest.mark.parametrize("block", [16, 32])
+def test_floor_rule_bruteforce_e2m1(block):
+    """OCP rule: e = floor(log2 max|x|) - 2, elements nearest with saturation at 6."""
+    rng = np.random.default_rng(block)
+    x = (rng.standard_normal((4, 64)) * np.exp2(rng.integers(-8, 8, (4, 1)))).astype(np.float32)
+    x[0, :block] = 0.0
+    x[1, 2] = 7.5            # max with mantissa > 1.5: elements land in (6, 8) and saturate
+    c, s = O.mx_quantize_variant(x, "mxfp4", block, "floor")
+    codes = O.unpack_codes(c)
+    fl = Fraction(float(np.float32(1e-8)))
+    for r in range(4):
+        for b in range(64 // block):
+            blk = [Fraction(float(v)) for v in x[r, b * block:(b + 1) * block]]
+            e = _bf_floor_exponent(max(max(abs(v) for v in blk), fl)) - 2
+            assert s[r, b] == e + 127
+            for i, v in enumerate(blk):
+                idx = bf_nearest_e2m1(abs(v) / Fraction(2) ** e)
+                sign = int(np.signbit(x[r, b * block + i]))
+                assert codes[r, b * block + i] == idx | (sign << 3)
+
+
+def test_floor_rule_e4m3_matches_saturating_torch_cast():
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((5, 64)) * np.exp2(rng.integers(-12, 12, (5, 1)))).astype(np.float32)
+    x[2, 9] = 500.0 * 2.0 ** 3      # max mantissa 1.95: elements up to 500 > 448 saturate
+    c, s = O.mx_quantize_variant(x, "mxfp8_e4m3", 32, "floor")
+    fl = Fraction(float(np.float32(1e-8)))
+    e = np.array([[_bf_floor_exponent(max(Fraction(float(np.abs(b).max())), fl)) - 8 for b in row.reshape(-1, 32)]
+                  for row in x])
+    assert np.array_equal(s, (e + 127).astype(np.uint8))
+    scaled = x.reshape(5, 2, 32).astype(np.float64) * np.exp2(-e.astype(np.float64))[..., None]
+    scaled = np.clip(scaled, -448.0, 448.0).reshape(5, 64)
+    ref = torch.from_numpy(scaled).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(c, ref)
+
+
+def test_global_scale_bruteforce_k16():
+    """S_block = 2^ceil(log2(m / (6 g))) with a per-tensor g: smallest e with
+    m <= 6 g 2^e; elements nearest to x / (g 2^e)."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((3, 48)) * 5).astype(np.float32)
+    g = np.float32(0.3712)
+    c, s = O.mx_quantize_variant(x, "mxfp4", 16, "ceil", global_scale=g)
+    codes = O.unpack_codes(c)
+    G = Fraction(float(g))
+    fl = Fraction(float(np.float32(1e-8)))
+    for r in range(3):
+        for b in range(3):
+            blk = [Fraction(float(v)) for v in x[r, 16 * b:16 * b + 16]]
+            m = max(max(abs(v) for v in blk), fl)
+            e = 0
+            while m > 6 * G * Fraction(2) ** e:
+                e += 1
+            while m <= 6 * G * Fraction(2) ** (e - 1):
+                e -= 1
+            assert s[r, b] == e + 127
+            for i, v in enumerate(blk):
+                idx = bf_nearest_e2m1(abs(v) / (G * Fraction(2) ** e))
+                assert codes[r, 16 * b + i] == idx | (int(np.signbit(x[r, 16 * b + i])) << 3)
+    y = O.dequantize_variant("mxfp4", c, s, 48, global_scale=g)
+    q = O.dequantize("mxfp4", c, s)
+    assert np.array_equal(y, (q * g).astype(np.float32))
+
+
+@pytest.mark.parametrize("fmt,block,K", [("mxfp4", 32, 50), ("mxfp4", 16, 7), ("mxfp8_e5m2", 32, 33),
+                                         ("mxfp6_e3m2", 32, 95)])
+def test_zero_padded_tails_equal_explicit_padding(fmt, block, K):
+    rng = np.random.default_rng(K)
+    x = (rng.standard_normal((4, K)) * 4).astype(np.float32)
+    c, s = O.mx_quantize_variant(x, fmt, block)
+    Kp = -(-K // block) * block
+    xp = np.zeros((4, Kp), np.float32)
+    xp[:, :K] = x
+    if block == 32:
+        c2, s2 = O.mx_quantize_fmt(xp, fmt)
+    else:
+        c2, s2 = O.mxfp4_quantize(xp, block=block)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+    y = O.dequantize_variant(fmt, c, s, K)
+    assert y.shape == (4, K)
+
+
+def test_naive_per_tensor_stored_form():
+    """Codes of the stored form reproduce the pages' worked example, and its
+    reconstruction equals naive_per_tensor_fp4 when fp32(max/6) is exact."""
+    rows = _rows("naive_outlier_example.txt")
+    x = np.array([[float(r[0]) for r in rows]], np.float32)
+    x = np.concatenate([x, np.zeros((1, x.shape[1] % 2), np.float32)], axis=1) if x.shape[1] % 2 else x
+    c, s = O.naive_per_tensor_quantize(x)
+    q = O.e2m1_decode(O.unpack_codes(c))[0, :len(rows)]
+    assert np.array_equal(q, np.array([float(r[1]) for r in rows]))
+    rng = np.random.default_rng(2)
+    y = (rng.standard_normal((3, 40)) * 2).astype(np.float32)
+    y[1, 5] = 6.0 * 8.0                                  # max / 6 = 8 exactly
+    c, s = O.naive_per_tensor_quantize(y)
+    assert s == np.float32(8.0)
+    assert np.array_equal(O.dequantize_naive(c, s).astype(np.float64), O.naive_per_tensor_fp4(y))
+
+
+def test_snr_closed_form():
+    assert abs(O.reconstruction_snr_db(np.array([1.0, 1.0]), np.array([1.0, 0.5])) - 10 * np.log10(8.0)) < 1e-12
+    assert O.reconstruction_snr_db(np.array([2.0]), np.array([2.0])) == float("inf")
