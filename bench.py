@@ -17,7 +17,9 @@ quantize + GEMM 2048x28672x8192, the fused dynamic-quantize grouped GEMM
 (8 experts, N=4096, K=14336, 8192 tokens), the routed expert layer
 around it (4096 tokens, top-2: route, gathered quantize, grouped GEMM,
 combine), the fused RMSNorm + quantize, and MXFP8 / MXFP6 products on the
-4096x8192x8192 shape (FP8 x FP4, FP8 x FP8, FP6 x FP6).
+4096x8192x8192 shape (FP8 x FP4, FP8 x FP8, FP6 x FP6), and the
+quantization variants (16-element E8M0 blocks, the OCP floor rule, naive
+per-tensor FP4, ...) with the reconstruction SNR of each.
 
 cpu_baseline: the CPU oracle (numpy, fp64) on a bounded sub-problem of the
 same step, timed on this host.
@@ -263,6 +265,38 @@ def bench_wide(args, torch, mx, W):
     return res
 
 
+def bench_variants(args, torch, mx, W):
+    """The emulation variants on the 4096 x 8192 fp32 activations (outlier
+    columns): quantize time and rate of each scheme, and the reconstruction
+    SNR (dB) of its GPU dequantized output against the input (the accuracy
+    measure of the pages' emulation demo; the error sums are measurement only)."""
+    w = W.C3
+    dev = torch.device("cuda:0")
+    d = W.make(w)
+    x = torch.from_numpy(d["x"]).to(dev)
+    M, K = x.shape
+    R = max(1, args.side_iters)
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device=dev)
+    x64 = x.double()
+    sig = float((x64 * x64).sum())
+    res = {}
+    schemes = [("mxfp4_k32_ceil", "mxfp4", {}), ("mxfp4_k32_floor_ocp", "mxfp4", {"rule": "floor"}),
+               ("mxfp4_k16_e8m0", "mxfp4_k16", {}), ("mxfp4_k16_e8m0_tensor_scale", "mxfp4_k16", {"static_global": 0.75}),
+               ("nvfp4_k16_e4m3", "nvfp4", {}), ("fp4_per_tensor_naive", "fp4_tensor", {}),
+               ("mxfp8_e4m3", "mxfp8_e4m3", {}), ("mxfp6_e2m3", "mxfp6_e2m3", {})]
+    for name, fmt, kw in schemes:
+        q = mx.empty_quantized(M, K, fmt, dev)
+        t = time_graph(torch, capture(torch, lambda: mx.mx_quantize(x, fmt, out=q, workspace=ws, **kw), R), R)
+        y = mx.mx_dequantize(q)
+        err = float(((x64 - y.double()) ** 2).sum())
+        bits = mx.element_bits(fmt)
+        qbytes = M * K * 4 + M * K * bits // 8 + (0 if q.scales is None else q.scales.numel())
+        res[name] = {"quant_avg_ms": t, "quant_GB/s": qbytes / (t * 1e-3) / 1e9,
+                     "snr_db": 10.0 * __import__("math").log10(sig / err) if err > 0 else None}
+        del q, y
+    return res
+
+
 def bench_grouped(args, torch, mx, W):
     w = W.C5
     G, N, K, T = w.experts, w.N, w.K, w.M
@@ -408,6 +442,9 @@ def main():
         torch.cuda.empty_cache()
         log("secondary: MXFP8 / MXFP6 GEMM pairs")
         sec["mx_wide_gemm_4096x8192x8192"] = bench_wide(args, torch, mx, W)
+        torch.cuda.empty_cache()
+        log("secondary: quantization variants and reconstruction SNR")
+        sec["variants_4096x8192_fp32"] = bench_variants(args, torch, mx, W)
         torch.cuda.empty_cache()
         log("secondary: fused dynamic-quantize grouped GEMM")
         sec["grouped_8x4096x14336_T8192"] = bench_grouped(args, torch, mx, W)

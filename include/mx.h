@@ -24,6 +24,17 @@
  *     exponent/mantissa trade-off of "How Microscaling FP4 (MXFP4)...",
  *     section "The Representation Dilemma").
  *
+ *   Emulation variants ("NVFP4 Architecture", section "1. The Dual-Level
+ *     Mathematical Formulation", equation S_block with S_global, and section
+ *     "End-to-End Implementation", whose emulation uses 16-element blocks
+ *     with power-of-two scales and zero-pads to whole blocks):
+ *     MX_FMT_MXFP4_K16 = E2M1 in 16-element blocks with E8M0 scales and an
+ *     optional fp32 tensor scale g (global_scale; NULL = 1):
+ *     S_block = 2^ceil(log2(m / (6 g))); MX_FMT_FP4_TENSOR = the naive
+ *     baseline (section "The Problem", figure "The Outlier Distortion in
+ *     Coarse-Grained FP4"): one fp32 scale s = fp32(max(max|x|, 1e-8) / 6)
+ *     for the whole tensor in global_scale, no block scales.
+ *
  * Memory layout of a quantized [rows, cols] tensor (blocks run along cols):
  *   codes  uint8 [rows, cols*b/8] for b-bit elements (b = 4, 6 or 8), rows
  *          packed back to back; element i of a row occupies bits
@@ -31,6 +42,11 @@
  *          (4-bit: element 2j in the low nibble of byte j, 2j+1 in the high
  *          nibble; 8-bit: one byte per element).
  *   scales uint8 [rows, cols/k], row pitch cols/k bytes (k = 32 or 16).
+ *   E8M0-scaled formats (MXFP4, MXFP8, MXFP6, MXFP4_K16) accept any cols:
+ *   each row is stored zero-padded to P = ceil(cols/k)*k elements (codes
+ *   [rows, P*b/8], scales [rows, P/k]); the padding quantizes to +0.
+ *   MX_FMT_FP4_TENSOR: codes [rows, cols/2] (cols even), scales unused (may
+ *   be NULL), global_scale fp32[1].
  *   global_scale  fp32[1] (NVFP4 only).
  *
  * Conventions for every entry point:
@@ -74,7 +90,9 @@ enum {
   MX_FMT_MXFP8_E4M3 = 2,  /* 8-bit E4M3 elements, 32-element blocks, E8M0 scales */
   MX_FMT_MXFP8_E5M2 = 3,  /* 8-bit E5M2 */
   MX_FMT_MXFP6_E2M3 = 4,  /* 6-bit E2M3 */
-  MX_FMT_MXFP6_E3M2 = 5   /* 6-bit E3M2 */
+  MX_FMT_MXFP6_E3M2 = 5,  /* 6-bit E3M2 */
+  MX_FMT_MXFP4_K16 = 6,   /* E2M1, 16-element blocks, E8M0 scales, optional fp32 tensor scale */
+  MX_FMT_FP4_TENSOR = 7   /* E2M1 with one fp32 scale for the whole tensor (naive baseline) */
 };
 enum { MX_DT_F32 = 0, MX_DT_BF16 = 1 };
 
@@ -83,7 +101,11 @@ enum {
   MX_QUANT_DEFAULT = 0,
   /* NVFP4: use *global_scale as given (a calibrated, static per-tensor scale)
      instead of computing it from the tensor's max |x|. */
-  MX_QUANT_STATIC_GLOBAL = 1
+  MX_QUANT_STATIC_GLOBAL = 1,
+  /* E8M0-scaled formats: the OCP exponent rule e = floor(log2 max|x|) -
+     floor(log2 Emax) instead of the pages' smallest e with max|x| <= Emax*2^e;
+     elements beyond Emax then saturate to +-Emax. */
+  MX_QUANT_SCALE_FLOOR = 2
 };
 
 /* mx_workspace_bytes operations */
@@ -112,6 +134,17 @@ typedef struct mx_tensor {
  * byte nearest to m/(6g) (ties to even, saturating at 448); elements take the
  * E2M1 state nearest to x/(s*g), saturating at +-6.  The computed g is written
  * to *out->global_scale.
+ * MXFP4_K16: as MXFP4 with 16-element blocks and, when out->global_scale is
+ * not NULL, g = *global_scale (set by the caller): e = smallest integer with
+ * max(m, 1e-8) <= 6*g*2^e, elements the state nearest to x/(g*2^e) (g must
+ * keep every e in [-127, 127]).  MX_FMT_FP4_TENSOR: s = fp32(max(max|x|,
+ * 1e-8)/6) written to *out->global_scale, elements the state nearest to x/s
+ * (saturating at 6); needs a workspace like dynamic NVFP4.  Flag
+ * MX_QUANT_SCALE_FLOOR selects the OCP exponent rule for the E8M0-scaled
+ * formats (not with a MXFP4_K16 tensor scale).  Rows whose length is not a
+ * multiple of the block are zero-padded (layout above).  These variant paths
+ * (MXFP4_K16, FP4_TENSOR, the floor rule, rows of any length) read x element
+ * by element: any ld_x >= cols is accepted (x aligned to its element size).
  * MXFP8 / MXFP6: as MXFP4 with the element format's largest value Emax in
  * place of 6: e = smallest integer with max(m, fp32(1e-8)) <= Emax*2^e, scale
  * byte e + 127, each element the code nearest to x/2^e (ties to the even
@@ -131,7 +164,10 @@ int mx_quantize(const void *x, int32_t x_dtype, int64_t ld_x, const mx_tensor *o
  * mx_dequantize -- x_hat = q * S_block * S_global ("NVFP4 Architecture",
  * section "1. The Dual-Level Mathematical Formulation", reconstruction
  * equation).  MXFP4, MXFP8, MXFP6: q * 2^(E-127) (exact in fp32 for every
- * scale the quantizer emits; otherwise rounded to nearest fp32).  NVFP4:
+ * scale the quantizer emits; otherwise rounded to nearest fp32); MXFP4_K16:
+ * fp32(q * 2^(E-127) * g); FP4_TENSOR: fp32(q * s).  Only the first cols
+ * elements of a padded row are written, and for those variant formats (and
+ * rows of any length) any ld_y >= cols is accepted.  NVFP4:
  * fp32(fp32(q * s) * g).  bf16 output is the round-to-nearest-even of that
  * fp32 value.  y is device [in->rows, in->cols] with row pitch ld_y elements.
  */
@@ -159,8 +195,12 @@ int mx_dequantize(const mx_tensor *in, void *y, int32_t y_dtype, int64_t ld_y, v
  * or MXFP6 E2M3/E3M2, mixed pairs allowed, e.g. FP8 activations x FP4
  * weights): C = sum_b 2^(eA+eB) sum_{k in b} qA qB with fp32 accumulation;
  * dense, pre-quantized A only (MX_ERR_UNSUPPORTED for grouped or dynamic
- * calls), K % 128 == 0 and K <= 2^22 (else MX_ERR_UNSUPPORTED).  NVFP4 pairs
- * only with NVFP4 (else MX_ERR_FORMAT).
+ * calls), padded K % 128 == 0 and K <= 2^22 (else MX_ERR_UNSUPPORTED).  NVFP4
+ * pairs only with NVFP4 (else MX_ERR_FORMAT).  Pre-quantized MX operands
+ * with K % 32 != 0 (zero-padded rows) multiply over the padded length, which
+ * gives the same product.  MXFP4_K16 and FP4_TENSOR operands are not
+ * provided (MX_ERR_UNSUPPORTED: their scales do not map onto the matrix
+ * cores' 32-element blocks).
  */
 typedef struct mx_gemm_args {
   int64_t M, N, K;

@@ -19,7 +19,8 @@ __all__ = [
     "empty_quantized", "mx_quantize", "mx_dequantize", "mx_gemm", "mx_gemv", "mx_workspace_bytes",
     "mx_status_string", "mx_version", "MX_OP_MOE_ROUTE", "mx_moe_route", "mx_quantize_rows", "mx_moe_combine",
     "moe_forward", "mx_rmsnorm_quantize", "MX_FMT_MXFP8_E4M3", "MX_FMT_MXFP8_E5M2", "MX_FMT_MXFP6_E2M3",
-    "MX_FMT_MXFP6_E3M2", "element_bits",
+    "MX_FMT_MXFP6_E3M2", "element_bits", "MX_FMT_MXFP4_K16", "MX_FMT_FP4_TENSOR", "MX_QUANT_SCALE_FLOOR",
+    "padded_cols",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -27,17 +28,26 @@ library_path = os.path.join(_PKG, "libmx.so")
 
 MX_FMT_MXFP4, MX_FMT_NVFP4 = 0, 1
 MX_FMT_MXFP8_E4M3, MX_FMT_MXFP8_E5M2, MX_FMT_MXFP6_E2M3, MX_FMT_MXFP6_E3M2 = 2, 3, 4, 5
+MX_FMT_MXFP4_K16, MX_FMT_FP4_TENSOR = 6, 7
 MX_DT_F32, MX_DT_BF16 = 0, 1
-MX_QUANT_DEFAULT, MX_QUANT_STATIC_GLOBAL = 0, 1
+MX_QUANT_DEFAULT, MX_QUANT_STATIC_GLOBAL, MX_QUANT_SCALE_FLOOR = 0, 1, 2
 MX_OP_QUANTIZE, MX_OP_GEMM, MX_OP_MOE_ROUTE = 0, 1, 2
 STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_ALIGN", -4: "MX_ERR_DTYPE",
           -5: "MX_ERR_UNSUPPORTED", -6: "MX_ERR_HIP", -7: "MX_ERR_WORKSPACE", -8: "MX_ERR_FORMAT"}
 _FMT = {"mxfp4": MX_FMT_MXFP4, "nvfp4": MX_FMT_NVFP4, "mxfp8_e4m3": MX_FMT_MXFP8_E4M3,
-        "mxfp8_e5m2": MX_FMT_MXFP8_E5M2, "mxfp6_e2m3": MX_FMT_MXFP6_E2M3, "mxfp6_e3m2": MX_FMT_MXFP6_E3M2}
+        "mxfp8_e5m2": MX_FMT_MXFP8_E5M2, "mxfp6_e2m3": MX_FMT_MXFP6_E2M3, "mxfp6_e3m2": MX_FMT_MXFP6_E3M2,
+        "mxfp4_k16": MX_FMT_MXFP4_K16, "fp4_tensor": MX_FMT_FP4_TENSOR}
 _BLOCK = {MX_FMT_MXFP4: 32, MX_FMT_NVFP4: 16, MX_FMT_MXFP8_E4M3: 32, MX_FMT_MXFP8_E5M2: 32,
-          MX_FMT_MXFP6_E2M3: 32, MX_FMT_MXFP6_E3M2: 32}
+          MX_FMT_MXFP6_E2M3: 32, MX_FMT_MXFP6_E3M2: 32, MX_FMT_MXFP4_K16: 16, MX_FMT_FP4_TENSOR: 2}
 _BITS = {MX_FMT_MXFP4: 4, MX_FMT_NVFP4: 4, MX_FMT_MXFP8_E4M3: 8, MX_FMT_MXFP8_E5M2: 8,
-         MX_FMT_MXFP6_E2M3: 6, MX_FMT_MXFP6_E3M2: 6}
+         MX_FMT_MXFP6_E2M3: 6, MX_FMT_MXFP6_E3M2: 6, MX_FMT_MXFP4_K16: 4, MX_FMT_FP4_TENSOR: 4}
+
+
+def padded_cols(cols: int, fmt) -> int:
+    """Stored row length: E8M0-scaled formats pad rows to whole blocks."""
+    f = _FMT[fmt] if isinstance(fmt, str) else fmt
+    k = _BLOCK[f]
+    return -(-cols // k) * k if f not in (MX_FMT_NVFP4, MX_FMT_FP4_TENSOR) else cols
 
 
 def element_bits(fmt) -> int:
@@ -143,7 +153,8 @@ class MXTensor:
     global_scale: object = None   # float32 [1] (NVFP4)
 
     def desc(self) -> CMxTensor:
-        return CMxTensor(self.fmt, 0, self.rows, self.cols, self.codes.data_ptr(), self.scales.data_ptr(),
+        return CMxTensor(self.fmt, 0, self.rows, self.cols, self.codes.data_ptr(),
+                         self.scales.data_ptr() if self.scales is not None else None,
                          self.global_scale.data_ptr() if self.global_scale is not None else None)
 
     @property
@@ -157,9 +168,10 @@ def empty_quantized(rows: int, cols: int, fmt="mxfp4", device="cuda", lead=()) -
     import torch
     f = _FMT[fmt] if isinstance(fmt, str) else fmt
     k = _BLOCK[f]
-    codes = torch.empty(rows, cols * _BITS[f] // 8, dtype=torch.uint8, device=device)
-    scales = torch.empty(rows, cols // k, dtype=torch.uint8, device=device)
-    g = torch.ones(1, dtype=torch.float32, device=device) if f == MX_FMT_NVFP4 else None
+    p = padded_cols(cols, f)
+    codes = torch.empty(rows, p * _BITS[f] // 8, dtype=torch.uint8, device=device)
+    scales = None if f == MX_FMT_FP4_TENSOR else torch.empty(rows, p // k, dtype=torch.uint8, device=device)
+    g = torch.ones(1, dtype=torch.float32, device=device) if f in (MX_FMT_NVFP4, MX_FMT_FP4_TENSOR) else None
     return MXTensor(f, rows, cols, codes, scales, g)
 
 
@@ -167,8 +179,11 @@ def mx_workspace_bytes(op: int, desc, flags: int = 0) -> int:
     return int(lib().mx_workspace_bytes(op, ctypes.cast(ctypes.pointer(desc), ctypes.c_void_p), flags))
 
 
-def mx_quantize(x, fmt="mxfp4", out: MXTensor | None = None, static_global=None, workspace=None) -> MXTensor:
-    """Quantize a 2-D fp32/bf16 CUDA tensor (row pitch x.stride(0))."""
+def mx_quantize(x, fmt="mxfp4", out: MXTensor | None = None, static_global=None, workspace=None,
+                rule: str = "ceil") -> MXTensor:
+    """Quantize a 2-D fp32/bf16 CUDA tensor (row pitch x.stride(0)).
+    static_global: NVFP4's calibrated per-tensor scale, or MXFP4_K16's tensor
+    scale g.  rule="floor" selects the OCP exponent rule (E8M0 formats)."""
     import torch
     assert x.dim() == 2 and x.stride(1) == 1
     rows, cols = x.shape
@@ -176,8 +191,15 @@ def mx_quantize(x, fmt="mxfp4", out: MXTensor | None = None, static_global=None,
         out = empty_quantized(rows, cols, fmt, x.device)
     flags = MX_QUANT_DEFAULT
     if static_global is not None:
+        if out.global_scale is None:
+            out.global_scale = torch.empty(1, dtype=torch.float32, device=x.device)
         out.global_scale.fill_(float(static_global))
-        flags = MX_QUANT_STATIC_GLOBAL
+        if out.fmt == MX_FMT_NVFP4:
+            flags = MX_QUANT_STATIC_GLOBAL
+    if rule == "floor":
+        flags = MX_QUANT_SCALE_FLOOR
+    elif rule != "ceil":
+        raise ValueError(rule)
     d = out.desc()
     need = mx_workspace_bytes(MX_OP_QUANTIZE, d, flags)
     if need and workspace is None:

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmx.so")
-SOURCES = ["quantize.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemm_mxw.hip", "gemv.hip", "moe.hip", "norm_quant.hip", "mx_api.cpp"]
+SOURCES = ["quantize.hip", "quantize_variant.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemm_mxw.hip", "gemv.hip", "moe.hip", "norm_quant.hip", "mx_api.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are disabled for all device code (the compiler

@@ -19,12 +19,19 @@ constexpr size_t kNvPartialBytes = 4096 * sizeof(uint32_t);
 
 inline bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
-inline int block_of(int32_t fmt) { return fmt == MX_FMT_NVFP4 ? 16 : 32; }
-inline bool fmt_known(int32_t fmt) { return fmt >= MX_FMT_MXFP4 && fmt <= MX_FMT_MXFP6_E3M2; }
+inline int block_of(int32_t fmt) {
+  return fmt == MX_FMT_NVFP4 || fmt == MX_FMT_MXFP4_K16 ? 16 : (fmt == MX_FMT_FP4_TENSOR ? 2 : 32);
+}
+inline bool fmt_known(int32_t fmt) { return fmt >= MX_FMT_MXFP4 && fmt <= MX_FMT_FP4_TENSOR; }
+// formats with E8M0 block scales: rows of any length (the last block zero-padded)
+inline bool fmt_e8m0(int32_t fmt) { return fmt != MX_FMT_NVFP4 && fmt != MX_FMT_FP4_TENSOR; }
+inline int64_t pad_to(int64_t v, int64_t k) { return (v + k - 1) / k * k; }
 // MXFP8 / MXFP6 (every MX element format but E2M1)
 inline bool fmt_wide(int32_t fmt) { return fmt >= MX_FMT_MXFP8_E4M3 && fmt <= MX_FMT_MXFP6_E3M2; }
 // element-format code of the block-scaled MFMA: E4M3 0, E5M2 1, E2M3 2, E3M2 3, E2M1 4
-inline int mfma_fmt(int32_t fmt) { return fmt == MX_FMT_MXFP4 ? 4 : fmt - MX_FMT_MXFP8_E4M3; }
+inline int mfma_fmt(int32_t fmt) {
+  return (fmt == MX_FMT_MXFP4 || fmt == MX_FMT_MXFP4_K16) ? 4 : fmt - MX_FMT_MXFP8_E4M3;
+}
 
 inline size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 inline int esize(int32_t dt) { return dt == MX_DT_F32 ? 4 : 2; }
@@ -37,20 +44,21 @@ int check_tensor(const mx_tensor* t) {
   if (t->reserved != 0) return MX_ERR_SHAPE;
   if (t->rows < 0 || t->cols < 0 || t->rows > kMaxDim || t->cols > kMaxDim) return MX_ERR_SHAPE;
   if (t->rows > 0 && t->cols > 0 && t->rows > kMaxElems / t->cols) return MX_ERR_SHAPE;
-  if (t->cols % block_of(t->fmt) != 0) return MX_ERR_UNSUPPORTED;
+  if (!fmt_e8m0(t->fmt) && t->cols % block_of(t->fmt) != 0) return MX_ERR_UNSUPPORTED;
   if (t->rows == 0 || t->cols == 0) return MX_OK;
-  if (!t->codes || !t->scales) return MX_ERR_NULL;
-  if (t->fmt == MX_FMT_NVFP4 && !t->global_scale) return MX_ERR_NULL;
-  if (!al16(t->codes) || !al16(t->scales)) return MX_ERR_ALIGN;
+  if (!t->codes || (!t->scales && t->fmt != MX_FMT_FP4_TENSOR)) return MX_ERR_NULL;
+  if ((t->fmt == MX_FMT_NVFP4 || t->fmt == MX_FMT_FP4_TENSOR) && !t->global_scale) return MX_ERR_NULL;
+  if (!al16(t->codes) || (t->scales && !al16(t->scales))) return MX_ERR_ALIGN;
   if (t->global_scale && (reinterpret_cast<uintptr_t>(t->global_scale) & 3u)) return MX_ERR_ALIGN;
   return MX_OK;
 }
 
-int check_dense_input(const void* x, int32_t dt, int64_t ld, int64_t rows, int64_t cols) {
+int check_dense_input(const void* x, int32_t dt, int64_t ld, int64_t rows, int64_t cols, bool any_pitch = false) {
   if (!dtype_ok(dt)) return MX_ERR_DTYPE;
   if (ld < cols) return MX_ERR_SHAPE;
   if (rows == 0 || cols == 0) return MX_OK;
   if (!x) return MX_ERR_NULL;
+  if (any_pitch) return (reinterpret_cast<uintptr_t>(x) % esize(dt)) ? MX_ERR_ALIGN : MX_OK;   // element loads
   if (!al16(x) || (ld * esize(dt)) % 16 != 0) return MX_ERR_ALIGN;
   return MX_OK;
 }
@@ -87,6 +95,7 @@ size_t mx_workspace_bytes(int32_t op, const void* desc, int32_t flags) {
   if (op == MX_OP_QUANTIZE) {
     const mx_tensor* t = static_cast<const mx_tensor*>(desc);
     if (t->fmt == MX_FMT_NVFP4 && !(flags & MX_QUANT_STATIC_GLOBAL)) return kNvPartialBytes;
+    if (t->fmt == MX_FMT_FP4_TENSOR) return kNvPartialBytes;
     return 0;
   }
   if (op == MX_OP_GEMM) {
@@ -105,20 +114,37 @@ int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* o
                 size_t workspace_bytes, void* stream) {
   int st = check_tensor(out);
   if (st) return st;
-  if (flags != MX_QUANT_DEFAULT && flags != MX_QUANT_STATIC_GLOBAL) return MX_ERR_UNSUPPORTED;
-  if (out->fmt != MX_FMT_NVFP4 && flags != MX_QUANT_DEFAULT) return MX_ERR_UNSUPPORTED;
-  st = check_dense_input(x, x_dtype, ld_x, out->rows, out->cols);
-  if (st) return st;
+  if (flags != MX_QUANT_DEFAULT && flags != MX_QUANT_STATIC_GLOBAL && flags != MX_QUANT_SCALE_FLOOR)
+    return MX_ERR_UNSUPPORTED;
+  if (flags == MX_QUANT_STATIC_GLOBAL && out->fmt != MX_FMT_NVFP4) return MX_ERR_UNSUPPORTED;
+  if (flags == MX_QUANT_SCALE_FLOOR && (!fmt_e8m0(out->fmt) || (out->fmt == MX_FMT_MXFP4_K16 && out->global_scale)))
+    return MX_ERR_UNSUPPORTED;
   const bool dyn_nv = out->fmt == MX_FMT_NVFP4 && !(flags & MX_QUANT_STATIC_GLOBAL);
-  if (dyn_nv && (!workspace || workspace_bytes < kNvPartialBytes || !al16(workspace))) return MX_ERR_WORKSPACE;
+  const bool naive = out->fmt == MX_FMT_FP4_TENSOR;
+  // rows of whole 32-element blocks run in the vector kernels (either exponent
+  // rule); 16-element E8M0 blocks and ragged rows in the per-block kernel
+  const bool variant = fmt_e8m0(out->fmt) && (out->fmt == MX_FMT_MXFP4_K16 || out->cols % 32 != 0);
+  const bool floor_rule = flags == MX_QUANT_SCALE_FLOOR;
+  st = check_dense_input(x, x_dtype, ld_x, out->rows, out->cols, naive || variant);
+  if (st) return st;
+  if ((dyn_nv || naive) && (!workspace || workspace_bytes < kNvPartialBytes || !al16(workspace)))
+    return MX_ERR_WORKSPACE;
   if (out->rows == 0 || out->cols == 0) return MX_OK;
   const int bf = x_dtype == MX_DT_BF16;
   hipError_t e;
-  if (out->fmt == MX_FMT_MXFP4) {
-    e = mxk::launch_quant_mx(x, bf, ld_x, out->rows, out->cols, out->codes, out->scales, as_stream(stream));
+  if (naive) {
+    e = mxk::launch_quant_naive(x, bf, ld_x, out->rows, out->cols, out->codes, out->global_scale,
+                                static_cast<uint32_t*>(workspace), (int)(kNvPartialBytes / 4), as_stream(stream));
+  } else if (variant) {
+    e = mxk::launch_quant_variant(mfma_fmt(out->fmt), block_of(out->fmt), floor_rule,
+                                  out->fmt == MX_FMT_MXFP4_K16 ? out->global_scale : nullptr, x, bf, ld_x, out->rows,
+                                  out->cols, out->codes, out->scales, as_stream(stream));
+  } else if (out->fmt == MX_FMT_MXFP4) {
+    e = mxk::launch_quant_mx(x, bf, ld_x, out->rows, out->cols, out->codes, out->scales, as_stream(stream), nullptr, 0,
+                             floor_rule);
   } else if (fmt_wide(out->fmt)) {
     e = mxk::launch_quant_wide(mfma_fmt(out->fmt), x, bf, ld_x, out->rows, out->cols, out->codes, out->scales,
-                               as_stream(stream));
+                               as_stream(stream), floor_rule);
   } else {
     e = mxk::launch_quant_nv(x, bf, ld_x, out->rows, out->cols, out->codes, out->scales, out->global_scale, !dyn_nv,
                              static_cast<uint32_t*>(workspace), as_stream(stream));
@@ -129,9 +155,20 @@ int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* o
 int mx_dequantize(const mx_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, void* stream) {
   int st = check_tensor(in);
   if (st) return st;
-  st = check_dense_input(y, y_dtype, ld_y, in->rows, in->cols);
+  const bool elementwise = in->fmt == MX_FMT_FP4_TENSOR || in->fmt == MX_FMT_MXFP4_K16 ||
+                           (fmt_e8m0(in->fmt) && in->cols % 32 != 0);
+  st = check_dense_input(y, y_dtype, ld_y, in->rows, in->cols, elementwise);
   if (st) return st;
   if (in->rows == 0 || in->cols == 0) return MX_OK;
+  const bool ybf = y_dtype == MX_DT_BF16;
+  if (in->fmt == MX_FMT_FP4_TENSOR)
+    return hip_status(mxk::launch_dequant_naive(in->codes, in->global_scale, in->rows, in->cols, y, ybf, ld_y,
+                                                as_stream(stream)));
+  if (in->fmt == MX_FMT_MXFP4_K16 || (fmt_e8m0(in->fmt) && in->cols % 32 != 0))
+    return hip_status(mxk::launch_dequant_variant(mfma_fmt(in->fmt), block_of(in->fmt),
+                                                  in->fmt == MX_FMT_MXFP4_K16 ? in->global_scale : nullptr,
+                                                  in->codes, in->scales, in->rows, in->cols, y, ybf, ld_y,
+                                                  as_stream(stream)));
   if (fmt_wide(in->fmt))
     return hip_status(mxk::launch_dequant_wide(mfma_fmt(in->fmt), in->codes, in->scales, in->rows, in->cols, y,
                                                y_dtype == MX_DT_BF16, ld_y, as_stream(stream)));
@@ -148,6 +185,11 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
   if (st) return st;
   const int32_t fmt = a->b->fmt;
   if (a->b->cols != a->K) return MX_ERR_SHAPE;
+  if (fmt == MX_FMT_MXFP4_K16 || fmt == MX_FMT_FP4_TENSOR) return MX_ERR_UNSUPPORTED;
+  if (a->a && (a->a->fmt == MX_FMT_MXFP4_K16 || a->a->fmt == MX_FMT_FP4_TENSOR)) return MX_ERR_UNSUPPORTED;
+  // a row length that is not a multiple of 32 is stored zero-padded: the
+  // product over the padded length is the same
+  const int64_t Kp = fmt == MX_FMT_NVFP4 ? a->K : pad_to(a->K, 32);
   if (a->groups == 0) {
     if (a->b->rows != a->N) return MX_ERR_SHAPE;
   } else {
@@ -168,11 +210,11 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
       if (!a->c) return MX_ERR_NULL;
       if (!al16(a->c)) return MX_ERR_ALIGN;
     }
-    if (a->K % 128 != 0 || a->K > (int64_t(1) << 22)) return MX_ERR_UNSUPPORTED;
+    if (Kp % 128 != 0 || Kp > (int64_t(1) << 22)) return MX_ERR_UNSUPPORTED;
     if (a->M == 0 || a->N == 0) return MX_OK;
     return hip_status(mxk::launch_gemm_mxw(mfma_fmt(a->a->fmt), mfma_fmt(fmt), a->a->codes, a->a->scales,
                                            a->b->codes, a->b->scales, a->c, a->c_dtype == MX_DT_BF16, a->ldc,
-                                           a->M, a->N, a->K, as_stream(stream)));
+                                           a->M, a->N, Kp, as_stream(stream)));
   }
   if (fmt_wide(fmt)) return MX_ERR_UNSUPPORTED;   // dynamic activation quantization is MXFP4 only
   if (!dtype_ok(a->c_dtype)) return MX_ERR_DTYPE;
@@ -193,6 +235,7 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
     a_codes = a->a->codes; a_scales = a->a->scales; a_global = a->a->global_scale;
   } else {
     if (fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;   // dynamic path quantizes A to MXFP4
+    if (a->K % 32 != 0) return MX_ERR_UNSUPPORTED;        // ... with whole blocks only
     st = check_dense_input(a->a_raw, a->a_raw_dtype, a->lda_raw, a->M, a->K);
     if (st) return st;
     if (a->M > kMaxElems / (a->K > 0 ? a->K : 1)) return MX_ERR_SHAPE;
@@ -220,7 +263,7 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
   const int cbf = a->c_dtype == MX_DT_BF16;
   if (fmt == MX_FMT_MXFP4)
     return hip_status(mxk::launch_gemm_mx(a_codes, a_scales, a->b->codes, a->b->scales, a->c, cbf, a->ldc, a->M, a->N,
-                                          a->K, a->groups, a->group_offsets, s));
+                                          Kp, a->groups, a->group_offsets, s));
   return hip_status(mxk::launch_gemm_nv(a_codes, a_scales, a_global, a->b->codes, a->b->scales, a->b->global_scale,
                                         a->c, cbf, a->ldc, a->M, a->N, a->K, s));
 }
@@ -242,7 +285,7 @@ int mx_quantize_rows(const void* x, int32_t x_dtype, int64_t ld_x, int64_t x_row
                      const mx_tensor* out, void* stream) {
   int st = check_tensor(out);
   if (st) return st;
-  if (out->fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
+  if (out->fmt != MX_FMT_MXFP4 || out->cols % 32 != 0) return MX_ERR_UNSUPPORTED;
   if (x_rows < 0) return MX_ERR_SHAPE;
   st = check_dense_input(x, x_dtype, ld_x, x_rows, out->cols);
   if (st) return st;
@@ -296,7 +339,7 @@ int mx_gemv(const void* x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_te
   int st = check_tensor(w);
   if (st) return st;
   if (x_dtype != MX_DT_BF16 || y_dtype != MX_DT_BF16) return MX_ERR_DTYPE;
-  if (w->fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
+  if (w->fmt != MX_FMT_MXFP4 || w->cols % 32 != 0) return MX_ERR_UNSUPPORTED;
   if (M < 0) return MX_ERR_SHAPE;
   if (M > 16) return MX_ERR_UNSUPPORTED;
   const int64_t N = w->rows, K = w->cols;

@@ -7,7 +7,8 @@ namespace mxk {
 // gidx != nullptr: output row r quantizes input row gidx[r] (zero row if the
 // index is outside [0, x_rows)).
 hipError_t launch_quant_mx(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
-                           uint8_t* scales, hipStream_t st, const int32_t* gidx = nullptr, int64_t x_rows = 0);
+                           uint8_t* scales, hipStream_t st, const int32_t* gidx = nullptr, int64_t x_rows = 0,
+                           bool floor_rule = false);
 int nv_partials_count(int64_t rows, int64_t cols, int xdt_bf16);
 hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* gscale, bool static_global, uint32_t* partial, hipStream_t st);
@@ -22,12 +23,24 @@ hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const
 // Wider MX elements; fmt is the block-scaled MFMA's element code (E4M3 0,
 // E5M2 1, E2M3 2, E3M2 3; the GEMM also takes E2M1 4).
 hipError_t launch_quant_wide(int fmt, const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols,
-                             uint8_t* codes, uint8_t* scales, hipStream_t st);
+                             uint8_t* codes, uint8_t* scales, hipStream_t st, bool floor_rule = false);
 hipError_t launch_dequant_wide(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, void* y,
                                bool out_bf16, int64_t ldy, hipStream_t st);
 hipError_t launch_gemm_mxw(int fa, int fb, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                            const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
                            hipStream_t st);
+// Emulation variants (quantize_variant.hip): block 16 or 32, the OCP floor
+// rule, a per-tensor scale g (NULL = 1), rows of any length (zero-padded to
+// whole blocks); naive per-tensor FP4.
+hipError_t launch_quant_variant(int fmt, int block, bool floor_rule, const float* g, const void* x, int xdt_bf16,
+                                int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                hipStream_t st);
+hipError_t launch_dequant_variant(int fmt, int block, const float* g, const uint8_t* codes, const uint8_t* scales,
+                                  int64_t rows, int64_t cols, void* y, bool out_bf16, int64_t ldy, hipStream_t st);
+hipError_t launch_quant_naive(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
+                              float* s, uint32_t* partial, int max_partials, hipStream_t st);
+hipError_t launch_dequant_naive(const uint8_t* codes, const float* s, int64_t rows, int64_t cols, void* y, bool out_bf16,
+                                int64_t ldy, hipStream_t st);
 hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st);
 hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int experts, int32_t* offsets,

@@ -40,8 +40,10 @@ __device__ __forceinline__ uint32_t block_umax(uint32_t v) {
 }
 
 // MODE 0: contiguous rows; 1: rows ld apart; 2: output row r is input row
-// gidx[r] (an index outside [0, x_rows) gives a zero row).
-template <typename TIn, int MODE>
+// gidx[r] (an index outside [0, x_rows) gives a zero row).  FLOOR: the OCP
+// exponent rule e = floor(log2 max|x|) - 2 (= F - 129), elements beyond 6
+// saturating (the conversion saturates), same floor of -29.
+template <typename TIn, int MODE, bool FLOOR = false>
 __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr,
                                                  uint32_t nvec, uint8_t* __restrict__ codes,
                                                  uint8_t* __restrict__ scales, const int32_t* __restrict__ gidx,
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int6
 #pragma unroll
       for (int i = 0; i < EPL; ++i) am = max(am, fbits(f[i]) & 0x7fffffffu);
       am = block_umax<LPB>(am);
-      const int e = mx_block_exp(am);
+      const int e = FLOOR ? max((int)(am >> 23) - 129, -29) : mx_block_exp(am);
       const float s = pow2f(e);
       uint32_t out = 0;
       out = cvt_fp4x2<0>(out, f[0], f[1], s);
@@ -315,11 +317,16 @@ template <> struct WideFmt<1> { static constexpr int E = 5, M = 2, BIAS = 15, P 
 template <> struct WideFmt<2> { static constexpr int E = 2, M = 3, BIAS = 1, P = 2; static constexpr uint32_t FE = 0x700000u; };
 template <> struct WideFmt<3> { static constexpr int E = 3, M = 2, BIAS = 3, P = 4; static constexpr uint32_t FE = 0x600000u; };
 
-template <int F>
+template <int F, bool FLOOR = false>
 __device__ __forceinline__ int wide_block_exp(uint32_t amax_bits) {
   using T = WideFmt<F>;
-  const int e = (int)(amax_bits >> 23) - 127 - T::P + ((amax_bits & 0x7fffffu) > T::FE ? 1 : 0);
+  // FLOOR: the OCP rule floor(log2 max|x|) - P
+  const int e = (int)(amax_bits >> 23) - 127 - T::P + ((!FLOOR && (amax_bits & 0x7fffffu) > T::FE) ? 1 : 0);
   return e < -27 - T::P ? -27 - T::P : e;
+}
+template <int F>
+__device__ __forceinline__ float wide_emax() {
+  return F == 0 ? 448.0f : (F == 1 ? 57344.0f : (F == 2 ? 7.5f : 28.0f));
 }
 
 // Code of x (sign from x's bit pattern) for the block scale factor inv = 2^-e.
@@ -327,7 +334,9 @@ template <int F>
 __device__ __forceinline__ uint32_t wide_encode(uint32_t xbits, float inv) {
   using T = WideFmt<F>;
   constexpr int BITS = 1 + T::E + T::M;
-  const float v = ffrom(xbits & 0x7fffffffu) * inv;
+  // saturation (only reachable under the floor rule): rounding a value in
+  // (Emax, Emax + half a step) and then saturating gives Emax too
+  const float v = fminf(ffrom(xbits & 0x7fffffffu) * inv, wide_emax<F>());
   const uint32_t u = fbits(v);
   const uint32_t sub = (uint32_t)__builtin_rintf(v * pow2f(T::BIAS - 1 + T::M));
   uint32_t t = u >> (23 - T::M);
@@ -338,7 +347,7 @@ __device__ __forceinline__ uint32_t wide_encode(uint32_t xbits, float inv) {
   return mag | ((xbits >> 31) << (BITS - 1));
 }
 
-template <typename TIn, int F, bool CONTIG>
+template <typename TIn, int F, bool CONTIG, bool FLOOR = false>
 __global__ __launch_bounds__(QT) void k_quant_wide(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr, uint32_t nvec,
                                                    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   constexpr int EPL = 16 / (int)sizeof(TIn);
@@ -386,7 +395,7 @@ __global__ __launch_bounds__(QT) void k_quant_wide(const TIn* __restrict__ x, in
 #pragma unroll
       for (int i = 0; i < EPL; ++i) am = max(am, xb[i] & 0x7fffffffu);
       am = block_umax<LPB>(am);
-      const int e = wide_block_exp<F>(am);
+      const int e = wide_block_exp<F, FLOOR>(am);
       const float inv = pow2f(-e);
       uint32_t c[EPL];
 #pragma unroll
@@ -506,13 +515,21 @@ static int grid_for(uint64_t work_items, int per_block) {
 }
 
 hipError_t launch_quant_mx(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
-                           uint8_t* scales, hipStream_t st, const int32_t* gidx, int64_t x_rows) {
+                           uint8_t* scales, hipStream_t st, const int32_t* gidx, int64_t x_rows, bool floor_rule) {
   const int epl = xdt_bf16 ? 8 : 4;
   const uint32_t vpr = (uint32_t)(cols / epl);
   const uint32_t nvec = (uint32_t)(rows * cols / epl);
   const int mode = gidx ? 2 : (ldx == cols ? 0 : 1);
   const int grid = grid_for(nvec, QT * QU);
 #define MX_QMX(T, MODE) hipLaunchKernelGGL((k_quant_mx<T, MODE>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales, gidx, x_rows)
+#define MX_QMXF(T, MODE) hipLaunchKernelGGL((k_quant_mx<T, MODE, true>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales, gidx, x_rows)
+  if (floor_rule) {
+    if (mode == 2) return hipErrorInvalidValue;
+    if (xdt_bf16) { if (mode == 0) MX_QMXF(uint16_t, 0); else MX_QMXF(uint16_t, 1); }
+    else { if (mode == 0) MX_QMXF(float, 0); else MX_QMXF(float, 1); }
+#undef MX_QMXF
+    return hipGetLastError();
+  }
   if (xdt_bf16) {
     if (mode == 0) MX_QMX(uint16_t, 0); else if (mode == 1) MX_QMX(uint16_t, 1); else MX_QMX(uint16_t, 2);
   } else {
@@ -571,14 +588,15 @@ hipError_t launch_dequant(bool nv, const uint8_t* codes, const uint8_t* scales, 
 }
 
 hipError_t launch_quant_wide(int fmt, const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols,
-                             uint8_t* codes, uint8_t* scales, hipStream_t st) {
+                             uint8_t* codes, uint8_t* scales, hipStream_t st, bool floor_rule) {
   const int epl = xdt_bf16 ? 8 : 4;
   const uint32_t vpr = (uint32_t)(cols / epl);
   const uint32_t nvec = (uint32_t)(rows * cols / epl);
   const bool contig = ldx == cols;
   const int grid = grid_for(nvec, QT * QU);
-#define MX_QW3(T, F, C) hipLaunchKernelGGL((k_quant_wide<T, F, C>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales)
-#define MX_QW2(T, F) if (contig) MX_QW3(T, F, true); else MX_QW3(T, F, false)
+#define MX_QW4(T, F, C, FL) hipLaunchKernelGGL((k_quant_wide<T, F, C, FL>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales)
+#define MX_QW3(T, F, C) if (floor_rule) MX_QW4(T, F, C, true); else MX_QW4(T, F, C, false)
+#define MX_QW2(T, F) if (contig) { MX_QW3(T, F, true); } else { MX_QW3(T, F, false); }
 #define MX_QW(F) if (xdt_bf16) { MX_QW2(uint16_t, F); } else { MX_QW2(float, F); }
   switch (fmt) {
     case 0: MX_QW(0); break;
@@ -590,6 +608,7 @@ hipError_t launch_quant_wide(int fmt, const void* x, int xdt_bf16, int64_t ldx, 
 #undef MX_QW
 #undef MX_QW2
 #undef MX_QW3
+#undef MX_QW4
   return hipGetLastError();
 }
 

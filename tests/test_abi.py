@@ -57,9 +57,8 @@ def test_quantize_validation():
     assert L.mx_quantize(FAKE, 0, 256, None, 0, None, 0, None) == -1           # NULL descriptor
     assert quant(x=None) == -1                                                  # NULL input
     assert quant(t=T(codes=None)) == -1
-    assert quant(t=T(fmt=7)) == -8                                              # unknown format
+    assert quant(t=T(fmt=9)) == -8                                              # unknown format
     assert quant(dt=5) == -4                                                    # unknown dtype
-    assert quant(t=T(cols=48)) == -5                                            # cols % 32 != 0
     assert quant(t=T(fmt=1, cols=40, g=FAKE)) == -5                             # cols % 16 != 0
     assert quant(ld=100) == -2                                                  # ld < cols
     assert quant(t=T(rows=-1)) == -2
@@ -132,7 +131,7 @@ def test_gemm_validation():
     assert call_gemm(mism) == -8                              # A NVFP4, B MXFP4
     assert call_gemm(gemm_args(groups=2)) == -1               # grouped without offsets
     assert call_gemm(gemm_args(groups=2, fmt=1, group_offsets=FAKE)) == -5
-    assert call_gemm(gemm_args(K=48)) == -5                   # K % 32
+    assert call_gemm(gemm_args(K=48, M=0)) == 0              # K % 32 != 0: zero-padded rows accepted
     assert call_gemm(gemm_args(fmt=1, K=48)) == -5            # NVFP4 GEMM needs K % 32 == 0
     # dynamic activation path
     d = gemm_args(a=False, a_raw=FAKE, a_raw_dtype=1, lda_raw=256)
@@ -233,13 +232,44 @@ def test_rmsnorm_quantize_validation():
     assert L.mx_rmsnorm_quantize(FAKE, 1, 32800, FAKE, 0, f(1e-6), ctypes.byref(big), 0, None) == -5
 
 
+def test_variant_format_validation():
+    """Emulation variants: MXFP4_K16 (E8M0 per 16, optional tensor scale),
+    FP4_TENSOR (one fp32 scale), the floor-rule flag, ragged rows."""
+    L = mx.lib()
+    assert quant(t=T(fmt=7, g=None)) == -1                                  # FP4_TENSOR needs its scale
+    assert quant(t=T(fmt=7, g=FAKE)) == -7                                  # ... and a workspace
+    assert quant(t=T(fmt=7, cols=255, g=FAKE), ld=256) == -5                # odd cols
+    assert quant(t=T(fmt=7, g=FAKE), flags=2) == -5                         # no floor rule
+    assert quant(t=T(fmt=6, g=FAKE), flags=2) == -5                         # floor rule has no tensor scale
+    assert quant(t=T(fmt=6), flags=1) == -5                                 # static flag is NVFP4's
+    assert quant(t=T(fmt=1, g=FAKE), flags=2) == -5                         # NVFP4: no floor rule
+    assert quant(t=T(fmt=1, cols=40, g=FAKE), ld=48) == -5                  # NVFP4 rows stay whole
+    assert quant(t=T(fmt=0, rows=0, cols=50), ld=56) == 0                    # ragged MXFP4: accepted (empty)
+    assert quant(t=T(fmt=6, rows=0, cols=7), ld=8) == 0
+    # GEMM: variants are not matrix-core formats; ragged K with dynamic A is not provided
+    g = gemm_args(K=256, fmt=6)
+    assert call_gemm(g) == -5
+    g = gemm_args(K=256)
+    g.a.contents.fmt = 7
+    g.a.contents.global_scale = FAKE
+    assert call_gemm(g) == -5
+    d = gemm_args(a=False, a_raw=FAKE, a_raw_dtype=1, lda_raw=264, K=250, ldc=128)
+    assert call_gemm(d) == -5
+    # GEMV, gathered quantize: whole blocks only
+    w = T(0, 512, 250)
+    assert L.mx_gemv(FAKE, 1, 1, 256, ctypes.byref(w), FAKE, 1, 512, None) == -5
+    t = T(fmt=0, rows=16, cols=250)
+    assert L.mx_quantize_rows(FAKE, 0, 256, 10, FAKE, ctypes.byref(t), None) == -5
+    t7 = T(fmt=7, g=FAKE)
+    assert L.mx_workspace_bytes(mx.MX_OP_QUANTIZE, ctypes.cast(ctypes.pointer(t7), ctypes.c_void_p), 0) >= 4096
+
+
 def test_wide_format_validation():
     """MXFP8 / MXFP6 descriptors: quantize and dequantize accept them, the
     GEMM takes any MX pair (dense, pre-quantized A, K % 128 == 0) and every
     other entry point reports them unsupported."""
     L = mx.lib()
     for f in (2, 3, 4, 5):
-        assert quant(t=T(fmt=f, cols=48)) == -5                            # cols % 32
         assert quant(t=T(fmt=f), flags=1) == -5                            # no static-scale flag
         assert quant(t=T(fmt=f, rows=0)) == 0
         assert L.mx_dequantize(ctypes.byref(T(fmt=f)), FAKE + 4, 0, 256, None) == -3
