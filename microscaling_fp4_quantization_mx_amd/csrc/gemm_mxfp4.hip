@@ -545,7 +545,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_ring(MxG
 // ---------------------------------------------------------------------------
 constexpr int BK2 = 256, BKB2 = 128;
 
-template <int BM, int BN, int WM, int WN>
+// SP (K % 512 == 0): the scale bytes of two stages (16 per row) travel
+// together, one lane per row, into a three-entry ring of their own.  Loading a
+// stage's 8 bytes per row touches one cache line per row for 8 bytes; pairing
+// stages halves the line touches and spreading the pair's A and B halves over
+// two stages leaves one scale load per wave per stage (instead of four).
+template <int BM, int BN, int WM, int WN, bool SP>
 __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxGemmParams p) {
   constexpr int NWX = BN / WN;
   constexpr int NT = (BM / WM) * NWX * 64;
@@ -556,8 +561,12 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
   constexpr int SLOT_B = BN * BKB2;
   constexpr int OFF_SA = SLOT_A + SLOT_B;        // 2 x [BM] dwords, then 2 x [BN]
   constexpr int OFF_SB = OFF_SA + 8 * BM;
-  constexpr int SLOT = OFF_SB + 8 * BN;          // 69632
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * SLOT];
+  constexpr int SLOT = SP ? SLOT_A + SLOT_B : OFF_SB + 8 * BN;   // 65536 / 69632
+  constexpr int SCL_OFF = 2 * SLOT;              // SP: ring of 3 x ([BM] + [BN]) x 16 bytes
+  constexpr int SCL_BUF = (BM + BN) * 16;
+  constexpr int SMEM = SP ? SCL_OFF + 3 * SCL_BUF : 2 * SLOT;     // 155648 / 139264
+  constexpr int LPS = SP ? 17 : 20;              // loads per wave per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -627,6 +636,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
   }
   const int srow = (wave * 64 + lane) * KS;
   const int nst = p.K / BK2;
+  // SP: the 16 scale bytes of stages 2P, 2P+1 of row wave*64 + lane -> ring
+  // entry P % 3 (one 16-byte load per lane; half 0 = A rows, half 1 = B rows)
+  auto issue_scales = [&](int P, int half) {
+    uint8_t* dst = smem + SCL_OFF + (P % 3) * SCL_BUF + half * (BM * 16) + wave * 1024;
+    const bool in = 2 * P < nst;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(half ? rsb : rsa, (lds_ptr_t)dst, 16, in ? srow + P * 16 : 0x7ffffff0,
+                                             0, 0, 0);
+  };
   // All offsets in voffset (range checked); stages past the end load zeros.
   auto issue = [&](int st) {
     uint8_t* slot = smem + (st & 1) * SLOT;
@@ -640,12 +657,17 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
     for (int j = 0; j < 8; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + SLOT_A + (wave * 8 + j) * 1024), 16,
                                                in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
+    if (SP) {
+      // scale pair (st + 1) / 2, half (st + 1) % 2 (A rows, then B rows)
+      issue_scales((st + 1) >> 1, (st + 1) & 1);
+    } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(slot + OFF_SA + h * 4 * BM + wave * 256), 4,
-                                               in ? srow + st * 8 + h * 4 : 0x7ffffff0, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(slot + OFF_SB + h * 4 * BN + wave * 256), 4,
-                                               in ? srow + st * 8 + h * 4 : 0x7ffffff0, 0, 0, 0);
+      for (int h = 0; h < 2; ++h) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(slot + OFF_SA + h * 4 * BM + wave * 256), 4,
+                                                 in ? srow + st * 8 + h * 4 : 0x7ffffff0, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(slot + OFF_SB + h * 4 * BN + wave * 256), 4,
+                                                 in ? srow + st * 8 + h * 4 : 0x7ffffff0, 0, 0, 0);
+      }
     }
   };
 
@@ -690,11 +712,22 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
 #pragma unroll
     for (int j = 0; j < TJ; ++j) fb[kk][j] = *reinterpret_cast<const i32x4*>(slot + offb[kk][j]);
   };
-  auto read_scales = [&](int h, const uint8_t* slot) {
+  // scale dword h (blocks 4h..4h+3) of stage st, read from `slot` (or, SP,
+  // from ring entry (st / 2) % 3 at dword 2 * (st % 2) + h of the row)
+  const int ringa = SCL_OFF + (wy * WM + lrow) * 16, ringb = SCL_OFF + BM * 16 + (wx * WN + lrow) * 16;
+  auto read_scales = [&](int h, const uint8_t* slot, int st) {
+    if (SP) {
+      const int o = ((st >> 1) % 3) * SCL_BUF + (2 * (st & 1) + h) * 4;
 #pragma unroll
-    for (int i = 0; i < TI; ++i) sa[h][i] = *reinterpret_cast<const uint32_t*>(slot + offsa + h * 4 * BM + i * 128);
+      for (int i = 0; i < TI; ++i) sa[h][i] = *reinterpret_cast<const uint32_t*>(smem + ringa + o + i * 512);
 #pragma unroll
-    for (int j = 0; j < TJ; ++j) sb[h][j] = *reinterpret_cast<const uint32_t*>(slot + offsb + h * 4 * BN + j * 128);
+      for (int j = 0; j < TJ; ++j) sb[h][j] = *reinterpret_cast<const uint32_t*>(smem + ringb + o + j * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < TI; ++i) sa[h][i] = *reinterpret_cast<const uint32_t*>(slot + offsa + h * 4 * BM + i * 128);
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) sb[h][j] = *reinterpret_cast<const uint32_t*>(slot + offsb + h * 4 * BN + j * 128);
+    }
   };
   // 16 MFMAs of segment KK: the lane's block is 2*KK + khalf, i.e. byte
   // 2*(KK%2) + khalf of scale dword KK/2; shifting by 8*khalf leaves it at
@@ -717,17 +750,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
   __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - (NDS) / 2, 0);  \
   __builtin_amdgcn_sched_barrier(0);
 
+  if (SP) {
+    issue_scales(0, 0);
+    issue_scales(0, 1);
+  }
   issue(0);
   issue(1);
-  asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+  wait_vmcnt<LPS>();
   block_barrier();
   read_frag(0, smem);
-  read_scales(0, smem);
+  read_scales(0, smem, 0);
   for (int s = 0; s < nst; ++s) {
     const uint8_t* cur = smem + (s & 1) * SLOT;
     const uint8_t* nxt = smem + ((s + 1) & 1) * SLOT;
     read_frag(1, cur);
-    read_scales(1, cur);
+    read_scales(1, cur, s);
     read_frag(2, cur);
     MX_SEG(0, 0)
     MX_INTERLEAVE(2 * (TI + TJ) + 4)
@@ -753,11 +790,11 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // B2: this wave's loads of stage s+1 have landed (only stage s+2's 20 may
+    // B2: this wave's loads of stage s+1 have landed (only stage s+2's LPS may
     // still be in flight); after the barrier every wave's have.
-    asm volatile("s_waitcnt vmcnt(20)" ::: "memory");
+    wait_vmcnt<LPS>();
     block_barrier();
-    read_scales(0, nxt);
+    read_scales(0, nxt, s + 1);
     read_frag(0, nxt);
     MX_SEG(3, 2)
     MX_INTERLEAVE(TI + TJ + 4)
@@ -835,8 +872,10 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
   int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   constexpr int NT = (GBM / GWM) * (GBN / GWN) * 64;
-  if (K % BK2 == 0)
-    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
+  if (K % (2 * BK2) == 0)
+    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, true>), dim3((unsigned)grid), dim3(NT), 0, st, p);
+  else if (K % BK2 == 0)
+    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, false>), dim3((unsigned)grid), dim3(NT), 0, st, p);
   else if (K % MX_BK == 0)
     hipLaunchKernelGGL((k_gemm_mx_ring<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
   else
