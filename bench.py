@@ -41,7 +41,7 @@ PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-GEMM_KERNEL = "k_gemm_mx"
+GEMM_KERNEL = "k_gemm_mx_k256"
 PROFILES = os.path.join(ROOT, "profiles")
 
 

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int6
         }
         p = x + (size_t)(ok ? src : 0) * ldx + (size_t)c * EPL;
       }
-      d[u] = ok ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+      // streaming input: non-temporal loads keep it from displacing the
+      // quantized outputs (which the consumer reads next) from the caches
+      d[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)) : u32x4{0, 0, 0, 0};
     }
   };
   // the next iteration's vectors are in flight while this one is converted
@@ -368,7 +370,7 @@ __global__ __launch_bounds__(QT) void k_quant_wide(const TIn* __restrict__ x, in
         const uint32_t r = v / vpr, c = v - r * vpr;
         p = x + (size_t)r * ldx + (size_t)c * EPL;
       }
-      d[u] = v < nvec ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+      d[u] = v < nvec ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)) : u32x4{0, 0, 0, 0};
     }
   };
   u32x4 d[QU], dn[QU];
