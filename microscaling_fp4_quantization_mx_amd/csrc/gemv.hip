@@ -23,6 +23,10 @@
 
 namespace mxk {
 
+// Weight codes and scales are read once per call: non-temporal loads (cache
+// policy bit NT) keep the weight stream from displacing the activations.
+constexpr int GV_NT = 2;
+
 constexpr int GV_T = 256;              // 4 waves
 constexpr int GV_WIN = 64 * 32;        // K elements per window (64 lanes x 1 block)
 constexpr int GV_SK_RB = 4;            // weight rows per workgroup of the small-M kernel
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(GV_T) void k_gemv_sk(const uint16_t* __restrict__ x
     uint32_t sc[RB];
     u32x4 xv[M][4], cw[RB];
 #pragma unroll
-    for (int r = 0; r < RB; ++r) sc[r] = __builtin_amdgcn_raw_buffer_load_b8(rws, kok ? r * KS + kb : 0x7ffffff0, 0, 0);
+    for (int r = 0; r < RB; ++r) sc[r] = __builtin_amdgcn_raw_buffer_load_b8(rws, kok ? r * KS + kb : 0x7ffffff0, 0, GV_NT);
 #pragma unroll
     for (int m = 0; m < M; ++m) {
       const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)(x + (size_t)m * ldx), 0, K * 2, 0x00020000);
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(GV_T) void k_gemv_sk(const uint16_t* __restrict__ x
     }
 #pragma unroll
     for (int r = 0; r < RB; ++r)
-      cw[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwc, kok ? r * KB + kb * 16 : 0x7ffffff0, 0, 0));
+      cw[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwc, kok ? r * KB + kb * 16 : 0x7ffffff0, 0, GV_NT));
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
@@ -209,10 +213,10 @@ __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x
     const int kb = w * 64 + lane;
     const bool kok = kb < KS;
 #pragma unroll
-    for (int r = 0; r < RB; ++r) sc[b][r] = __builtin_amdgcn_raw_buffer_load_b8(rws, kok ? r * KS + kb : oob, 0, 0);
+    for (int r = 0; r < RB; ++r) sc[b][r] = __builtin_amdgcn_raw_buffer_load_b8(rws, kok ? r * KS + kb : oob, 0, GV_NT);
 #pragma unroll
     for (int r = 0; r < RB; ++r)
-      cw[b][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwc, kok ? r * KB + kb * 16 : oob, 0, 0));
+      cw[b][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwc, kok ? r * KB + kb * 16 : oob, 0, GV_NT));
   };
   constexpr int LOADS = XPW + 2 * RB;              // vector-memory ops per window and wave
 
