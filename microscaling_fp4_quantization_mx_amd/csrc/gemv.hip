@@ -4,20 +4,20 @@
 // points"; decode is bound by streaming weight bytes: "NVFP4 Architecture",
 // section "The Problem").
 //
-// The weights are streamed once from HBM and dequantized in registers; the
-// matrix cores are not used.  A lane owns one 32-element MX block of a weight
-// row per 2048-element window of K (64 lanes x 32): its 16 code bytes expand
-// with v_cvt_scalef32_pk_bf16_fp4 into 32 bf16 weights equal to q * 2^e
-// exactly (at most 2 significant bits), and v_dot2_f32_bf16 multiplies pairs
-// of them with the matching bf16 activation pairs into fp32 accumulators, so
-// every product is exact and only the fp32 summation order differs from the
-// plain definition.  Partial sums are reduced across the 64 lanes at the end.
+// The weights are streamed once from HBM and dequantized on chip: 16 code
+// bytes (one 32-element MX block) expand with v_cvt_scalef32_pk_bf16_fp4 into
+// 32 bf16 weights equal to q * 2^e exactly (at most 2 significant bits), so
+// every product with a bf16 activation is exact in fp32 and only the fp32
+// summation order differs from the plain definition.
 //
-// Two kernels:
-//  * M <= 4 is bound by HBM: many small workgroups, split-K across waves.
-//  * M >= 5 is bound by the VALU (one dot2 per weight pair and activation
-//    row): each weight pair is converted once and used for all M rows, and
-//    the activations come from LDS, staged once per workgroup and window.
+// Three kernels:
+//  * M = 1 is bound by HBM: many small workgroups, split-K across waves,
+//    v_dot2_f32_bf16 on the VALU, the lane's partial sums reduced at the end.
+//  * M = 2, 3 (and any M when K is not a multiple of 256): dot2 again, each
+//    weight pair converted once and used for all M rows, activations staged
+//    in LDS once per workgroup and window.
+//  * M = 4 .. 16: one dot2 per weight pair and activation row would make the
+//    VALU the bound, so the matrix cores take the products (bf16 MFMA).
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(GV_T) void k_gemv_sk(const uint16_t* __restrict__ x
   }
 }
 
-// Larger M (VALU-bound).  A workgroup of 8 waves owns 8 x RB weight rows
+// Moderate M (VALU-bound).  A workgroup of 8 waves owns 8 x RB weight rows
 // (RB per wave) and walks the windows of K together.  Per window:
 //  * the activations of all M rows (M x 4 KiB) are copied into LDS by the
 //    LDS-DMA path (buffer_load ... lds), one buffer ahead, in a layout where
@@ -303,6 +303,144 @@ __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x
     y[(size_t)m * ldy + n0 + r] = (uint16_t)f32_to_bf16_rne(tot);
 }
 
+// Skinny M (4..16 rows) on the matrix cores.  With one dot2 per weight pair
+// and activation row the VALU caps the large-M kernel far below the weight
+// stream; v_mfma_f32_16x16x32_bf16 takes the arithmetic instead (activation
+// rows padded to 16; bf16 x bf16 products are exact and the instruction
+// accumulates them without truncation).
+//
+// A workgroup of 8 waves owns 32 weight rows (two 16-row column groups) and
+// walks K in 512-element chunks through a ring of four LDS slots, three
+// chunks in flight, starting at a chunk that depends on the workgroup (so
+// that concurrent workgroups spread over the weight columns).  A chunk's weight codes (32 rows x 256
+// bytes) and activations (8 or 16 rows x 1 KiB) arrive by LDS-DMA copies of
+// whole cache lines,
+// each byte once per workgroup; wave w then covers column group w & 1 and MX
+// blocks 4 (w >> 1) .. + 3 of the chunk, one MFMA per block.  In MFMA block
+// b, lane l (row or column l % 16, lane group g = l / 16) takes K elements
+// 32b + 8g .. + 7: 16 activation bytes (one LDS read) and one code dword,
+// expanded with the block's scale into 8 bf16 weights (exactly q * 2^e) by
+// v_cvt_scalef32_pk_bf16_fp4.  LDS rows are XOR-swizzled in 16-byte units so
+// that these reads are free of bank conflicts.  One barrier per chunk; the
+// four quarter-K partial tiles of each column group meet in LDS at the end.
+constexpr int GM_T = 512;              // 8 waves
+constexpr int GV_MF_MIN_M = 4;         // smallest M that takes the matrix-core kernel
+constexpr int GM_CK = 512;             // K elements per chunk
+
+template <int M>
+__global__ __launch_bounds__(GM_T) void k_gemv_mf(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
+                                                  const uint8_t* __restrict__ ws, int N, int K,
+                                                  uint16_t* __restrict__ y, int64_t ldy) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  constexpr int MA = M <= 8 ? 8 : 16;              // activation rows staged
+  constexpr int R = 4;                             // ring slots; chunks in flight: R - 1
+  constexpr int WOFF = MA * 1024;                  // weight codes after the activations
+  constexpr int SLOT = WOFF + 32 * 256;
+  // the ring, and after the loop the partial tiles (float [8][16][16])
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[R * SLOT];
+  auto ring = [&](int p) -> uint8_t* { return smem + p * SLOT; };
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int cg = wave & 1, qd = wave >> 1;         // column group, quarter of the chunk's blocks
+  const int n0 = blockIdx.x * 32;
+  const int KB = K / 2, KS = K / 32;
+  const int rows_ok = __builtin_amdgcn_readfirstlane(max(0, min(32, N - n0)));
+  const __amdgpu_buffer_rsrc_t rwc = __builtin_amdgcn_make_buffer_rsrc((void*)(wc + (size_t)n0 * KB), 0, rows_ok * KB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (size_t)n0 * KS), 0, rows_ok * KS, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)x, 0, __builtin_amdgcn_readfirstlane((int)(((M - 1) * ldx + K) * 2)), 0x00020000);
+  const int nck = (K + GM_CK - 1) / GM_CK;
+  const int np = (nck + R - 1) / R * R;            // chunk slots the loop runs through (uniform)
+  const int rot = blockIdx.x % np;                 // position v holds chunk (v + rot) mod np
+  // Out-of-range parts add 2^30 to an offset, which puts the load past its
+  // buffer (every range is below 2^30 bytes) so that it returns zeros.
+  constexpr uint32_t FAR = 0x40000000u;
+
+  // Copies of chunk v into slot p.  Weights: copy `wave`, lane l -> row
+  // 4 wave + l / 16, position l % 16, holding block (l % 16) ^ (row & 15).
+  // Activations: copy m < MA (wave m & 7), lane l -> row m, position l,
+  // holding 16-byte piece l ^ m (zeros for rows m >= M).  Scale bytes of this wave's four
+  // blocks go to registers.
+  const int wrow = 4 * wave + (lane >> 4), wpos = lane & 15;
+  uint32_t sc[R];
+  auto issue = [&](int p, int v) {
+    // chunk at position v (positions past the loop's end copy zeros)
+    const int c = v >= np ? nck : (v + rot < np ? v + rot : v + rot - np);
+    const int b0 = c * (GM_CK / 32);               // first block of the chunk
+    uint8_t* slot = ring(p);
+    {
+      const int blk = b0 + (wpos ^ (wrow & 15));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rwc, (lds_ptr_t)(slot + WOFF + wave * 1024), 16,
+                                               blk < KS ? (uint32_t)(wrow * KB + blk * 16) : FAR, 0, 0, GV_NT);
+    }
+#pragma unroll
+    for (int e = 0; e < MA / 8; ++e) {             // rows m >= M copy zeros (no memory traffic)
+      const int m = wave + 8 * e;
+      const int k = c * GM_CK + 8 * (lane ^ m);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(slot + m * 1024), 16,
+                                               (m < M && k < K) ? (uint32_t)(m * ldx + k) * 2 : FAR, 0, 0, 0);
+    }
+    const int sb = b0 + 4 * qd;
+    sc[p] = __builtin_amdgcn_raw_buffer_load_b32(rws, sb < KS ? (uint32_t)((16 * cg + j) * KS + sb) : FAR, 0, GV_NT);
+  };
+  constexpr int LPC = 2 + MA / 8;                  // vector-memory ops per chunk and wave
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](int p) {
+    const uint8_t* slot = ring(p);
+    const int r = 16 * cg + j;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int b = 4 * qd + s;                    // block within the chunk
+      // (rows j >= MA repeat rows j - 8; their outputs are never stored)
+      const int ja = j & (MA - 1);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(slot + ja * 1024 + (((4 * b + g) ^ ja) << 4));
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(slot + WOFF + r * 256 + ((b ^ (r & 15)) << 4) + 4 * g);
+      const float sf = pow2f((int)((sc[p] >> (8 * s)) & 0xff) - 127);   // byte 0 gives +0.0
+      bf16x2 w2[4];
+      w2[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 0);
+      w2[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 1);
+      w2[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 2);
+      w2[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sf, 3);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, w2), acc,
+                                                    0, 0, 0);
+    }
+  };
+
+  // Position v sits in slot v % R.  After the barrier of position v every
+  // wave is done with position v - 1, whose slot then takes position v + R - 1.
+  // Chunks past the end copy zeros; the trip count is uniform.
+#pragma unroll
+  for (int p = 0; p < R - 1; ++p) issue(p, p);
+  for (int v0 = 0; v0 < nck; v0 += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      // this wave's copies of position v0 + u have landed and its reads of
+      // the previous one are done; after the barrier the same holds for all waves
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wait_vmcnt<(R - 2) * LPC>();
+      block_barrier();
+      issue((u + R - 1) % R, v0 + u + R - 1);
+      compute(u);
+    }
+  }
+  wait_vmcnt<0>();
+
+  // lane l holds rows 4g .. 4g + 3 of column j of the wave's 16 x 16 tile
+  block_barrier();                                 // every wave is done with the ring
+  float(*red)[16][16] = reinterpret_cast<float(*)[16][16]>(smem);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[wave][4 * g + q][j] = acc[q];
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int c = t >> 8, i = (t >> 4) & 15, jj = t & 15;
+  float sum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sum += red[c + 2 * q][i][jj];
+  const int n = n0 + 16 * c + jj;
+  if (i < M && n < N) y[(size_t)i * ldy + n] = (uint16_t)f32_to_bf16_rne(sum);
+}
+
 hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st) {
   if (N == 0) return hipSuccess;
@@ -315,6 +453,17 @@ hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc,
       default: return hipErrorInvalidValue;
     }
 #undef MX_GVS
+    return hipGetLastError();
+  }
+  if (M >= GV_MF_MIN_M && K % 256 == 0 && K < (1 << 25) && ((M - 1) * ldx + K) * 2 < (int64_t)0x3ffffff0) {
+    const int grid = (int)((N + 31) / 32);
+#define MX_GVM(MM) case MM: hipLaunchKernelGGL((k_gemv_mf<MM>), dim3(grid), dim3(GM_T), 0, st, (const uint16_t*)x, ldx, wc, ws, (int)N, (int)K, (uint16_t*)y, ldy); break;
+    switch ((int)M) {
+      MX_GVM(4) MX_GVM(5) MX_GVM(6) MX_GVM(7) MX_GVM(8) MX_GVM(9) MX_GVM(10) MX_GVM(11) MX_GVM(12)
+      MX_GVM(13) MX_GVM(14) MX_GVM(15) MX_GVM(16)
+      default: return hipErrorInvalidValue;
+    }
+#undef MX_GVM
     return hipGetLastError();
   }
   constexpr int RB = GV_LG_RB;

@@ -305,8 +305,8 @@ def test_grouped_dynamic_gemm(offs, xdt):
 
 
 # --------------------------------------------------------------------- GEMV
-@pytest.mark.parametrize("M", [1, 3, 8, 16])
-@pytest.mark.parametrize("NK", [(300, 4096), (64, 96), (17, 8192)])
+@pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 12, 16])
+@pytest.mark.parametrize("NK", [(300, 4096), (64, 96), (17, 8192), (40, 768)])
 def test_gemv_parity(M, NK):
     N, K = NK
     announce(f"gemv M={M} N={N} K={K}")
