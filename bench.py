@@ -447,6 +447,11 @@ def main():
                                                        "unit": "GB/s", "frac": g1["frac_hbm"],
                                                        "traffic": load_traffic("gemv_m1_8192x8192_counters.txt",
                                                                                ["gemv.hip", "mx_device.h"])}
+        g16 = sec["w4a16_gemv_8192x8192"]["M=16"]
+        sec["w4a16_gemv_8192x8192"]["roofline_M16"] = {"bound": "hbm", "achieved": g16["GB/s"], "peak": PEAK_HBM_GBS,
+                                                        "unit": "GB/s", "frac": g16["frac_hbm"],
+                                                        "traffic": load_traffic("gemv_m16_8192x8192_counters.txt",
+                                                                                ["gemv.hip", "mx_device.h"])}
         torch.cuda.empty_cache()
         log("secondary: NVFP4 quantize + GEMM")
         sec["nvfp4_2048x28672x8192"] = bench_nvfp4(args, torch, mx, W)
