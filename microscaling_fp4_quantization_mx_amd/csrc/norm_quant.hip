@@ -17,7 +17,8 @@
 //   y_k = fp32(fp32(x_k * r) * gamma_k);
 //   y is then quantized exactly as mx_quantize quantizes an fp32 tensor
 //   (MXFP4, or NVFP4 with the caller's per-tensor scale).
-// One workgroup per row; the row stays in registers between the two passes.
+// A workgroup walks rows (the next row's loads in flight); a row stays in
+// registers between the two passes; gamma is loaded once per workgroup.
 #include "mx_device.h"
 #include "mx_kernels.h"
 
@@ -32,40 +33,61 @@ __global__ __launch_bounds__(NQ_T) void k_rmsnorm_quant(const uint16_t* __restri
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                         const float* __restrict__ gscale) {
   static_assert(CH >= 1 && CH <= NQ_MAXCH, "chunks per thread");
+  constexpr int GV = G_BF16 ? 4 : 8;               // 16-byte gamma vectors per 32-element chunk
   __shared__ float wsum[NQ_T / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nch = K / 32;
   const float g = NV ? *gscale : 1.0f;
   const double six_g = 6.0 * (double)g;
+  // Loads are buffer loads whose out-of-range offsets (chunks past the row)
+  // return zeros, so none is conditional and the counted waits below are exact.
+  constexpr uint32_t FAR = 0x40000000u;
+  auto chunk_off = [&](int j) -> uint32_t {
+    const int c = tid + j * NQ_T;
+    return c < nch ? (uint32_t)c * 64 : FAR;       // 32 bf16 = 64 bytes per chunk
+  };
+  // gamma of this thread's chunks, the same for every row: loaded once
+  u32x4 gm[CH][GV];
+  {
+    const __amdgpu_buffer_rsrc_t rg =
+        __builtin_amdgcn_make_buffer_rsrc((void*)gamma, 0, K * (G_BF16 ? 2 : 4), 0x00020000);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t o = chunk_off(j) * (G_BF16 ? 1 : 2);
+#pragma unroll
+      for (int q = 0; q < GV; ++q)
+        gm[j][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, o + q * 16, 0, 0));
+    }
+  }
   // the next row's chunks are loaded while this row is reduced and quantized
   u32x4 xv[CH][4], xn[CH][4];
   auto load_row = [&](u32x4 (&dst)[CH][4], int64_t row) {
-    const uint16_t* xr = x + (size_t)row * ldx;
+    // rows past the end load zeros (an empty range)
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + (size_t)(row < rows ? row : 0) * ldx), 0, row < rows ? K * 2 : 0, 0x00020000);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = tid + j * NQ_T;
+      const uint32_t o = chunk_off(j);
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        dst[j][q] = c < nch ? *reinterpret_cast<const u32x4*>(xr + c * 32 + q * 8) : u32x4{0, 0, 0, 0};
+        dst[j][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, o + q * 16, 0, 2));
     }
   };
-  if ((int64_t)blockIdx.x < rows) load_row(xv, blockIdx.x);
+  load_row(xv, blockIdx.x);
   for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    if (row + gridDim.x < rows) load_row(xn, row + gridDim.x);
+    load_row(xn, row + gridDim.x);
+    wait_vmcnt<CH * 4>();                          // this row (and gamma) landed; the next is in flight
     float part = 0.0f;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int c = tid + j * NQ_T;
-      if (c < nch) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = bf16_lo(xv[j][q][i]), b = bf16_hi(xv[j][q][i]);
-            part = part + a * a;
-            part = part + b * b;
-          }
-      }
+        for (int i = 0; i < 4; ++i) {              // chunks past the row are zeros
+          const float a = bf16_lo(xv[j][q][i]), b = bf16_hi(xv[j][q][i]);
+          part = part + a * a;
+          part = part + b * b;
+        }
     }
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) part = fadd_xor(part, m);
@@ -81,28 +103,25 @@ __global__ __launch_bounds__(NQ_T) void k_rmsnorm_quant(const uint16_t* __restri
       float y[32];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float gm[8];
+        float gf[8];
         if (G_BF16) {
-          const u32x4 gv = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(gamma) + c * 32 + q * 8);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            gm[2 * i] = bf16_lo(gv[i]);
-            gm[2 * i + 1] = bf16_hi(gv[i]);
+            gf[2 * i] = bf16_lo(gm[j][q][i]);
+            gf[2 * i + 1] = bf16_hi(gm[j][q][i]);
           }
         } else {
-          const float* gp = reinterpret_cast<const float*>(gamma) + c * 32 + q * 8;
-          const f32x4 g0 = *reinterpret_cast<const f32x4*>(gp), g1 = *reinterpret_cast<const f32x4*>(gp + 4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            gm[i] = g0[i];
-            gm[4 + i] = g1[i];
+            gf[i] = ffrom(gm[j][2 * q][i]);
+            gf[4 + i] = ffrom(gm[j][2 * q + 1][i]);
           }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float a = bf16_lo(xv[j][q][i]) * r, b = bf16_hi(xv[j][q][i]) * r;
-          y[q * 8 + 2 * i] = a * gm[2 * i];
-          y[q * 8 + 2 * i + 1] = b * gm[2 * i + 1];
+          y[q * 8 + 2 * i] = a * gf[2 * i];
+          y[q * 8 + 2 * i + 1] = b * gf[2 * i + 1];
         }
       }
       uint8_t* crow = codes + (size_t)row * (K / 2) + c * 16;
@@ -159,7 +178,9 @@ hipError_t launch_rmsnorm_quant(const void* x, int64_t ldx, int64_t rows, int64_
                                 float eps, bool nv, uint8_t* codes, uint8_t* scales, const float* gscale,
                                 hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const int grid = (int)(rows < 256 * 8 ? rows : 256 * 8);
+  // about two resident workgroups per CU, each walking many rows with the next
+  // row in flight
+  const int grid = (int)(rows < 256 * 2 ? rows : 256 * 2);
 #define MX_RNQ3(NVB, GB, C)                                                                                        \
   hipLaunchKernelGGL((k_rmsnorm_quant<NVB, GB, C>), dim3(grid), dim3(NQ_T), 0, st, (const uint16_t*)x, ldx, rows, \
                      (int)K, gamma, eps, codes, scales, gscale)
