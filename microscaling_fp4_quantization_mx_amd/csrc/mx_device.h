@@ -97,11 +97,13 @@ __device__ __forceinline__ void nv_boundaries(double y, uint32_t U[7]) {
     U[j] = (y == 0.0) ? 0xffffffffu : (ok ? ub : ub + 1u);
   }
 }
+// The boundaries increase with j, so the count is found by bisection: three
+// compares instead of seven.
 __device__ __forceinline__ uint32_t nv_code(uint32_t xbits, const uint32_t U[7]) {
-  uint32_t a = xbits & 0x7fffffffu;
-  uint32_t c = 0;
-#pragma unroll
-  for (int j = 0; j < 7; ++j) c += (a >= U[j]) ? 1u : 0u;
+  const uint32_t a = xbits & 0x7fffffffu;
+  uint32_t c = a >= U[3] ? 4u : 0u;
+  c += a >= (c ? U[5] : U[1]) ? 2u : 0u;
+  c += a >= ((c & 4u) ? ((c & 2u) ? U[6] : U[4]) : ((c & 2u) ? U[2] : U[0])) ? 1u : 0u;
   return c | ((xbits >> 31) << 3);
 }
 
