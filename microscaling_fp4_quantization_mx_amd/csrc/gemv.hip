@@ -29,7 +29,7 @@ constexpr int GV_NT = 2;
 
 constexpr int GV_T = 256;              // 4 waves
 constexpr int GV_WIN = 64 * 32;        // K elements per window (64 lanes x 1 block)
-constexpr int GV_SK_RB = 4;            // weight rows per workgroup of the small-M kernel
+constexpr int GV_SK_RB = 16;           // weight rows per workgroup of the small-M kernel
 
 // Sum each of V values (V a power of two, at most 64) over the 64 lanes of a
 // wave with V - 1 + (6 - log2 V) * 1 exchanges instead of 6 V: at each of
@@ -66,9 +66,11 @@ __device__ __forceinline__ float wave_transpose_sum(float (&v)[V], int lane, int
 }
 
 // Small M (memory-bound): split-K inside the workgroup.  A workgroup owns RB
-// weight rows; its four waves take the 2048-element windows of K in turn
-// (wave w: windows w, w+4, ...), so each wave streams RB x 1 KiB of codes per
-// window while reading only its own 4 KiB slice of each activation row.  The
+// weight rows (16: every workgroup reads the whole activation row, so fewer,
+// larger workgroups read it fewer times); its four waves take the
+// 2048-element windows of K in turn (wave w: windows w, w+4, ...), so each
+// wave streams RB x 1 KiB of codes per window while reading only its own
+// 4 KiB slice of each activation row.  The
 // loads of a window go out in the order they are consumed (scale bytes,
 // activations, codes) so the counted waits let arithmetic start on the first
 // row while later rows are still in flight.  The four per-wave partial sums
@@ -449,7 +451,7 @@ hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc,
     const int grid = (int)((N + RB - 1) / RB);
 #define MX_GVS(MM) case MM: hipLaunchKernelGGL((k_gemv_sk<MM, RB>), dim3(grid), dim3(GV_T), 0, st, (const uint16_t*)x, ldx, wc, ws, (int)N, (int)K, (uint16_t*)y, ldy); break;
     switch ((int)M) {
-      MX_GVS(1) MX_GVS(2) MX_GVS(3) MX_GVS(4)
+      MX_GVS(1)
       default: return hipErrorInvalidValue;
     }
 #undef MX_GVS
