@@ -216,6 +216,7 @@ def mx_dequantize(t: MXTensor, dtype=None, out=None):
     dtype = dtype or torch.float32
     if out is None:
         out = torch.empty(t.rows, t.cols, dtype=dtype, device=t.codes.device)
+    assert out.dim() == 2 and out.stride(1) == 1, "rows of out must be contiguous"
     d = t.desc()
     _check(lib().mx_dequantize(ctypes.byref(d), out.data_ptr(), _dt(out), out.stride(0),
                                _stream(torch, out.device)), "mx_dequantize")
@@ -257,6 +258,7 @@ def mx_gemm(a, b: MXTensor, N: int | None = None, out_dtype=None, out=None, grou
     args.groups = groups
     args.b = ctypes.pointer(bd)
     args.group_offsets = offsets.data_ptr() if offsets is not None else None
+    assert out.dim() == 2 and out.stride(1) == 1, "rows of out must be contiguous"
     args.c = out.data_ptr()
     args.c_dtype = _dt(out)
     args.ldc = out.stride(0)
@@ -276,6 +278,7 @@ def mx_gemv(x, w: MXTensor, out=None):
     M, K = x.shape
     if out is None:
         out = torch.empty(M, w.rows, dtype=torch.bfloat16, device=x.device)
+    assert x.dim() == 2 and x.stride(1) == 1 and out.stride(1) == 1, "rows of x and out must be contiguous"
     d = w.desc()
     _check(lib().mx_gemv(x.data_ptr(), _dt(x), M, x.stride(0), ctypes.byref(d), out.data_ptr(), _dt(out),
                          out.stride(0), _stream(torch, x.device)), "mx_gemv")
@@ -327,6 +330,7 @@ def mx_moe_combine(y, dest_row, weights, tokens: int, topk: int, out=None, out_d
     N = y.shape[1]
     if out is None:
         out = torch.empty(tokens, N, dtype=out_dtype, device=y.device)
+    assert y.stride(1) == 1 and out.stride(1) == 1, "rows of y and out must be contiguous"
     _check(lib().mx_moe_combine(y.data_ptr(), _dt(y), y.stride(0), y.shape[0], dest_row.data_ptr(),
                                 weights.data_ptr(), tokens, topk, N, out.data_ptr(), _dt(out), out.stride(0),
                                 _stream(torch, y.device)), "mx_moe_combine")

@@ -322,6 +322,28 @@ def test_gemv_parity(M, NK):
     assert_within(y, yref, O.gemm_tolerance(x, wh, yref, out="bf16"), f"gemv M={M} N={N} K={K}")
 
 
+@pytest.mark.parametrize("M", [1, 3, 8, 16])
+def test_gemv_strided_rows(M):
+    """Activations and outputs as column slices of wider tensors (row pitch > K / N)."""
+    N, K = 96, 2048
+    announce(f"gemv strided M={M} N={N} K={K}")
+    rng = np.random.default_rng(77 + M)
+    x = bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    w = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    wq = mx_quant_gpu(w, torch.float32)
+    rc, rs = O.mxfp4_quantize(w)
+    xw = torch.zeros(M, K + 256, dtype=torch.bfloat16, device="cuda")
+    xw[:, :K] = dev(x, torch.bfloat16)
+    xw[:, K:] = float("nan")                      # never read
+    yw = torch.full((M, N + 64), -1.0, dtype=torch.bfloat16, device="cuda")
+    mx.mx_gemv(xw[:, :K], wq, out=yw[:, :N])
+    got = host(yw.float())
+    yref = O.gemv(x, rc, rs)
+    wh = O.dequantize("mxfp4", rc, rs)
+    assert_within(got[:, :N], yref, O.gemm_tolerance(x, wh, yref, out="bf16"), f"gemv strided M={M}")
+    assert np.all(got[:, N:] == -1.0), "columns past N were written"
+
+
 # ------------------------------------------------- full-size workloads (sampled)
 def _sample(n, k, seed):
     return np.sort(np.random.default_rng(seed).choice(n, size=min(n, k), replace=False))
