@@ -178,13 +178,17 @@ __device__ __forceinline__ float nv_global_from_partials(const uint32_t* __restr
   return r == 0 ? 1.0f : ffrom(r) / 2688.0f;
 }
 
+// One lane per 16-element block (QB blocks in flight per lane): the block's
+// scale and its seven decision boundaries (fp64 work) are computed once per
+// block rather than once per 16-byte vector, and no lane exchange is needed.
 template <typename TIn, bool CONTIG>
-__global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr,
-                                                 uint32_t nvec, uint8_t* __restrict__ codes,
+__global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int64_t ldx, uint32_t bpr,
+                                                 uint32_t nblk, uint8_t* __restrict__ codes,
                                                  uint8_t* __restrict__ scales, float* __restrict__ gout,
                                                  const uint32_t* __restrict__ partial, int npart) {
-  constexpr int EPL = 16 / (int)sizeof(TIn);
-  constexpr int LPB = 16 / EPL;  // lanes per 16-element block (4 or 2)
+  constexpr int EPL = 16 / (int)sizeof(TIn);   // elements per 16-byte vector
+  constexpr int VPB = 16 / EPL;                // vectors per block (4 or 2)
+  constexpr int QB = 2;                        // blocks per lane per iteration
   __shared__ uint32_t red[QT / 64];
   float g;
   if (partial) {
@@ -197,54 +201,56 @@ __global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int6
   const int lane = threadIdx.x & 63;
   const uint32_t wave_global = (blockIdx.x * QT + threadIdx.x) >> 6;
   const uint32_t nwaves = (gridDim.x * QT) >> 6;
-  for (uint32_t base = wave_global * (64 * QU); base < nvec; base += nwaves * (64 * QU)) {
-    u32x4 d[QU];
+  for (uint32_t base = wave_global * (64 * QB); base < nblk; base += nwaves * (64 * QB)) {
+    u32x4 d[QB][VPB];
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-      uint32_t v = base + u * 64 + lane;
+    for (int u = 0; u < QB; ++u) {
+      const uint32_t b = base + u * 64 + lane;
       const TIn* p;
       if (CONTIG) {
-        p = x + (size_t)v * EPL;
+        p = x + (size_t)b * 16;
       } else {
-        uint32_t r = v / vpr, c = v - r * vpr;
-        p = x + (size_t)r * ldx + (size_t)c * EPL;
+        const uint32_t r = b / bpr, c = b - r * bpr;
+        p = x + (size_t)r * ldx + (size_t)c * 16;
       }
-      d[u] = (v < nvec) ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < VPB; ++q) d[u][q] = (b < nblk) ? *reinterpret_cast<const u32x4*>(p + q * EPL) : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < QU; ++u) {
-      const uint32_t v = base + u * 64 + lane;
-      uint32_t xb[EPL];
-      if constexpr (EPL == 4) {
+    for (int u = 0; u < QB; ++u) {
+      const uint32_t b = base + u * 64 + lane;
+      uint32_t xb[16];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xb[i] = d[u][i];
-      } else {
+      for (int q = 0; q < VPB; ++q) {
+        if constexpr (EPL == 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          xb[2 * i] = d[u][i] << 16;
-          xb[2 * i + 1] = d[u][i] & 0xffff0000u;
+          for (int i = 0; i < 4; ++i) xb[q * 4 + i] = d[u][q][i];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            xb[q * 8 + 2 * i] = d[u][q][i] << 16;
+            xb[q * 8 + 2 * i + 1] = d[u][q][i] & 0xffff0000u;
+          }
         }
       }
       uint32_t am = 0;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) am = max(am, xb[i] & 0x7fffffffu);
-#pragma unroll
-      for (int m = 1; m < LPB; m <<= 1) am = umax_xor(am, m);
+      for (int i = 0; i < 16; ++i) am = max(am, xb[i] & 0x7fffffffu);
       // s_b = E4M3 nearest to amax / (6 g); unit y = s_b * g is exact in fp64.
       const uint32_t sc = e4m3_rne_sat((double)ffrom(am) / six_g);
       const double y = (double)e4m3_to_f32(sc) * (double)g;
       uint32_t U[7];
       nv_boundaries(y, U);
-      uint32_t out = 0;
+      uint32_t lo = 0, hi = 0;
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) out |= nv_code(xb[i], U) << (4 * i);
-      if (v < nvec) {
-        if constexpr (EPL == 4) {
-          reinterpret_cast<uint16_t*>(codes)[v] = (uint16_t)out;
-        } else {
-          reinterpret_cast<uint32_t*>(codes)[v] = out;
-        }
-        if ((lane & (LPB - 1)) == 0) scales[v / LPB] = (uint8_t)sc;
+      for (int i = 0; i < 8; ++i) {
+        lo |= nv_code(xb[i], U) << (4 * i);
+        hi |= nv_code(xb[8 + i], U) << (4 * i);
+      }
+      if (b < nblk) {
+        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<u32x2_t*>(codes + (size_t)b * 8) = u32x2_t{lo, hi};
+        scales[b] = (uint8_t)sc;
       }
     }
   }
@@ -562,9 +568,10 @@ hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t row
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int grid = grid_for(nvec, QT * QU);
+  const uint32_t bpr = (uint32_t)(cols / 16), nblk = (uint32_t)(rows * cols / 16);
+  const int grid = grid_for(nblk, QT * 2);
   const uint32_t* pp = static_global ? nullptr : partial;
-#define MX_QNV(T, C) hipLaunchKernelGGL((k_quant_nv<T, C>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales, gscale, pp, npart)
+#define MX_QNV(T, C) hipLaunchKernelGGL((k_quant_nv<T, C>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, bpr, nblk, codes, scales, gscale, pp, npart)
   if (xdt_bf16) { if (contig) MX_QNV(uint16_t, true); else MX_QNV(uint16_t, false); }
   else { if (contig) MX_QNV(float, true); else MX_QNV(float, false); }
 #undef MX_QNV
