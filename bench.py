@@ -7,10 +7,11 @@ the fp32 weights W [8192, 8192] to MXFP4 + the W4A4 GEMM (bf16 out).
 value = 2*M*N*K / step time, in TFLOPS.  Inputs are resident in HBM before
 timing; two input sets (804 MB) alternate so that the 256 MB last-level cache
 cannot hold a step's inputs.  The timed steps replay HIP graphs (two steps,
-one per input set, per graph launch; checked to reproduce the eager result);
-per-kernel durations come
-from HIP events around graphs of back-to-back launches of that kernel, on
-the stream they run on.
+one per input set, per graph launch; checked to reproduce the eager result).
+The default 200 warmup steps (about 45 ms) let the clock settle under load;
+after only 5 (1 ms) the timed steps run about 8 % slower.  Per-kernel
+durations come from HIP events around graphs of back-to-back launches of
+that kernel, on the stream they run on.
 
 Secondary measurements (same JSON line, `secondary`): the W4A16 GEMV
 N=K=8192 at M = 1, 8, 16 (GB/s, weights rotated over 16 copies), the NVFP4
@@ -169,9 +170,9 @@ def bench_main(args, torch, mx, W):
 
     def alt(fn):
         return lambda: [fn(*sets[i]) for i in (0, 1)]
-    qx_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(x, out=aq)), R), 2 * R)
-    qw_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(wt, out=bq)), R), 2 * R)
-    g_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_gemm(aq, bq, out=c)), R), 2 * R)
+    qx_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(x, out=aq)), R), 2 * R, replays=20)
+    qw_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(wt, out=bq)), R), 2 * R, replays=20)
+    g_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_gemm(aq, bq, out=c)), R), 2 * R, replays=20)
     flops = 2.0 * M * N * K
     qx_bytes = M * K * 4 + M * K // 2 + M * K // 32
     qw_bytes = N * K * 4 + N * K // 2 + N * K // 32
@@ -402,8 +403,9 @@ def cpu_baseline(d):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200,
+                    help="untimed steps first; the clock needs tens of milliseconds of load to settle")
     ap.add_argument("--only-main", action="store_true", help="skip secondary measurements and the CPU baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--gemv-iters", type=int, default=200)
