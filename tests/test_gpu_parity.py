@@ -221,7 +221,10 @@ def gemm_case(M, N, K, fmt, out_dtype, seed, x_scale=1.0, w_sigma=1.0, outlier=5
     return host(y.float()), yref, tol, (a, b)
 
 
-GEMM_CASES = [(64, 256, 256), (100, 70, 96), (1, 1, 32), (300, 520, 384), (257, 513, 1056), (512, 256, 4096)]
+# K % 256 == 0 cases run the K = 256-stage kernel (and K % 512 == 0 its paired
+# scale loads); ragged M / N and N % 4 != 0 exercise its edge stores.
+GEMM_CASES = [(64, 256, 256), (100, 70, 96), (1, 1, 32), (300, 520, 384), (257, 513, 1056), (512, 256, 4096),
+              (257, 300, 512), (130, 97, 256), (300, 258, 768)]
 
 
 @pytest.mark.parametrize("mnk", GEMM_CASES)
@@ -270,10 +273,12 @@ def test_gemm_deterministic():
 
 @pytest.mark.parametrize("offs", [[0, 100, 100, 300], [0, 0, 256, 513], [0, 1, 2, 3]])
 @pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float32])
-def test_grouped_dynamic_gemm(offs, xdt):
-    G, N, K = 3, 96, 288
+@pytest.mark.parametrize("nk", [(96, 288), (200, 512)])
+def test_grouped_dynamic_gemm(offs, xdt, nk):
+    G = 3
+    N, K = nk
     T = offs[-1]
-    announce(f"grouped dynamic gemm offsets={offs} xdt={xdt}")
+    announce(f"grouped dynamic gemm offsets={offs} xdt={xdt} N={N} K={K}")
     rng = np.random.default_rng(T + N)
     x = rng.standard_normal((T, K)).astype(np.float32)
     x[:, 7] *= 40
