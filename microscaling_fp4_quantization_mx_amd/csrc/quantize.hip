@@ -549,7 +549,12 @@ hipError_t launch_quant_mx(const void* x, int xdt_bf16, int64_t ldx, int64_t row
 
 int nv_partials_count(int64_t rows, int64_t cols, int xdt_bf16) {
   const int epl = xdt_bf16 ? 8 : 4;
-  return grid_for((uint64_t)(rows * cols / epl), QT * 4);
+  // Every quantize workgroup first reduces all partials: for tensors of up to
+  // 2^23 16-byte vectors (workgroups live briefly) at most 1024 of them; larger
+  // tensors keep the full amax-pass grid.
+  const uint64_t nvec = (uint64_t)(rows * cols / epl);
+  const int n = grid_for(nvec, QT * 4);
+  return nvec <= (1ull << 23) && n > 1024 ? 1024 : n;
 }
 
 hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,

@@ -499,6 +499,8 @@ hipError_t launch_quant_naive(const void* x, int xdt_bf16, int64_t ldx, int64_t 
                               float* s, uint32_t* partial, int max_partials, hipStream_t st) {
   const int64_t groups = rows * ((cols + 7) / 8);
   int npart = var_grid(groups);
+  // every quantize workgroup first reduces all partials (see nv_partials_count)
+  if (groups <= (int64_t)1 << 22 && npart > 1024) npart = 1024;
   if (npart > max_partials) npart = max_partials;
   const int grid = var_grid(groups);
   const int64_t esz = xdt_bf16 ? 2 : 4;

@@ -153,6 +153,40 @@ def test_quantize_nvfp4_bit_exact(shape, dtype):
         assert np.array_equal(host(t.codes), rc)
 
 
+# Tensor-wide maximum at full size: the amax pass is a grid-stride loop whose
+# per-workgroup partials every quantize workgroup reduces again; the largest
+# |x| (negative) is planted at the start, a few grid strides in and in the
+# last element in turn (2050 x 4096 leaves a partial last stride).
+AMAX_POS = [0, 1_048_576 + 77, 2 * 1_048_576 + 123, 3 * 1_048_576 + 9, 5 * 1_048_576 + 1000, 2050 * 4096 - 1]
+
+
+@pytest.mark.parametrize("pos", AMAX_POS)
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("fmt", ["nvfp4", "fp4_tensor"])
+def test_tensor_scale_full_size(fmt, dtype, pos):
+    announce(f"tensor scale full size {fmt} {dtype} max at {pos}")
+    rows, cols = 2050, 4096
+    rng = np.random.default_rng(pos % 1000 + 7)
+    x = rng.standard_normal((rows, cols)).astype(np.float32)
+    x.reshape(-1)[pos] = -400.0
+    if dtype == torch.bfloat16:
+        x = bf16_values(x)
+    q = mx.mx_quantize(dev(x, dtype), fmt)
+    prow = pos // cols
+    sample = sorted({0, prow, rows // 2, rows - 1})
+    got_codes = host(q.codes)[sample]
+    if fmt == "nvfp4":
+        g = O.nvfp4_global_scale(x)
+        assert host(q.global_scale)[0] == g
+        rc, rs, _ = O.nvfp4_quantize(x[sample], global_scale=g)
+        assert np.array_equal(host(q.scales)[sample], rs)
+    else:
+        # the sampled rows hold the tensor maximum, so their own scale is the tensor's
+        rc, s = O.naive_per_tensor_quantize(x[sample])
+        assert host(q.global_scale)[0] == s
+    assert np.array_equal(got_codes, rc)
+
+
 def test_quantize_nvfp4_static_global_and_zero_tensor():
     announce("quantize nvfp4 static global scale / all-zero tensor")
     rng = np.random.default_rng(5)
