@@ -295,7 +295,9 @@ __global__ __launch_bounds__(256) void k_gemm_mxw(MxwParams p) {
           uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + (size_t)row * p.ldc + col;
           if (vec_ok && col + 3 < p.N) {
             typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])};
+            // non-temporal: C is not read again here, and the L2 keeps the A/B panels
+            __builtin_nontemporal_store(u32x2{pack_bf16x2_rne(v[0], v[1]), pack_bf16x2_rne(v[2], v[3])},
+                                        reinterpret_cast<u32x2*>(dst));
           } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
@@ -304,7 +306,7 @@ __global__ __launch_bounds__(256) void k_gemm_mxw(MxwParams p) {
         } else {
           float* dst = reinterpret_cast<float*>(p.c) + (size_t)row * p.ldc + col;
           if (vec_ok && col + 3 < p.N) {
-            *reinterpret_cast<f32x4*>(dst) = v;
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst));
           } else {
 #pragma unroll
             for (int q = 0; q < 4; ++q)
