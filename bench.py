@@ -414,7 +414,7 @@ def main():
                     help="also run a plain 512 MiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); --gpus {args.gpus} is not "
+        print(f"bench.py measures one GPU only (the library has no multi-GPU path); --gpus {args.gpus} is not "
               f"supported", file=sys.stderr)
         sys.exit(2)
     import torch
