@@ -25,6 +25,32 @@
 namespace mxk {
 
 constexpr int NQ_T = 256;
+
+// The boundaries depend only on the block's E4M3 scale byte (0..126) and the
+// tensor scale g, so a workgroup evaluates them once for all 128 bytes:
+// tab[c] = nv_boundaries(e4m3_to_f32(c) * g).  A block then reads its seven
+// boundaries with two 16-byte LDS loads instead of seven fp64 evaluations;
+// the values are identical.  (In the standalone NVFP4 quantizer, bound by
+// HBM, the table costs more than it saves.)  Every thread of the workgroup
+// calls this; it ends with a barrier.
+__device__ __forceinline__ void nv_boundary_table(float g, uint32_t (*tab)[8]) {
+  for (int c = threadIdx.x; c < 128; c += blockDim.x) {
+    uint32_t U[7];
+    nv_boundaries((double)e4m3_to_f32((uint32_t)c) * (double)g, U);
+#pragma unroll
+    for (int j = 0; j < 7; ++j) tab[c][j] = U[j];
+    tab[c][7] = 0xffffffffu;
+  }
+  __syncthreads();
+}
+__device__ __forceinline__ void nv_boundaries_of(const uint32_t (*tab)[8], uint32_t sc, uint32_t U[7]) {
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const v4u a = *reinterpret_cast<const v4u*>(&tab[sc][0]);
+  const v4u b = *reinterpret_cast<const v4u*>(&tab[sc][4]);
+  U[0] = a.x; U[1] = a.y; U[2] = a.z; U[3] = a.w;
+  U[4] = b.x; U[5] = b.y; U[6] = b.z;
+}
+
 constexpr int NQ_MAXCH = 4;   // chunks of 32 per thread: K <= 256 * 32 * 4
 
 template <bool NV, bool G_BF16, int CH>
@@ -39,6 +65,8 @@ __global__ __launch_bounds__(NQ_T) void k_rmsnorm_quant(const uint16_t* __restri
   const int nch = K / 32;
   const float g = NV ? *gscale : 1.0f;
   const double six_g = 6.0 * (double)g;
+  __shared__ __attribute__((aligned(16))) uint32_t nvt[NV ? 128 : 1][8];
+  if constexpr (NV) nv_boundary_table(g, nvt);
   // Loads are buffer loads whose out-of-range offsets (chunks past the row)
   // return zeros, so none is conditional and the counted waits below are exact.
   constexpr uint32_t FAR = 0x40000000u;
@@ -153,7 +181,7 @@ __global__ __launch_bounds__(NQ_T) void k_rmsnorm_quant(const uint16_t* __restri
           for (int i = 0; i < 16; ++i) am = max(am, fbits(y[h * 16 + i]) & 0x7fffffffu);
           const uint32_t sc = e4m3_rne_sat((double)ffrom(am) / six_g);
           uint32_t U[7];
-          nv_boundaries((double)e4m3_to_f32(sc) * (double)g, U);
+          nv_boundaries_of(nvt, sc, U);
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             uint32_t o = 0;
