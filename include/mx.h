@@ -59,8 +59,9 @@
  *     returns MX_ERR_HIP.  Faults inside kernels surface at the caller's sync.
  *   - Device pointers must be 16-byte aligned; leading dimensions are in
  *     elements and must keep every row 16-byte aligned.
- *   - The library has no global state and is thread-safe; calls on one stream
- *     run in order.
+ *   - The library has no global state (except the static device scratch of
+ *     mx_quantize_noalloc) and is thread-safe; calls on one stream run in
+ *     order.
  */
 #ifndef MX_H_
 #define MX_H_
@@ -159,6 +160,24 @@ typedef struct mx_tensor {
  */
 int mx_quantize(const void *x, int32_t x_dtype, int64_t ld_x, const mx_tensor *out,
                 int32_t flags, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * mx_quantize_noalloc -- mx_quantize without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same arguments,
+ * layouts, results and errors as mx_quantize; the dynamic NVFP4 and
+ * FP4_TENSOR paths keep their per-workgroup partial maxima in a static
+ * device array of 16 KiB inside the library (one per device, held until the
+ * process ends) instead of a caller workspace, and the call allocates and
+ * frees nothing.  Every call on one device shares that device's array, so
+ * calls that overlap on one device (different streams or threads) race;
+ * calls ordered on one stream do not.  Nothing in the array needs clearing:
+ * every call writes each partial it reads.  A call whose scratch need
+ * exceeds the array (never, for the sizes mx_quantize accepts) returns
+ * MX_ERR_WORKSPACE.
+ */
+int mx_quantize_noalloc(const void *x, int32_t x_dtype, int64_t ld_x, const mx_tensor *out, int32_t flags,
+                        void *stream);
 
 /*
  * mx_dequantize -- x_hat = q * S_block * S_global ("NVFP4 Architecture",

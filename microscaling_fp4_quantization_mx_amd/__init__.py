@@ -20,7 +20,7 @@ __all__ = [
     "mx_status_string", "mx_version", "MX_OP_MOE_ROUTE", "mx_moe_route", "mx_quantize_rows", "mx_moe_combine",
     "moe_forward", "mx_rmsnorm_quantize", "MX_FMT_MXFP8_E4M3", "MX_FMT_MXFP8_E5M2", "MX_FMT_MXFP6_E2M3",
     "MX_FMT_MXFP6_E3M2", "element_bits", "MX_FMT_MXFP4_K16", "MX_FMT_FP4_TENSOR", "MX_QUANT_SCALE_FLOOR",
-    "padded_cols",
+    "padded_cols", "mx_quantize_noalloc",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -91,6 +91,8 @@ def lib() -> ctypes.CDLL:
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         L.mx_quantize.argtypes = [vp, i32, i64, ctypes.POINTER(CMxTensor), i32, vp, sz, vp]
         L.mx_quantize.restype = ctypes.c_int
+        L.mx_quantize_noalloc.argtypes = [vp, i32, i64, ctypes.POINTER(CMxTensor), i32, vp]
+        L.mx_quantize_noalloc.restype = ctypes.c_int
         L.mx_dequantize.argtypes = [ctypes.POINTER(CMxTensor), vp, i32, i64, vp]
         L.mx_dequantize.restype = ctypes.c_int
         L.mx_gemm.argtypes = [ctypes.POINTER(CMxGemmArgs), vp]
@@ -208,6 +210,27 @@ def mx_quantize(x, fmt="mxfp4", out: MXTensor | None = None, static_global=None,
     ws_bytes = workspace.numel() if workspace is not None else 0
     _check(lib().mx_quantize(x.data_ptr(), _dt(x), x.stride(0), ctypes.byref(d), flags, ws_ptr, ws_bytes,
                              _stream(torch, x.device)), "mx_quantize")
+    return out
+
+
+def mx_quantize_noalloc(x, out: MXTensor, static_global=None, rule: str = "ceil") -> MXTensor:
+    """mx_quantize into a preallocated `out` without a workspace: the library
+    keeps the tensor-wide max partials in its static per-device scratch, so
+    the call allocates nothing (calls overlapping on one device race)."""
+    import torch
+    assert x.dim() == 2 and x.stride(1) == 1
+    flags = MX_QUANT_DEFAULT
+    if static_global is not None:
+        out.global_scale.fill_(float(static_global))
+        if out.fmt == MX_FMT_NVFP4:
+            flags = MX_QUANT_STATIC_GLOBAL
+    if rule == "floor":
+        flags = MX_QUANT_SCALE_FLOOR
+    elif rule != "ceil":
+        raise ValueError(rule)
+    d = out.desc()
+    _check(lib().mx_quantize_noalloc(x.data_ptr(), _dt(x), x.stride(0), ctypes.byref(d), flags,
+                                     _stream(torch, x.device)), "mx_quantize_noalloc")
     return out
 
 

@@ -110,8 +110,10 @@ size_t mx_workspace_bytes(int32_t op, const void* desc, int32_t flags) {
   return 0;
 }
 
-int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* out, int32_t flags, void* workspace,
-                size_t workspace_bytes, void* stream) {
+// mx_quantize with the workspace given explicitly (a caller's buffer, or the
+// static scratch of mx_quantize_noalloc).  launch == false: validate only.
+static int quantize_impl(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* out, int32_t flags,
+                         void* workspace, size_t workspace_bytes, void* stream, bool launch = true) {
   int st = check_tensor(out);
   if (st) return st;
   if (flags != MX_QUANT_DEFAULT && flags != MX_QUANT_STATIC_GLOBAL && flags != MX_QUANT_SCALE_FLOOR)
@@ -129,7 +131,7 @@ int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* o
   if (st) return st;
   if ((dyn_nv || naive) && (!workspace || workspace_bytes < kNvPartialBytes || !al16(workspace)))
     return MX_ERR_WORKSPACE;
-  if (out->rows == 0 || out->cols == 0) return MX_OK;
+  if (out->rows == 0 || out->cols == 0 || !launch) return MX_OK;
   const int bf = x_dtype == MX_DT_BF16;
   hipError_t e;
   if (naive) {
@@ -150,6 +152,31 @@ int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* o
                              static_cast<uint32_t*>(workspace), as_stream(stream));
   }
   return hip_status(e);
+}
+
+int mx_quantize(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* out, int32_t flags, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  return quantize_impl(x, x_dtype, ld_x, out, flags, workspace, workspace_bytes, stream);
+}
+
+// The same work with the amax partials in the library's static per-device
+// scratch array instead of a caller workspace; calls that overlap on one
+// device share that array.
+int mx_quantize_noalloc(const void* x, int32_t x_dtype, int64_t ld_x, const mx_tensor* out, int32_t flags,
+                        void* stream) {
+  int st = check_tensor(out);
+  if (st) return st;
+  const size_t need = mx_workspace_bytes(MX_OP_QUANTIZE, out, flags);
+  if (need == 0) return quantize_impl(x, x_dtype, ld_x, out, flags, nullptr, 0, stream);
+  if (need > mxk::kNoallocScratchBytes) return MX_ERR_WORKSPACE;   // beyond the static scratch
+  // every argument is checked before the first HIP call (an aligned stand-in
+  // for the scratch, never dereferenced while only validating)
+  st = quantize_impl(x, x_dtype, ld_x, out, flags, reinterpret_cast<void*>(uintptr_t(256)), mxk::kNoallocScratchBytes,
+                     stream, false);
+  if (st || out->rows == 0 || out->cols == 0) return st;
+  void* scratch = nullptr;
+  if (mxk::noalloc_scratch(&scratch) != hipSuccess || !scratch) return MX_ERR_HIP;
+  return quantize_impl(x, x_dtype, ld_x, out, flags, scratch, mxk::kNoallocScratchBytes, stream);
 }
 
 int mx_dequantize(const mx_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, void* stream) {

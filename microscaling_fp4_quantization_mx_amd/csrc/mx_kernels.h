@@ -4,6 +4,11 @@
 #include <stdint.h>
 
 namespace mxk {
+// Static per-device scratch of the allocation-free entry points (noalloc.hip):
+// *ptr receives the current device's address of the array (looked up once per
+// device); it holds kNoallocScratchBytes bytes.
+constexpr size_t kNoallocScratchBytes = 16384;
+hipError_t noalloc_scratch(void** ptr);
 // gidx != nullptr: output row r quantizes input row gidx[r] (zero row if the
 // index is outside [0, x_rows)).
 hipError_t launch_quant_mx(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,

@@ -297,3 +297,21 @@ def test_wide_format_validation():
     t = T(fmt=4, rows=16, cols=256)
     assert L.mx_rmsnorm_quantize(FAKE, 1, 256, FAKE, 0, ctypes.c_float(1e-6), ctypes.byref(t), 0, None) == -5
     assert L.mx_quantize_rows(FAKE, 0, 256, 10, FAKE, ctypes.byref(t), None) == -5
+
+
+def test_quantize_noalloc_validation():
+    """The allocation-free quantize checks every argument before its first HIP
+    call (the scratch lookup), with mx_quantize's status codes."""
+    L = mx.lib()
+
+    def qn(x=FAKE, dt=0, ld=256, t=None, flags=0):
+        t = t or T()
+        return L.mx_quantize_noalloc(x, dt, ld, ctypes.byref(t), flags, None)
+    assert L.mx_quantize_noalloc(FAKE, 0, 256, None, 0, None) == -1
+    assert qn(t=T(fmt=1, g=FAKE), x=None) == -1                             # NVFP4: NULL input
+    assert qn(t=T(fmt=1, cols=40, g=FAKE)) == -5                            # cols % 16 != 0
+    assert qn(t=T(fmt=1, g=FAKE), x=FAKE + 4) == -3                         # misaligned input
+    assert qn(t=T(fmt=1, g=FAKE), dt=7) == -4
+    assert qn(t=T(fmt=7, scales=None, g=FAKE), ld=100) == -2                # naive: ld < cols
+    assert qn(t=T(fmt=1, g=FAKE, rows=0)) == 0                              # empty: no-op, no HIP call
+    assert qn(flags=1) == -5                                                # static scale: NVFP4 only
