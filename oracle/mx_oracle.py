@@ -23,7 +23,7 @@ __all__ = [
     "mx_block_exponent", "mxfp4_quantize", "nvfp4_global_scale",
     "nvfp4_quantize", "pack_codes", "unpack_codes", "dequantize",
     "round_to_bf16", "gemm", "gemm_tolerance", "gemv", "grouped_gemm",
-    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward", "rmsnorm_values", "rmsnorm_quantize", "MX_ELEMENT_FORMATS", "element_bits", "element_positive_values", "element_nearest_code", "mx_block_exponent_fmt", "pack_elements", "unpack_elements", "mx_quantize_fmt", "dequantize_fmt", "mx_quantize_variant", "dequantize_variant", "naive_per_tensor_quantize", "dequantize_naive", "reconstruction_snr_db",
+    "naive_per_tensor_fp4", "storage_bytes", "moe_route", "moe_combine", "moe_forward", "rmsnorm_values", "rmsnorm_quantize", "rmsnorm_fragile", "MX_ELEMENT_FORMATS", "element_bits", "element_positive_values", "element_nearest_code", "mx_block_exponent_fmt", "pack_elements", "unpack_elements", "mx_quantize_fmt", "dequantize_fmt", "mx_quantize_variant", "dequantize_variant", "naive_per_tensor_quantize", "dequantize_naive", "reconstruction_snr_db",
 ]
 
 # Table "The Complete Discrete State Mapping of E2M1" ("NVFP4 Architecture",
@@ -672,51 +672,56 @@ def moe_forward(x: np.ndarray, topk_ids: np.ndarray, topk_w: np.ndarray, w_packe
 
 
 def rmsnorm_values(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
-    """RMSNorm of bf16-valued rows, in the fixed fp32 order this library
-    defines so that the quantized result is reproducible (RMSNorm appears on
-    the pages only as an operation of an MXFP4 serving stack, "MXFP4" card,
-    section "Core Facts"; its order of summation is therefore a reading):
-      s = sum of x_k^2 in fp32: partial p_t over the 32-element chunks
-          t, t+256, t+512, ... in element order (t = 0..255), then a
-          pairwise tree over t within groups of 64, then (g0+g1)+(g2+g3);
-      r = fp32(1 / sqrt(s / K + eps)) computed in fp64;
-      y = fp32(fp32(x * r) * gamma)."""
-    x = np.asarray(x, np.float32)
-    gamma = np.asarray(gamma, np.float32)
-    R, K = x.shape
-    nch = K // 32
-    # part[:, t] accumulates, in order, the squares of chunks t, t+256, ...
-    part = np.zeros((R, 256), np.float32)
-    for j in range((nch + 255) // 256):
-        for e in range(32):
-            t = np.arange(256)
-            c = t + 256 * j
-            ok = c < nch
-            sq = np.zeros((R, 256), np.float32)
-            sq[:, ok] = x[:, c[ok] * 32 + e] * x[:, c[ok] * 32 + e]
-            part = (part + sq).astype(np.float32)
-    groups = []
-    for w in range(4):
-        q = part[:, 64 * w:64 * (w + 1)]
-        while q.shape[1] > 1:
-            q = (q[:, 0::2] + q[:, 1::2]).astype(np.float32)
-        groups.append(q[:, 0])
-    s = ((groups[0] + groups[1]).astype(np.float32) + (groups[2] + groups[3]).astype(np.float32)).astype(np.float32)
-    y = np.empty_like(x)
-    for i in range(R):
-        r = np.float32(1.0 / math.sqrt(float(s[i]) / K + float(eps)))
-        y[i] = ((x[i] * r).astype(np.float32) * gamma).astype(np.float32)
-    return y
+    """RMSNorm by its definition, in fp64: y = x / sqrt(mean(x^2) + eps) * gamma
+    per row (RMSNorm appears on the pages only as an operation of an MXFP4
+    serving stack, "MXFP4" card, section "Core Facts").  x and gamma are the
+    fp32 values given (bf16 activations are exact in fp32), eps the value as
+    passed (an fp32 number).  Returns float64 [R, K]: a kernel computing in
+    fp32 lands within its own rounding error of these values."""
+    x = np.asarray(x, np.float64)
+    gamma = np.asarray(gamma, np.float64)
+    ms = np.mean(x * x, axis=1, keepdims=True)
+    return x / np.sqrt(ms + float(eps)) * gamma
 
 
 def rmsnorm_quantize(x: np.ndarray, gamma: np.ndarray, eps: float, fmt: str = "mxfp4", global_scale=None):
-    """RMSNorm (rmsnorm_values) followed by block quantization of its fp32
-    output: MXFP4, or NVFP4 with a given static per-tensor scale."""
-    y = rmsnorm_values(x, gamma, eps)
+    """Block quantization of the RMSNorm output (rmsnorm_values rounded to
+    the nearest fp32): MXFP4, or NVFP4 with a given static per-tensor scale.
+    Where an fp64 value lies within a kernel's fp32 error of a decision
+    boundary the kernel's code may legitimately differ; the comparison
+    excludes exactly those decisions (see rmsnorm_fragile)."""
+    y = rmsnorm_values(x, gamma, eps).astype(np.float32)
     if fmt == "mxfp4":
         return mxfp4_quantize(y)
     c, s, _ = nvfp4_quantize(y, global_scale=global_scale)
     return c, s
+
+
+def rmsnorm_fragile(y64: np.ndarray, rel: float, fmt: str = "mxfp4", global_scale=None):
+    """Decisions of the quantization of y64 that a relative perturbation of at
+    most `rel` of every value can change: (block mask [R, K/k], element mask
+    [R, K]).  A block is fragile when its scale byte differs between
+    max|y|(1 - rel) and max|y|(1 + rel); an element when its state differs
+    between |y|(1 - rel) and |y|(1 + rel) at the block's scale."""
+    y64 = np.asarray(y64, np.float64)
+    R, K = y64.shape
+    k = MX_BLOCK if fmt == "mxfp4" else NV_BLOCK
+    mag = np.abs(y64).reshape(R, K // k, k)
+    m = mag.max(axis=-1)
+    lo, hi = 1.0 - rel, 1.0 + rel
+    if fmt == "mxfp4":
+        e_lo, e_hi = mx_block_exponent(m * lo), mx_block_exponent(m * hi)
+        block = e_lo != e_hi
+        unit = np.exp2(mx_block_exponent(m).astype(np.float64))
+    else:
+        g64 = float(np.float32(global_scale))
+        den = np.full(m.shape, 6.0 * g64)
+        s_lo, s_hi = e4m3_nearest_code(m * lo, den), e4m3_nearest_code(m * hi, den)
+        block = s_lo != s_hi
+        unit = _E4M3_POS[e4m3_nearest_code(m, den).astype(np.int64)] * g64
+    u = np.broadcast_to(unit[..., None], mag.shape)
+    elem = nearest_state_index(mag * lo, u) != nearest_state_index(mag * hi, u)
+    return block, elem.reshape(R, K)
 
 
 def naive_per_tensor_fp4(x: np.ndarray) -> np.ndarray:

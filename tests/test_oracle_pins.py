@@ -5,6 +5,7 @@ pages print (tests/golden/, each file cites its page and table/figure),
 brute force in exact rational arithmetic, closed forms, invariants and
 library routines (torch's float8_e4m3fn / bfloat16 casts, numpy int64 matmul).
 """
+import math
 import os
 from fractions import Fraction
 
@@ -326,56 +327,51 @@ def test_mx_every_block_max_round_trip():
             assert np.array_equal(O.dequantize("mxfp4", c, s), blk)
 
 
-# ------------------------------------------- P8: the pages' emulation and demo
-def page_emulation_quantize(t: torch.Tensor, block_size: int) -> torch.Tensor:
-    """The pages' PyTorch emulation ("End-to-End Implementation"), written
-    from its description: pad, view as blocks, block max, clamp at 1e-8,
-    S = 2^ceil(log2(max / 6)) in fp32, divide, nearest of the 8 states by
-    argmin (lowest index on ties) times sign; returns the dequantized tensor."""
-    states = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
-    flat = t.flatten()
-    pad = (-flat.numel()) % block_size
-    flat = torch.cat([flat, torch.zeros(pad)])
-    blocks = flat.view(-1, block_size)
-    mx = blocks.abs().max(dim=-1, keepdim=True).values.clamp(min=1e-8)
-    scale = torch.pow(2.0, torch.ceil(torch.log2(mx / 6.0)))
-    v = blocks / scale
-    idx = torch.argmin((v.abs().unsqueeze(-1) - states).abs(), dim=-1)
-    q = torch.sign(v) * states[idx]
-    out = (q * scale).flatten()
-    return out[: t.numel()].view(t.shape)
+# --------------------------------- P8: the pages' scale equation and their demo
+def equation_block_exponent(m: float) -> int:
+    """Exponent of S_block = 2^ceil(log2(max / (6 S_global))) ("NVFP4
+    Architecture", section "1. The Dual-Level Mathematical Formulation"), with
+    S_global = 1 and the maximum first raised to 1e-8 as the emulation of
+    section "End-to-End Implementation" does, evaluated in double precision
+    (for an fp32 maximum, max / 6 in double is exact or rounds far from a
+    power of two, so the ceiling is the exact one)."""
+    return math.ceil(math.log2(max(m, float(np.float32(1e-8))) / 6.0))
 
 
 @pytest.mark.parametrize("block", [32, 16])
-def test_agrees_with_page_emulation_on_gaussian_fp32(block):
-    g = torch.Generator().manual_seed(3)
-    x = torch.randn(64, 512, generator=g) * 0.7
+def test_scale_equation_and_nearest_state_on_gaussian_fp32(block):
+    """Gaussian fp32 blocks (one outlier column x40): every scale byte is the
+    printed scale equation's exponent + 127 and every code the brute-force
+    nearest state of x / S_block (exact rationals, sign copied)."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((24, 512)) * 0.7).astype(np.float32)
     x[:, 5] *= 40
-    emu = page_emulation_quantize(x, block).numpy()
-    c, s = O.mxfp4_quantize(x.numpy(), block=block)
-    ora = O.dequantize("mxfp4", c, s)
-    assert np.array_equal(np.abs(emu), np.abs(ora))
-    nz = emu != 0
-    assert np.array_equal(np.sign(emu[nz]), np.sign(ora[nz]))
+    c, s = O.mxfp4_quantize(x, block=block)
+    codes = O.unpack_codes(c)
+    for r in range(x.shape[0]):
+        for b in range(x.shape[1] // block):
+            blk = x[r, b * block:(b + 1) * block]
+            e = equation_block_exponent(float(np.abs(blk).max()))
+            assert int(s[r, b]) == e + 127
+            for j, v in enumerate(blk):
+                q = bf_nearest_e2m1(abs(Fraction(float(v))) / Fraction(2) ** e)
+                assert codes[r, b * block + j] == q | (8 if np.signbit(v) else 0)
 
 
 def test_page_demo_block_beats_naive():
-    """The emulation's demo input (seed 42, 1024 x N(0, 0.5^2), outliers 24.5 at
-    42 and -31.2 at 512, blocks of 16): the block-scaled reconstruction has a
-    higher SNR than the naive per-tensor one (the page prints no numbers)."""
-    torch.manual_seed(42)
-    x = torch.randn(1024) * 0.5
-    x[42] = 24.5
-    x[512] = -31.2
-    xn = x.numpy().reshape(1, -1)
+    """The emulation demo's setting ("End-to-End Implementation"): 1024 values
+    ~N(0, 0.5^2) with two outliers of about 25 and -31 planted, blocks of 16
+    with power-of-two scales against one per-tensor scale.  The page prints no
+    numbers, only that the block form reconstructs better; here the SNR gap
+    is larger than 10 dB, and there is one scale per 16 elements."""
+    rng = np.random.default_rng(2024)
+    x = (rng.standard_normal(1024) * 0.5).astype(np.float32)
+    x[100], x[700] = np.float32(24.5), np.float32(-31.2)
+    xn = x.reshape(1, -1)
     c, s = O.mxfp4_quantize(xn, block=16)
-    rec = O.dequantize("mxfp4", c, s)[0].astype(np.float64)
-    naive = O.naive_per_tensor_fp4(xn[0])
-    x64 = xn[0].astype(np.float64)
-    snr_b = 10 * np.log10(np.sum(x64 ** 2) / np.sum((x64 - rec) ** 2))
-    snr_n = 10 * np.log10(np.sum(x64 ** 2) / np.sum((x64 - naive) ** 2))
-    assert snr_b > snr_n + 10
-    # and the block scales exist only per 16 elements: 64 of them
+    snr_block = O.reconstruction_snr_db(xn, O.dequantize("mxfp4", c, s))
+    snr_naive = O.reconstruction_snr_db(x, O.naive_per_tensor_fp4(x))
+    assert snr_block > snr_naive + 10
     assert s.shape == (1, 64)
 
 
@@ -597,29 +593,39 @@ def test_moe_forward_equals_direct_per_token_sum():
 
 
 # ------------------------------------------------------- fused RMSNorm + FP4
-def test_rmsnorm_values_close_to_fp64_definition():
-    """The fixed-order fp32 normalization against RMSNorm in fp64: the sum of
-    K squares in fp32 (at most 4*32 sequential adds then 8 tree levels) is
-    within (136) * 2^-24 relative, so y is within a few hundred fp32 ulps."""
+def test_rmsnorm_values_match_torch_rms_norm_fp64():
+    """The oracle's RMSNorm against torch.nn.functional.rms_norm (a library
+    routine) in float64."""
     rng = np.random.default_rng(41)
     for K in (32, 256, 8192 + 64, 14336):
         x = torch.from_numpy((rng.standard_normal((3, K)) * rng.uniform(0.1, 40, (3, 1))).astype(np.float32)).to(
             torch.bfloat16).float().numpy()
-        gamma = rng.uniform(0.5, 2.0, K).astype(np.float32)
+        gamma = rng.uniform(-0.5, 2.0, K).astype(np.float32)
         y = O.rmsnorm_values(x, gamma, 1e-6)
-        x64 = x.astype(np.float64)
-        y64 = x64 / np.sqrt((x64 * x64).mean(axis=1, keepdims=True) + 1e-6) * gamma
-        assert np.all(np.abs(y - y64) <= np.abs(y64) * 200 * 2.0 ** -24 + 1e-30)
+        ref = torch.nn.functional.rms_norm(torch.from_numpy(x).double(), (K,), torch.from_numpy(gamma).double(),
+                                           eps=1e-6).numpy()
+        assert np.allclose(y, ref, rtol=1e-13, atol=0)
 
 
-def test_rmsnorm_sum_order_special_cases():
-    # constant rows: every partial is exact, so s = K c^2 exactly
+def test_rmsnorm_closed_forms():
+    # a constant row c: y = c / sqrt(c^2 + eps) * gamma
     K = 512
     x = np.full((2, K), 0.75, np.float32)
     x[1] = -3.0
-    y = O.rmsnorm_values(x, np.ones(K, np.float32), 0.0)
-    assert np.all(np.abs(y - np.sign(x)) <= 2.0 ** -23)
-    # zero row: r = 1/sqrt(eps), y = 0 with x's sign; codes are signed zeros
+    gamma = np.linspace(0.5, 1.5, K).astype(np.float32)
+    y = O.rmsnorm_values(x, gamma, 0.0)
+    assert np.allclose(y, np.sign(x) * gamma.astype(np.float64), rtol=1e-15, atol=0)
+    eps = 0.25
+    y = O.rmsnorm_values(x, np.ones(K, np.float32), eps)
+    assert np.allclose(y[0], 0.75 / np.sqrt(0.75 ** 2 + eps), rtol=1e-15)
+    # with eps = 0 and gamma = 1 the mean square of every row is 1, and scaling
+    # a row does not change it
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((4, 1000)).astype(np.float32)
+    y = O.rmsnorm_values(x, np.ones(1000, np.float32), 0.0)
+    assert np.allclose((y * y).mean(axis=1), 1.0, rtol=1e-14)
+    assert np.allclose(O.rmsnorm_values(x * np.float32(64.0), np.ones(1000, np.float32), 0.0), y, rtol=1e-14)
+    # zero row: y = 0 with x's sign; codes are signed zeros, scale byte 98
     z = np.zeros((1, 64), np.float32)
     z[0, 5] = -0.0
     c, s = O.rmsnorm_quantize(z, np.ones(64, np.float32), 1e-5)
@@ -631,7 +637,7 @@ def test_rmsnorm_quantize_is_quantize_of_values():
     rng = np.random.default_rng(42)
     x = torch.from_numpy(rng.standard_normal((4, 1024)).astype(np.float32) * 5).to(torch.bfloat16).float().numpy()
     gamma = rng.uniform(-2, 2, 1024).astype(np.float32)
-    y = O.rmsnorm_values(x, gamma, 1e-6)
+    y = O.rmsnorm_values(x, gamma, 1e-6).astype(np.float32)
     c1, s1 = O.rmsnorm_quantize(x, gamma, 1e-6)
     c2, s2 = O.mxfp4_quantize(y)
     assert np.array_equal(c1, c2) and np.array_equal(s1, s2)
@@ -639,6 +645,34 @@ def test_rmsnorm_quantize_is_quantize_of_values():
     c3, s3 = O.rmsnorm_quantize(x, gamma, 1e-6, "nvfp4", global_scale=g)
     c4, s4, _ = O.nvfp4_quantize(y, global_scale=g)
     assert np.array_equal(c3, c4) and np.array_equal(s3, s4)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
+def test_rmsnorm_fragile_marks_exactly_the_decisions_a_perturbation_moves(fmt):
+    """Planted near-boundary values are flagged; perturbing every value by a
+    relative amount within the bound changes only flagged decisions."""
+    rng = np.random.default_rng(5)
+    g = np.float32(0.01) if fmt == "nvfp4" else None
+    y = rng.standard_normal((64, 256)) * 2.0
+    rel = 2.0 ** -17
+    if fmt == "mxfp4":
+        # a block maximum exactly at 6 * 2^0 and an element at a state midpoint
+        y[0, :32] = np.clip(y[0, :32], -5.9, 5.9)
+        y[0, 3] = 6.0
+        y[1, :32] = np.clip(y[1, :32], -3.9, 3.9)
+        y[1, 0], y[1, 7] = 4.0, 1.25
+    block, elem = O.rmsnorm_fragile(y, rel, fmt, g)
+    if fmt == "mxfp4":
+        assert block[0, 0] and not block[1, 0] and elem[1, 7]
+    for trial in range(4):
+        yp = (y * (1.0 + rel * rng.uniform(-1, 1, y.shape))).astype(np.float32)
+        c0, s0 = (O.mxfp4_quantize(y.astype(np.float32)) if fmt == "mxfp4"
+                  else O.nvfp4_quantize(y.astype(np.float32), global_scale=g)[:2])
+        c1, s1 = (O.mxfp4_quantize(yp) if fmt == "mxfp4" else O.nvfp4_quantize(yp, global_scale=g)[:2])
+        assert np.all((s0 == s1) | block)
+        k = 32 if fmt == "mxfp4" else 16
+        ok = ~(np.repeat(block, k, axis=1) | elem)
+        assert np.all((O.unpack_codes(c0) == O.unpack_codes(c1)) | ~ok)
 
 
 # ------------------------------------------------ MXFP8 / MXFP6 element formats
