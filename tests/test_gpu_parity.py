@@ -4,7 +4,10 @@ for bit; GEMM / GEMV outputs must lie within 1e-5 * sum_k |a||b| of the
 oracle's fp64-accumulated result (plus one bf16 ulp of the reference value
 for bf16 outputs).  Small cases cover several tiles and ragged tails; the
 full-size workloads run in the launch configuration the benchmark uses and
-are checked on sampled outputs."""
+are checked completely: every code and scale byte and every output."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -383,41 +386,94 @@ def test_gemv_strided_rows(M):
     assert np.all(got[:, N:] == -1.0), "columns past N were written"
 
 
-# ------------------------------------------------- full-size workloads (sampled)
-def _sample(n, k, seed):
-    return np.sort(np.random.default_rng(seed).choice(n, size=min(n, k), replace=False))
+# ------------------------------------------------ full-size workloads (complete)
+# Every code byte, scale byte and per-tensor scale of every operand, and every
+# output element, at the workloads' full sizes and in the launch
+# configuration the benchmark times.  The oracle runs on row chunks in a
+# thread pool (its numpy steps release the GIL); chunking changes nothing in
+# its arithmetic, which is per block.
+THREADS = min(16, os.cpu_count() or 1)
+
+
+def oracle_rows(fn, x, chunk=128, **kw):
+    """fn applied to row chunks of x in parallel, outputs concatenated by row."""
+    parts = [(r, min(r + chunk, x.shape[0])) for r in range(0, x.shape[0], chunk)]
+    with ThreadPoolExecutor(THREADS) as ex:
+        outs = list(ex.map(lambda p: fn(x[p[0]:p[1]], **kw), parts))
+    res = []
+    for i in range(len(outs[0])):
+        if np.ndim(outs[0][i]) == 0:         # a per-tensor scalar, the same in every chunk
+            assert all(o[i] == outs[0][i] for o in outs)
+            res.append(outs[0][i])
+        else:
+            res.append(np.concatenate([o[i] for o in outs]))
+    return tuple(res)
+
+
+def assert_codes(got_codes, got_scales, ref_codes, ref_scales, what):
+    for name, g, r in (("scales", got_scales, ref_scales), ("codes", got_codes, ref_codes)):
+        if not np.array_equal(g, r):
+            bad = np.argwhere(g != r)
+            raise AssertionError(f"{what} {name}: {len(bad)} bytes differ; first at {tuple(bad[0])}: "
+                                 f"gpu={g[tuple(bad[0])]} oracle={r[tuple(bad[0])]}")
+    announce(f"{what}: {ref_codes.size} code bytes and {ref_scales.size} scale bytes identical")
+
+
+def full_gemm_check(y_gpu, ah, bh, what, rows=2048):
+    """All outputs against the fp64-accumulated oracle, in row blocks."""
+    worst = 0.0
+    for r0 in range(0, ah.shape[0], rows):
+        yref = O.gemm(ah[r0:r0 + rows], bh, out="bf16")
+        tol = O.gemm_tolerance(ah[r0:r0 + rows], bh, yref, out="bf16")
+        err = np.abs(y_gpu[r0:r0 + rows].astype(np.float64) - yref.astype(np.float64))
+        bad = err > tol
+        if bad.any():
+            i = np.argwhere(bad)[0]
+            raise AssertionError(f"{what}: {bad.sum()} outputs outside tolerance; first at row {r0 + i[0]}, "
+                                 f"col {i[1]}: gpu={y_gpu[r0 + i[0], i[1]]} ref={yref[tuple(i)]} tol={tol[tuple(i)]}")
+        worst = max(worst, float((err / np.maximum(tol, 1e-300)).max()))
+    announce(f"{what}: all {y_gpu.size} outputs within tolerance, max err / tol = {worst:.3g}")
+
+
+_W8192 = {}
+
+
+def weights_8192():
+    """The 8192 x 8192 N(0, 0.02) weights shared by the GEMV and GEMM
+    workloads, with their oracle MXFP4 codes (computed once per session)."""
+    if not _W8192:
+        d = W.make(W.C2)
+        _W8192["w"] = d["w"]
+        _W8192["x"] = d["x"]
+        _W8192["codes"], _W8192["scales"] = oracle_rows(O.mxfp4_quantize, d["w"])
+    return _W8192
 
 
 def test_full_gemv_8192():
-    d = W.make(W.C2)
+    ws = weights_8192()
     announce("full W4A16 GEMV N=K=8192, M=1/8/16")
-    wq = mx_quant_gpu(d["w"], torch.float32)
-    rows = _sample(8192, 48, 1)
-    rc, rs = O.mxfp4_quantize(d["w"][rows])
-    assert np.array_equal(host(wq.codes)[rows], rc) and np.array_equal(host(wq.scales)[rows], rs)
-    wh = O.dequantize("mxfp4", rc, rs)
+    wq = mx_quant_gpu(ws["w"], torch.float32)
+    assert_codes(host(wq.codes), host(wq.scales), ws["codes"], ws["scales"], "GEMV weights 8192x8192")
+    wh = O.dequantize("mxfp4", ws["codes"], ws["scales"])
     for M in W.GEMV_M:
-        x = d["x"][:M]
-        y = host(mx.mx_gemv(dev(x, torch.bfloat16), wq).float())[:, rows]
-        yref = O.gemm(x, wh, out="bf16")
-        assert_within(y, yref, O.gemm_tolerance(x, wh, yref, out="bf16"), f"full gemv M={M}")
+        x = ws["x"][:M]
+        y = host(mx.mx_gemv(dev(x, torch.bfloat16), wq).float())
+        full_gemm_check(y, x, wh, f"full gemv M={M}")
 
 
 def test_full_mxfp4_gemm_4096x8192x8192():
     d = W.make(W.C3)
+    ws = weights_8192()
+    assert np.array_equal(d["w"], ws["w"])
     announce("full MXFP4 GEMM 4096x8192x8192")
     a = mx_quant_gpu(d["x"], torch.float32)
     b = mx_quant_gpu(d["w"], torch.float32)
-    y = mx.mx_gemm(a, b, out_dtype=torch.bfloat16)
-    rm, rn = _sample(4096, 24, 2), _sample(8192, 96, 3)
-    ra, rsa = O.mxfp4_quantize(d["x"][rm])
-    rb, rsb = O.mxfp4_quantize(d["w"][rn])
-    assert np.array_equal(host(a.codes)[rm], ra) and np.array_equal(host(a.scales)[rm], rsa)
-    assert np.array_equal(host(b.codes)[rn], rb) and np.array_equal(host(b.scales)[rn], rsb)
-    ah, bh = O.dequantize("mxfp4", ra, rsa), O.dequantize("mxfp4", rb, rsb)
-    yref = O.gemm(ah, bh, out="bf16")
-    got = host(y.float())[np.ix_(rm, rn)]
-    assert_within(got, yref, O.gemm_tolerance(ah, bh, yref, out="bf16"), "full mxfp4 gemm")
+    y = host(mx.mx_gemm(a, b, out_dtype=torch.bfloat16).float())
+    ra, rsa = oracle_rows(O.mxfp4_quantize, d["x"])
+    assert_codes(host(a.codes), host(a.scales), ra, rsa, "X 4096x8192 fp32")
+    assert_codes(host(b.codes), host(b.scales), ws["codes"], ws["scales"], "W 8192x8192 fp32")
+    full_gemm_check(y, O.dequantize("mxfp4", ra, rsa), O.dequantize("mxfp4", ws["codes"], ws["scales"]),
+                    "full mxfp4 gemm")
 
 
 def test_full_nvfp4_gemm_2048x28672x8192():
@@ -425,18 +481,14 @@ def test_full_nvfp4_gemm_2048x28672x8192():
     announce("full NVFP4 quantize + GEMM 2048x28672x8192")
     a = mx_quant_gpu(d["x"], torch.float32, fmt="nvfp4")
     b = mx_quant_gpu(d["w"], torch.float32, fmt="nvfp4")
-    y = mx.mx_gemm(a, b, out_dtype=torch.bfloat16)
+    y = host(mx.mx_gemm(a, b, out_dtype=torch.bfloat16).float())
     ga, gb = O.nvfp4_global_scale(d["x"]), O.nvfp4_global_scale(d["w"])
     assert host(a.global_scale)[0] == ga and host(b.global_scale)[0] == gb
-    rm, rn = _sample(2048, 24, 4), _sample(28672, 96, 5)
-    ra, rsa, _ = O.nvfp4_quantize(d["x"][rm], global_scale=ga)
-    rb, rsb, _ = O.nvfp4_quantize(d["w"][rn], global_scale=gb)
-    assert np.array_equal(host(a.codes)[rm], ra) and np.array_equal(host(a.scales)[rm], rsa)
-    assert np.array_equal(host(b.codes)[rn], rb) and np.array_equal(host(b.scales)[rn], rsb)
-    ah, bh = O.dequantize("nvfp4", ra, rsa, ga), O.dequantize("nvfp4", rb, rsb, gb)
-    yref = O.gemm(ah, bh, out="bf16")
-    got = host(y.float())[np.ix_(rm, rn)]
-    assert_within(got, yref, O.gemm_tolerance(ah, bh, yref, out="bf16"), "full nvfp4 gemm")
+    ra, rsa, _ = oracle_rows(O.nvfp4_quantize, d["x"], global_scale=ga)
+    rb, rsb, _ = oracle_rows(O.nvfp4_quantize, d["w"], global_scale=gb)
+    assert_codes(host(a.codes), host(a.scales), ra, rsa, "X 2048x8192 fp32 (NVFP4)")
+    assert_codes(host(b.codes), host(b.scales), rb, rsb, "W 28672x8192 fp32 (NVFP4)")
+    full_gemm_check(y, O.dequantize("nvfp4", ra, rsa, ga), O.dequantize("nvfp4", rb, rsb, gb), "full nvfp4 gemm")
 
 
 def test_full_grouped_dynamic_gemm():
@@ -451,16 +503,13 @@ def test_full_grouped_dynamic_gemm():
     y = mx.mx_gemm(dev(d["x"], torch.bfloat16), wq, N=N, out_dtype=torch.bfloat16, groups=G, offsets=offsets,
                    a_codes_out=acodes, a_scales_out=ascales)
     yh = host(y.float())
-    ach, ash = host(acodes), host(ascales)
+    ra, rsa = oracle_rows(O.mxfp4_quantize, d["x"])
+    assert_codes(host(acodes), host(ascales), ra, rsa, "tokens 8192x14336 bf16 (quantized inside the call)")
     wch, wsh = host(wq.codes), host(wq.scales)
-    rn = _sample(N, 32, 6)
+    del wq
     for g in range(G):
+        rb, rsb = oracle_rows(O.mxfp4_quantize, d["w"][g])
+        assert_codes(wch[g * N:(g + 1) * N], wsh[g * N:(g + 1) * N], rb, rsb, f"expert {g} weights 4096x14336")
         r0, r1 = int(offs[g]), int(offs[g + 1])
-        rm = r0 + _sample(r1 - r0, 4, 10 + g)
-        ra, rsa = O.mxfp4_quantize(d["x"][rm])
-        assert np.array_equal(ach[rm], ra) and np.array_equal(ash[rm], rsa)
-        rb, rsb = O.mxfp4_quantize(d["w"][g][rn])
-        assert np.array_equal(wch[g * N + rn], rb) and np.array_equal(wsh[g * N + rn], rsb)
-        ah, bh = O.dequantize("mxfp4", ra, rsa), O.dequantize("mxfp4", rb, rsb)
-        yref = O.gemm(ah, bh, out="bf16")
-        assert_within(yh[np.ix_(rm, rn)], yref, O.gemm_tolerance(ah, bh, yref, out="bf16"), f"grouped g={g}")
+        full_gemm_check(yh[r0:r1], O.dequantize("mxfp4", ra[r0:r1], rsa[r0:r1]), O.dequantize("mxfp4", rb, rsb),
+                        f"grouped expert {g} ({r1 - r0} rows)")
