@@ -244,11 +244,20 @@ int mx_gemm(const mx_gemm_args *args, void *stream);
 
 /*
  * mx_gemv -- W4A16 decode product y[M, N] = x[M, K] . W_hat[N, K]^T with bf16
- * activations and MXFP4 weights dequantized in registers (no matrix cores):
- * weights stay compressed, the arithmetic is 16-bit x dequantized weight with
+ * activations and MXFP4 weights dequantized in registers: weights stay
+ * compressed in memory, the arithmetic is 16-bit x dequantized weight with
  * fp32 accumulation ("Extreme Quantization and Precision Engineering", section
- * "Key points", W4A16).  1 <= M <= 16; x bf16 [M, K] pitch ld_x; y bf16
- * [M, N] pitch ld_y.  Requires K % 32 == 0.
+ * "Key points", W4A16).  Every weight is expanded on chip to the exact bf16
+ * value q * 2^e, so each product is exact and only the fp32 summation order
+ * varies.  Which unit takes the products:
+ *   M <= 3, or any M when K % 256 != 0: the vector ALU (v_dot2_f32_bf16);
+ *     no matrix cores;
+ *   4 <= M <= 16 with K % 256 == 0: the bf16 matrix cores
+ *     (v_mfma_f32_16x16x32_bf16, activation rows zero-padded to 16), because
+ *     one dot2 per weight pair and activation row makes the vector ALU, not
+ *     the weight stream, the bound from M = 4 on.
+ * 1 <= M <= 16; x bf16 [M, K] pitch ld_x; y bf16 [M, N] pitch ld_y.
+ * Requires K % 32 == 0.
  */
 int mx_gemv(const void *x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_tensor *w,
             void *y, int32_t y_dtype, int64_t ld_y, void *stream);
