@@ -109,6 +109,15 @@ enum {
   MX_QUANT_SCALE_FLOOR = 2
 };
 
+/* mx_gemm_args.flags */
+enum {
+  /* MX pairs with an FP8 or FP6 operand: use the block-scaled FP8/FP6/FP4
+     matrix cores (faster; products truncated, see mx_gemm) instead of the
+     exact route.  Ignored for MXFP4 x MXFP4, whose products those matrix
+     cores form exactly. */
+  MX_GEMM_F8F6F4_MATRIX_CORES = 1
+};
+
 /* mx_workspace_bytes operations */
 enum { MX_OP_QUANTIZE = 0, MX_OP_GEMM = 1, MX_OP_MOE_ROUTE = 2 };
 
@@ -212,7 +221,16 @@ int mx_dequantize(const mx_tensor *in, void *y, int32_t y_dtype, int64_t ld_y, v
  * Requires K % 32 == 0 (MXFP4) or K % 16 == 0 (NVFP4).
  * MX element pairs beyond MXFP4 x MXFP4 (A and B each MXFP4, MXFP8 E4M3/E5M2
  * or MXFP6 E2M3/E3M2, mixed pairs allowed, e.g. FP8 activations x FP4
- * weights): C = sum_b 2^(eA+eB) sum_{k in b} qA qB with fp32 accumulation;
+ * weights): C = sum_b 2^(eA+eB) sum_{k in b} qA qB with fp32 accumulation,
+ * every product exact (the codes are expanded to bf16 values q * 2^e for the
+ * bf16 matrix cores, exact while each lies in [2^-126, 2^128), as for every
+ * tensor the quantizer writes from inputs below 2^127 in magnitude; scale
+ * bytes 0 and 255, which the quantizer never writes, are taken as 1 and 254).  With flags MX_GEMM_F8F6F4_MATRIX_CORES the
+ * pair runs on the block-scaled FP8/FP6/FP4 matrix cores instead, about twice
+ * as fast, which truncate each product of a group of 8 consecutive K to 13
+ * bits below the largest product of the group (measured on gfx950): per
+ * output the error grows by at most 8 * 2^(L_g - 12) per group g, L_g the
+ * binary exponent of that largest product;
  * dense, pre-quantized A only (MX_ERR_UNSUPPORTED for grouped or dynamic
  * calls), padded K % 128 == 0 and K <= 2^22 (else MX_ERR_UNSUPPORTED).  NVFP4
  * pairs only with NVFP4 (else MX_ERR_FORMAT).  Pre-quantized MX operands
@@ -232,7 +250,7 @@ typedef struct mx_gemm_args {
   const int32_t *group_offsets;  /* device int32 [groups + 1] (grouped)     */
   void *c;                       /* device [M, N]                           */
   int32_t c_dtype;
-  int32_t reserved;              /* must be 0 */
+  int32_t flags;                 /* 0 or MX_GEMM_F8F6F4_MATRIX_CORES        */
   int64_t ldc;                   /* elements                                */
   uint8_t *a_codes_out;          /* optional [M, K/2] (dynamic path)        */
   uint8_t *a_scales_out;         /* optional [M, K/32] (dynamic path)       */

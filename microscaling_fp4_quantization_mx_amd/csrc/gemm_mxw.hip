@@ -319,9 +319,200 @@ __global__ __launch_bounds__(256) void k_gemm_mxw(MxwParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Exact route for MX pairs with an FP8 or FP6 operand.  The block-scaled MFMA
+// above truncates each product of a group of eight K values to 13 bits below
+// the group's largest product (measured), which FP4 x FP4 never reaches but
+// FP8 and FP6 operands can.  Here every code is expanded, once per workgroup
+// while staging into LDS, to the exact bf16 value q * 2^(E-127): the scaled
+// conversions v_cvt_scalef32_pk_bf16_fp8 / _bf8 / _fp4 and
+// v_cvt_scalef32_pk32_bf16_fp6 / _bf6 apply the block's power of two.  Such a
+// value has at most 4 significant bits, so it is exact in bf16 wherever it
+// lies in bf16's normal range [2^-126, 2^128); every tensor the quantizer
+// writes from inputs below 2^127 in magnitude stays there (its smallest
+// nonzero element value is 2^-58, an E5M2 subnormal at the floor scale).  The
+// bf16 matrix cores (v_mfma_f32_32x32x16_bf16) form exact products and add
+// them in fp32, so the result is the fp32-accumulated block-scaled sum.  4 waves, 256 x 256 tile,
+// 128 x 128 per wave, K = 64 per stage (two MX blocks per row), LDS rows of
+// 64 bf16 with XOR-swizzled 16-byte chunks, double buffered.
+// ---------------------------------------------------------------------------
+constexpr int MXX_BK = 64;        // K per stage
+constexpr int MXX_ROWB = 128;     // LDS bytes per bf16 row per stage
+
+__device__ __forceinline__ int mxx_swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// E8M0 byte -> the fp32 power of two the conversions scale by (bytes 0 and
+// 255, which the quantizer never writes, are taken as 1 and 254).
+__device__ __forceinline__ float mxx_scale(uint32_t e) { return ffrom(min(max(e, 1u), 254u) << 23); }
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x32_t __attribute__((ext_vector_type(32)));
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+// The 32 codes of one MX block (W dwords: 4 FP4, 6 FP6, 8 FP8) -> 16 dwords of
+// bf16 pairs, element order kept.
+template <int F>
+__device__ __forceinline__ void mxx_expand(const uint32_t* w, float sc, uint32_t (&o)[16]) {
+  if constexpr (F == 4) {                 // E2M1: 8 codes per dword
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      bf16x2 v[4];
+      v[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], sc, 0);
+      v[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], sc, 1);
+      v[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], sc, 2);
+      v[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], sc, 3);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) __builtin_memcpy(&o[4 * d + q], &v[q], 4);
+    }
+  } else if constexpr (F == 0 || F == 1) {   // E4M3 / E5M2: 4 codes per dword
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      bf16x2 lo, hi;
+      if constexpr (F == 0) {
+        lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], sc, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], sc, true);
+      } else {
+        lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[d], sc, false);
+        hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[d], sc, true);
+      }
+      __builtin_memcpy(&o[2 * d], &lo, 4);
+      __builtin_memcpy(&o[2 * d + 1], &hi, 4);
+    }
+  } else {                                    // E2M3 / E3M2: 32 codes in 6 dwords
+    const u32x6 v = {w[0], w[1], w[2], w[3], w[4], w[5]};
+    bf16x32_t r;
+    if constexpr (F == 2) r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(v, sc);
+    else r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(v, sc);
+    __builtin_memcpy(&o[0], &r, 64);
+  }
+}
+
+template <int FA, int FB>
+__global__ __launch_bounds__(256) void k_gemm_mxx(MxwParams p) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, TI = WM / 32, TJ = WN / 32;
+  constexpr int NT = 256;
+  constexpr int WA = MxwOp<FA>::BITS, WB = MxwOp<FB>::BITS;   // dwords per 32-code block = bits
+  constexpr int SEG = BM * 2 / NT;                            // block segments per thread per operand
+  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * MXX_ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * MXX_ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wy = wave >> 1, wx = wave & 1;
+  const int tn_count = (p.N + BN - 1) / BN, tm_count = (p.M + BM - 1) / BM;
+  int tm, tn;
+  {
+    const int total = tm_count * tn_count;
+    const int per_xcd = (total + 7) / 8;
+    const int local = blockIdx.x / 8;
+    if (local >= per_xcd) return;
+    const int t = (blockIdx.x % 8) * per_xcd + local;
+    if (t >= total) return;
+    const int per_group = MXW_GROUP_M * tn_count;
+    const int grp = t / per_group;
+    const int first_m = grp * MXW_GROUP_M;
+    const int gm = min(tm_count - first_m, MXW_GROUP_M);
+    const int in_grp = t % per_group;
+    tm = first_m + in_grp % gm;
+    tn = in_grp / gm;
+  }
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int KBA = p.K / 8 * WA, KBB = p.K / 8 * WB, KS = p.K / 32;   // code bytes per row = K * bits / 8
+
+  // segment q = tid + i*NT of a stage: row q >> 1, MX block q & 1 of the stage
+  uint32_t ca[SEG][WA], cb[SEG][WB], sa[SEG], sb[SEG];
+  auto load_stage = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      const int q = tid + i * NT, row = q >> 1, blk = s * 2 + (q & 1);
+      const bool oka = m0 + row < p.M && blk < KS, okb = n0 + row < p.N && blk < KS;
+      const uint32_t* pa = reinterpret_cast<const uint32_t*>(p.a_codes + (size_t)(m0 + row) * KBA + (size_t)blk * WA * 4);
+      const uint32_t* pb = reinterpret_cast<const uint32_t*>(p.b_codes + (size_t)(n0 + row) * KBB + (size_t)blk * WB * 4);
+#pragma unroll
+      for (int d = 0; d < WA; ++d) ca[i][d] = oka ? pa[d] : 0u;
+#pragma unroll
+      for (int d = 0; d < WB; ++d) cb[i][d] = okb ? pb[d] : 0u;
+      sa[i] = oka ? p.a_scales[(size_t)(m0 + row) * KS + blk] : 127u;
+      sb[i] = okb ? p.b_scales[(size_t)(n0 + row) * KS + blk] : 127u;
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < SEG; ++i) {
+      const int q = tid + i * NT, row = q >> 1, h = q & 1;
+      uint32_t o[16];
+      mxx_expand<FA>(ca[i], mxx_scale(sa[i]), o);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(&sA[buf][row * MXX_ROWB + (((4 * h + c) ^ mxx_swz(row)) << 4)]) =
+            u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+      mxx_expand<FB>(cb[i], mxx_scale(sb[i]), o);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<u32x4*>(&sB[buf][row * MXX_ROWB + (((4 * h + c) ^ mxx_swz(row)) << 4)]) =
+            u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
+    }
+  };
+
+  f32x16 acc[TI][TJ];
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  const int nstages = (p.K + MXX_BK - 1) / MXX_BK;
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+  const int lrow = lane & 31, khalf = lane >> 5;
+  for (int s = 0; s < nstages; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < nstages) load_stage(s + 1);
+#pragma unroll
+    for (int kk = 0; kk < MXX_BK / 16; ++kk) {
+      const int c = kk * 2 + khalf;  // lane holds K = 16 kk + 8 khalf + (0..7)
+      bf16x8_t fa[TI], fb[TJ];
+#pragma unroll
+      for (int i = 0; i < TI; ++i) {
+        const int row = wy * WM + i * 32 + lrow;
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(&sA[buf][row * MXX_ROWB + ((c ^ mxx_swz(row)) << 4)]);
+      }
+#pragma unroll
+      for (int j = 0; j < TJ; ++j) {
+        const int row = wx * WN + j * 32 + lrow;
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(&sB[buf][row * MXX_ROWB + ((c ^ mxx_swz(row)) << 4)]);
+      }
+#pragma unroll
+      for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    }
+    if (s + 1 < nstages) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < TI; ++i)
+#pragma unroll
+    for (int j = 0; j < TJ; ++j) {
+      const int col = n0 + wx * WN + j * 32 + lrow;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wy * WM + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row < p.M && col < p.N) {
+          if (p.c_bf16)
+            reinterpret_cast<uint16_t*>(p.c)[(size_t)row * p.ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+          else
+            reinterpret_cast<float*>(p.c)[(size_t)row * p.ldc + col] = acc[i][j][r];
+        }
+      }
+    }
+}
+
 hipError_t launch_gemm_mxw(int fa, int fb, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                            const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           hipStream_t st) {
+                           hipStream_t st, bool exact) {
   MxwParams p;
   p.a_codes = a_codes; p.a_scales = a_scales; p.b_codes = b_codes; p.b_scales = b_scales;
   p.c = c; p.ldc = ldc; p.M = (int)M; p.N = (int)N; p.K = (int)K; p.c_bf16 = c_bf16;
@@ -329,7 +520,9 @@ hipError_t launch_gemm_mxw(int fa, int fb, const uint8_t* a_codes, const uint8_t
   const int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (fa < 0 || fa > 4 || fb < 0 || fb > 4) return hipErrorInvalidValue;
-#define MXW_L(A, B) hipLaunchKernelGGL((k_gemm_mxw<A, B>), dim3((unsigned)grid), dim3(256), 0, st, p)
+#define MXW_L(A, B)                                                                     \
+  if (exact) hipLaunchKernelGGL((k_gemm_mxx<A, B>), dim3((unsigned)grid), dim3(256), 0, st, p); \
+  else hipLaunchKernelGGL((k_gemm_mxw<A, B>), dim3((unsigned)grid), dim3(256), 0, st, p)
 #define MXW_ROW(A)                \
   switch (fb) {                   \
     case 0: MXW_L(A, 0); break;   \

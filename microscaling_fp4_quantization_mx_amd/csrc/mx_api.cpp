@@ -205,7 +205,7 @@ int mx_dequantize(const mx_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, v
 
 int mx_gemm(const mx_gemm_args* a, void* stream) {
   if (!a) return MX_ERR_NULL;
-  if (a->reserved != 0) return MX_ERR_SHAPE;
+  if (a->flags & ~MX_GEMM_F8F6F4_MATRIX_CORES) return MX_ERR_SHAPE;
   if (a->M < 0 || a->N < 0 || a->K < 0 || a->M > kMaxDim || a->N > kMaxDim || a->K > kMaxDim) return MX_ERR_SHAPE;
   if (a->groups < 0) return MX_ERR_SHAPE;
   int st = check_tensor(a->b);
@@ -241,7 +241,8 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
     if (a->M == 0 || a->N == 0) return MX_OK;
     return hip_status(mxk::launch_gemm_mxw(mfma_fmt(a->a->fmt), mfma_fmt(fmt), a->a->codes, a->a->scales,
                                            a->b->codes, a->b->scales, a->c, a->c_dtype == MX_DT_BF16, a->ldc,
-                                           a->M, a->N, Kp, as_stream(stream)));
+                                           a->M, a->N, Kp, as_stream(stream),
+                                           !(a->flags & MX_GEMM_F8F6F4_MATRIX_CORES)));
   }
   if (fmt_wide(fmt)) return MX_ERR_UNSUPPORTED;   // dynamic activation quantization is MXFP4 only
   if (!dtype_ok(a->c_dtype)) return MX_ERR_DTYPE;

@@ -31,9 +31,12 @@ hipError_t launch_quant_wide(int fmt, const void* x, int xdt_bf16, int64_t ldx, 
                              uint8_t* codes, uint8_t* scales, hipStream_t st, bool floor_rule = false);
 hipError_t launch_dequant_wide(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, void* y,
                                bool out_bf16, int64_t ldy, hipStream_t st);
+// exact: codes expanded to exact bf16 values for the bf16 matrix cores;
+// otherwise the block-scaled FP8/FP6/FP4 matrix cores (faster; they truncate
+// products with FP8 or FP6 operands).
 hipError_t launch_gemm_mxw(int fa, int fb, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                            const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           hipStream_t st);
+                           hipStream_t st, bool exact);
 // Emulation variants (quantize_variant.hip): block 16 or 32, the OCP floor
 // rule, a per-tensor scale g (NULL = 1), rows of any length (zero-padded to
 // whole blocks); naive per-tensor FP4.

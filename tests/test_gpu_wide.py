@@ -1,17 +1,18 @@
 """GPU parity of the wider MX elements (MXFP8 E4M3/E5M2, MXFP6 E2M3/E3M2)
 against the CPU oracle: codes and scale bytes bit for bit, dequantized values
 exactly, and block-scaled products of every MX format pair (mixed pairs
-included) within the bound of the matrix-core arithmetic.
+included).
 
-The bound: 1e-5 * sum_k |a_k b_k| for the fp32 accumulation (+ one bf16 ulp
-for bf16 output), plus the truncation inside the block-scaled MFMA.  Measured
-with exact test values on the hardware: the products of each group of 8
-consecutive K are summed after each product is truncated toward zero at 13
-bits below the leading bit of the group's largest product (FP6 pairs keep at
-least that many).  So a product loses less than 2^(L - 13), L = floor(log2 of
-the group's largest |product|), and a group of 8 less than 8 * 2^(L + 1 - 13)
-(one bit of slack for the product's leading bit).  E2M1 x E2M1 products span
-7 bits and lose nothing."""
+Default (exact) route: within 1e-5 * sum_k |a_k b_k| (+ one bf16 ulp for bf16
+output), the same bar as the FP4 GEMM.  Route MX_GEMM_F8F6F4_MATRIX_CORES
+(block-scaled matrix cores): that bound plus the truncation those matrix
+cores apply -- the products of each group of 8 consecutive K are summed after
+each product is truncated toward zero at 13 bits below the leading bit of
+the group's largest product, so a product loses less than 2^(L - 13), L =
+floor(log2 of the group's largest |product|), and a group of 8 less than
+8 * 2^(L + 1 - 13) (one bit of slack for the product's leading bit).
+test_f8f6f4_truncation_probe pins that model with exact values.  E2M1 x E2M1
+products span 7 bits and lose nothing on either route."""
 import numpy as np
 import pytest
 import torch
@@ -123,19 +124,21 @@ def mfma_truncation_bound(ah, bh, keep=MFMA_KEEP_BITS, group=MFMA_GROUP, rows_pe
     return out
 
 
-def _gemm_case(fa, fb, M, N, K, out_dtype, seed):
+def _gemm_case(fa, fb, M, N, K, out_dtype, seed, fast=False):
     rng = np.random.default_rng(seed)
     a = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-6, 6, (M, 1)))).astype(np.float32)
     a[:, 5] *= 40.0                                           # an outlier channel
     b = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
     qa = mx.mx_quantize(torch.from_numpy(a).to(DEV), fa)
     qb = mx.mx_quantize(torch.from_numpy(b).to(DEV), fb)
-    c = mx.mx_gemm(qa, qb, out_dtype=out_dtype)
+    c = mx.mx_gemm(qa, qb, out_dtype=out_dtype, f8f6f4_matrix_cores=fast)
     ah = O.dequantize_fmt(fa, host(qa.codes), host(qa.scales))
     bh = O.dequantize_fmt(fb, host(qb.codes), host(qb.scales))
     out = "bf16" if out_dtype == torch.bfloat16 else "f32"
     ref = O.gemm(ah, bh, out=out)
-    tol = O.gemm_tolerance(ah, bh, ref, out=out) + mfma_truncation_bound(ah, bh)
+    tol = O.gemm_tolerance(ah, bh, ref, out=out)
+    if fast:
+        tol = tol + mfma_truncation_bound(ah, bh)
     got = host(c.float()).astype(np.float64)
     return got, ref.astype(np.float64), tol
 
@@ -143,38 +146,69 @@ def _gemm_case(fa, fb, M, N, K, out_dtype, seed):
 PAIRS = [(fa, fb) for fa in ALL for fb in ALL if (fa, fb) != ("mxfp4", "mxfp4")]
 
 
+@pytest.mark.parametrize("fast", [False, True])
 @pytest.mark.parametrize("fa,fb", PAIRS)
-def test_wide_gemm_pairs(fa, fb):
+def test_wide_gemm_pairs(fa, fb, fast):
     out_dtype = torch.bfloat16 if (ALL.index(fa) + ALL.index(fb)) % 2 else torch.float32
-    announce(f"wide gemm {fa} x {fb} 300x260x384 out={out_dtype}")
-    got, ref, tol = _gemm_case(fa, fb, 300, 260, 384, out_dtype, seed=ALL.index(fa) * 5 + ALL.index(fb))
+    announce(f"wide gemm {fa} x {fb} 300x260x384 out={out_dtype} f8f6f4={fast}")
+    got, ref, tol = _gemm_case(fa, fb, 300, 260, 384, out_dtype, seed=ALL.index(fa) * 5 + ALL.index(fb), fast=fast)
     bad = np.abs(got - ref) > tol
     assert not bad.any(), (np.argwhere(bad)[:5], np.abs(got - ref).max())
 
 
+@pytest.mark.parametrize("fast", [False, True])
 @pytest.mark.parametrize("M,N,K", [(1, 1, 128), (1, 257, 256), (513, 7, 128), (256, 256, 1024)])
-def test_wide_gemm_edges(M, N, K):
-    announce(f"wide gemm edges mxfp8_e4m3 x mxfp4 {M}x{N}x{K}")
-    got, ref, tol = _gemm_case("mxfp8_e4m3", "mxfp4", M, N, K, torch.float32, seed=M + N + K)
+def test_wide_gemm_edges(M, N, K, fast):
+    announce(f"wide gemm edges mxfp8_e4m3 x mxfp4 {M}x{N}x{K} f8f6f4={fast}")
+    got, ref, tol = _gemm_case("mxfp8_e4m3", "mxfp4", M, N, K, torch.float32, seed=M + N + K, fast=fast)
     assert np.all(np.abs(got - ref) <= tol), np.abs(got - ref).max()
 
 
-def test_wide_gemm_multi_tile():
-    announce("wide gemm mxfp8_e5m2 x mxfp6_e3m2 1024x768x2048")
-    got, ref, tol = _gemm_case("mxfp8_e5m2", "mxfp6_e3m2", 1024, 768, 2048, torch.bfloat16, seed=3)
+@pytest.mark.parametrize("fast", [False, True])
+def test_wide_gemm_multi_tile(fast):
+    announce(f"wide gemm mxfp8_e5m2 x mxfp6_e3m2 1024x768x2048 f8f6f4={fast}")
+    got, ref, tol = _gemm_case("mxfp8_e5m2", "mxfp6_e3m2", 1024, 768, 2048, torch.bfloat16, seed=3, fast=fast)
     assert np.all(np.abs(got - ref) <= tol), np.abs(got - ref).max()
 
 
+def test_f8f6f4_truncation_probe():
+    """Exact values that show the block-scaled matrix cores' truncation:
+    a = (448, 15/256, 0, ...) in E4M3, b = (1, 1, 0, ...): the exact product
+    448 + 15/256 comes out on the exact route; on the f8f6f4 route the second
+    product shares a group of 8 K with 448 (leading bit 2^8) and is cut to a
+    multiple of 2^(8-13): 448 + 1/32.  Moved to K = 8 (another group), the
+    small product is kept exactly by both routes."""
+    announce("f8f6f4 truncation probe")
+    K = 128
+    res = {}
+    for k_small in (1, 8):
+        a = np.zeros((1, K), np.float32)
+        a[0, 0], a[0, k_small] = 448.0, 15.0 / 256.0
+        b = np.zeros((1, K), np.float32)
+        b[0, 0], b[0, k_small] = 1.0, 1.0
+        qa = mx.mx_quantize(torch.from_numpy(a).to(DEV), "mxfp8_e4m3")
+        qb = mx.mx_quantize(torch.from_numpy(b).to(DEV), "mxfp8_e4m3")
+        assert np.array_equal(O.dequantize_fmt("mxfp8_e4m3", host(qa.codes), host(qa.scales)), a)
+        assert np.array_equal(O.dequantize_fmt("mxfp8_e4m3", host(qb.codes), host(qb.scales)), b)
+        for fast in (False, True):
+            c = mx.mx_gemm(qa, qb, out_dtype=torch.float32, f8f6f4_matrix_cores=fast)
+            res[(k_small, fast)] = float(host(c)[0, 0])
+    assert res[(1, False)] == 448.0 + 15.0 / 256.0
+    assert res[(1, True)] == 448.0 + 1.0 / 32.0
+    assert res[(8, False)] == res[(8, True)] == 448.0 + 15.0 / 256.0
+
+
+@pytest.mark.parametrize("fast", [False, True])
 @pytest.mark.parametrize("fa,fb", list(W.WIDE_PAIRS))
-def test_wide_gemm_full_size_sampled(fa, fb):
+def test_wide_gemm_full_size_sampled(fa, fb, fast):
     """The benchmark's 4096 x 8192 x 8192 products in their launch
     configuration; sampled rows and columns against the oracle."""
     w = W.WIDE
-    announce(f"wide gemm full size {fa} x {fb} {w.M}x{w.N}x{w.K}")
+    announce(f"wide gemm full size {fa} x {fb} {w.M}x{w.N}x{w.K} f8f6f4={fast}")
     d = W.make(w)
     qa = mx.mx_quantize(torch.from_numpy(d["x"]).to(torch.bfloat16).to(DEV), fa)
     qb = mx.mx_quantize(torch.from_numpy(d["w"]).to(DEV), fb)
-    c = mx.mx_gemm(qa, qb, out_dtype=torch.bfloat16)
+    c = mx.mx_gemm(qa, qb, out_dtype=torch.bfloat16, f8f6f4_matrix_cores=fast)
     rng = np.random.default_rng(17)
     rows = np.sort(rng.choice(w.M, 12, replace=False))
     cols = np.sort(rng.choice(w.N, 40, replace=False))
@@ -183,13 +217,14 @@ def test_wide_gemm_full_size_sampled(fa, fb):
     ah = O.dequantize_fmt(fa, ca, sa)
     bh = O.dequantize_fmt(fb, host(qb.codes)[cols], host(qb.scales)[cols])
     ref = O.gemm(ah, bh, out="bf16").astype(np.float64)
-    tol = O.gemm_tolerance(ah, bh, ref, out="bf16") + mfma_truncation_bound(ah, bh)
+    tol = O.gemm_tolerance(ah, bh, ref, out="bf16") + (mfma_truncation_bound(ah, bh) if fast else 0.0)
     got = host(c.float())[np.ix_(rows, cols)].astype(np.float64)
     assert np.all(np.abs(got - ref) <= tol), np.abs(got - ref).max()
 
 
+@pytest.mark.parametrize("fast", [False, True])
 @pytest.mark.parametrize("fa,fb", PAIRS)
-def test_wide_gemm_exact_structured(fa, fb):
+def test_wide_gemm_exact_structured(fa, fb, fast):
     """Integers 1..3 (signed) times a power of two per 32-element block, in
     every format exactly: products span 4 bits, so nothing is truncated, and
     every partial sum is exact in fp32 -- the result must equal the exact
@@ -208,5 +243,5 @@ def test_wide_gemm_exact_structured(fa, fb):
     qb = mx.mx_quantize(torch.from_numpy(b).to(DEV), fb)
     assert np.array_equal(O.dequantize_fmt(fa, host(qa.codes), host(qa.scales)), a)
     assert np.array_equal(O.dequantize_fmt(fb, host(qb.codes), host(qb.scales)), b)
-    c = host(mx.mx_gemm(qa, qb, out_dtype=torch.float32)).astype(np.float64)
+    c = host(mx.mx_gemm(qa, qb, out_dtype=torch.float32, f8f6f4_matrix_cores=fast)).astype(np.float64)
     assert np.array_equal(c, a.astype(np.float64) @ b.astype(np.float64).T)
