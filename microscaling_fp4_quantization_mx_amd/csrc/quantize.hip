@@ -16,6 +16,7 @@
 // scale byte.  Several vectors per lane are loaded before any is used so that
 // enough bytes are in flight to cover HBM latency.
 #include "mx_device.h"
+#include "nv_codes.h"
 #include "mx_kernels.h"
 
 namespace mxk {
@@ -163,15 +164,28 @@ __global__ __launch_bounds__(QT) void k_absmax(const TIn* __restrict__ x, int64_
 
 // Per-tensor scale from the partial maxima: g = fp32(amax / 2688), 2688 being
 // 6 (largest E2M1 state) x 448 (largest E4M3 value), or 1 for an all-zero
-// tensor; the fp32 division is IEEE correctly rounded.
-__device__ __forceinline__ float nv_global_from_partials(const uint32_t* __restrict__ partial, int npart,
-                                                         uint32_t* red) {
+// tensor; the fp32 division is IEEE correctly rounded.  The partials (a
+// multiple of 4, at most 4096) are loaded as 16-byte vectors by
+// nv_partials_load before the caller issues its data loads, so that using
+// them waits only for these (vector loads complete in order); the reduction
+// ends with a bare barrier, which leaves the data loads in flight.
+constexpr int NV_PV = 4;   // 16-byte partial vectors per thread: 4 x 4 x 256 = 4096
+__device__ __forceinline__ void nv_partials_load(const uint32_t* __restrict__ partial, int npart, u32x4 (&pv)[NV_PV]) {
+#pragma unroll
+  for (int k = 0; k < NV_PV; ++k) {
+    const int idx = (k * QT + (int)threadIdx.x) * 4;
+    pv[k] = idx < npart ? *reinterpret_cast<const u32x4*>(partial + idx) : u32x4{0, 0, 0, 0};
+  }
+}
+__device__ __forceinline__ float nv_global_from_partials(const u32x4 (&pv)[NV_PV], uint32_t* red) {
   uint32_t am = 0;
-  for (int i = threadIdx.x; i < npart; i += QT) am = max(am, partial[i]);
+#pragma unroll
+  for (int k = 0; k < NV_PV; ++k) am = max(max(am, max(pv[k][0], pv[k][1])), max(pv[k][2], pv[k][3]));
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) am = umax_xor(am, m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = am;
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS write is done
+  block_barrier();
   uint32_t r = red[0];
 #pragma unroll
   for (int i = 1; i < QT / 64; ++i) r = max(r, red[i]);
@@ -181,6 +195,8 @@ __device__ __forceinline__ float nv_global_from_partials(const uint32_t* __restr
 // One lane per 16-element block (QB blocks in flight per lane): the block's
 // scale and its seven decision boundaries (fp64 work) are computed once per
 // block rather than once per 16-byte vector, and no lane exchange is needed.
+// The first iteration's loads go out before the per-tensor scale is reduced
+// from the partial maxima (they do not depend on it).
 template <typename TIn, bool CONTIG>
 __global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int64_t ldx, uint32_t bpr,
                                                  uint32_t nblk, uint8_t* __restrict__ codes,
@@ -190,19 +206,11 @@ __global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int6
   constexpr int VPB = 16 / EPL;                // vectors per block (4 or 2)
   constexpr int QB = 2;                        // blocks per lane per iteration
   __shared__ uint32_t red[QT / 64];
-  float g;
-  if (partial) {
-    g = nv_global_from_partials(partial, npart, red);
-    if (blockIdx.x == 0 && threadIdx.x == 0) *gout = g;
-  } else {
-    g = *gout;  // static per-tensor scale supplied by the caller
-  }
-  const double six_g = 6.0 * (double)g;
   const int lane = threadIdx.x & 63;
   const uint32_t wave_global = (blockIdx.x * QT + threadIdx.x) >> 6;
   const uint32_t nwaves = (gridDim.x * QT) >> 6;
-  for (uint32_t base = wave_global * (64 * QB); base < nblk; base += nwaves * (64 * QB)) {
-    u32x4 d[QB][VPB];
+  const uint32_t stride = nwaves * (64 * QB);
+  auto load = [&](u32x4 (&d)[QB][VPB], uint32_t base) {
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       const uint32_t b = base + u * 64 + lane;
@@ -214,8 +222,25 @@ __global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int6
         p = x + (size_t)r * ldx + (size_t)c * 16;
       }
 #pragma unroll
-      for (int q = 0; q < VPB; ++q) d[u][q] = (b < nblk) ? *reinterpret_cast<const u32x4*>(p + q * EPL) : u32x4{0, 0, 0, 0};
+      for (int q = 0; q < VPB; ++q)
+        d[u][q] = (b < nblk) ? *reinterpret_cast<const u32x4*>(p + q * EPL) : u32x4{0, 0, 0, 0};
     }
+  };
+  u32x4 d[QB][VPB];
+  u32x4 pv[NV_PV];
+  if (partial) nv_partials_load(partial, npart, pv);
+  uint32_t base = wave_global * (64 * QB);
+  if (base < nblk) load(d, base);
+  float g;
+  if (partial) {
+    g = nv_global_from_partials(pv, red);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *gout = g;
+  } else {
+    g = *gout;  // static per-tensor scale supplied by the caller
+  }
+  const double six_g = 6.0 * (double)g;
+  for (; base < nblk; base += stride) {
+    if (base != wave_global * (64 * QB)) load(d, base);   // the first iteration's blocks are in flight already
 #pragma unroll
     for (int u = 0; u < QB; ++u) {
       const uint32_t b = base + u * 64 + lane;
@@ -239,13 +264,18 @@ __global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int6
       // s_b = E4M3 nearest to amax / (6 g); unit y = s_b * g is exact in fp64.
       const uint32_t sc = e4m3_rne_sat((double)ffrom(am) / six_g);
       const double y = (double)e4m3_to_f32(sc) * (double)g;
-      uint32_t U[7];
-      nv_boundaries(y, U);
-      uint32_t lo = 0, hi = 0;
+      const NvFast nf = nv_fast_setup(y, am);
+      uint32_t lo, hi;
+      const bool fast_lo = nv_fast_codes8(xb, nf, lo), fast_hi = nv_fast_codes8(xb + 8, nf, hi);
+      if (!(nf.ok && fast_lo && fast_hi)) {   // an element within 2^-20 of a boundary: exact test
+        uint32_t U[7];
+        nv_boundaries(y, U);
+        lo = hi = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        lo |= nv_code(xb[i], U) << (4 * i);
-        hi |= nv_code(xb[8 + i], U) << (4 * i);
+        for (int i = 0; i < 8; ++i) {
+          lo |= nv_code(xb[i], U) << (4 * i);
+          hi |= nv_code(xb[8 + i], U) << (4 * i);
+        }
       }
       if (b < nblk) {
         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -554,7 +584,9 @@ int nv_partials_count(int64_t rows, int64_t cols, int xdt_bf16) {
   // tensors keep the full amax-pass grid.
   const uint64_t nvec = (uint64_t)(rows * cols / epl);
   const int n = grid_for(nvec, QT * 4);
-  return nvec <= (1ull << 23) && n > 1024 ? 1024 : n;
+  // a multiple of 4 (the quantize kernel reads them as 16-byte vectors); the
+  // extra amax workgroups find no vectors and write 0
+  return ((nvec <= (1ull << 23) && n > 1024 ? 1024 : n) + 3) & ~3;
 }
 
 hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,

@@ -156,6 +156,68 @@ def test_quantize_nvfp4_bit_exact(shape, dtype):
         assert np.array_equal(host(t.codes), rc)
 
 
+def nvfp4_boundary_blocks(g, rng):
+    """16-element blocks whose first element fixes the E4M3 scale s (amax =
+    fp32(6 s g)) and whose other elements sit on, one fp32 step below and one
+    above every E2M1 decision boundary m_j * s * g of the block (m_j the seven
+    midpoints 0.25 .. 5; the unit s * g is formed in fp64), with random signs,
+    plus signed zeros and fp32 subnormals.  Every E4M3 scale from subnormal
+    codes to 416 is used."""
+    mids = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+    blocks = []
+    for code in list(range(1, 8)) + list(range(8, 0x7E, 3)):
+        s = O.e4m3_value_from_bits(code)
+        unit = s * float(g)
+        amax = np.float32(6.0 * unit)
+        cand = []
+        for m in mids:
+            f = np.float32(m * unit)
+            cand += [f, np.nextafter(f, np.float32(0)), np.nextafter(f, np.float32(np.inf))]
+        cand += [np.float32(0.0), np.float32(-0.0), np.float32(1e-40), np.float32(-3e-42)]
+        cand = np.array(cand, np.float32)
+        for k in range(0, len(cand), 15):
+            part = cand[k:k + 15]
+            blk = np.zeros(16, np.float32)
+            blk[0] = amax
+            blk[1:1 + len(part)] = part
+            signs = np.where(rng.random(16) < 0.5, -1.0, 1.0).astype(np.float32)
+            blocks.append(blk * signs)
+    return np.stack(blocks)
+
+
+def test_quantize_nvfp4_decision_boundaries():
+    """Codes on and beside every decision boundary match the oracle bit for
+    bit (ties stay on the even code), with a static per-tensor scale and with
+    the tensor scale computed from the data (one block sets the tensor max)."""
+    announce("quantize nvfp4 decision boundaries")
+    rng = np.random.default_rng(23)
+    # 1.5 * 2^-8 has two significant bits, so every boundary is an fp32 value
+    # (exact ties); 0.0037 has 24, so most boundaries fall between fp32 values
+    for g in (np.float32(0.0037), np.float32(1.5 * 2.0 ** -8)):
+        blocks = nvfp4_boundary_blocks(g, rng)
+        x = np.concatenate([blocks, np.zeros(((-len(blocks)) % 4, 16), np.float32)]).reshape(-1, 64)
+        rc, rs, _ = O.nvfp4_quantize(x, global_scale=g)
+        t = mx_quant_gpu(x, torch.float32, fmt="nvfp4", static_global=float(g))
+        assert np.array_equal(host(t.scales), rs)
+        assert np.array_equal(host(t.codes), rc)
+    # dynamic: plant a block whose max gives the tensor scale g2, then build
+    # the boundary blocks on that g2
+    amax_t = np.float32(2688.0 * 0.0021)
+    g2 = O.nvfp4_global_scale(np.array([amax_t], np.float32))
+    blocks = nvfp4_boundary_blocks(g2, rng)
+    lead = np.zeros((1, 16), np.float32)
+    lead[0, 0] = -amax_t
+    allb = np.concatenate([lead, blocks])
+    pad = (-len(allb)) % 4
+    x = np.concatenate([allb, np.zeros((pad, 16), np.float32)]).reshape(-1, 64)
+    rc, rs, rg = O.nvfp4_quantize(x)
+    assert rg == g2
+    t = mx_quant_gpu(x, torch.float32, fmt="nvfp4")
+    assert host(t.global_scale)[0] == rg
+    assert np.array_equal(host(t.scales), rs)
+    assert np.array_equal(host(t.codes), rc)
+
+
 # Tensor-wide maximum at full size: the amax pass is a grid-stride loop whose
 # per-workgroup partials every quantize workgroup reduces again; the largest
 # |x| (negative) is planted at the start, a few grid strides in and in the
