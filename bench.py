@@ -8,10 +8,11 @@ value = 2*M*N*K / step time, in TFLOPS.  Inputs are resident in HBM before
 timing; two input sets (804 MB) alternate so that the 256 MB last-level cache
 cannot hold a step's inputs.  The timed steps replay HIP graphs (two steps,
 one per input set, per graph launch; checked to reproduce the eager result).
-The default 200 warmup steps (about 45 ms) let the clock settle under load;
-after only 5 (1 ms) the timed steps run about 8 % slower.  Per-kernel
-durations come from HIP events around graphs of back-to-back launches of
-that kernel, on the stream they run on.
+Per-kernel durations come from HIP events around graphs of back-to-back
+launches of each kernel, on the stream they run on; they are measured first
+(about 45 ms of full-load work), which also lets the clock settle before the
+warmup and timed steps (without it, 5 warmup steps leave the timed steps
+about 8 % slower than 200 do).
 
 Secondary measurements (same JSON line, `secondary`): the W4A16 GEMV
 N=K=8192 at M = 1, 8, 16 (GB/s, weights rotated over 16 copies), the NVFP4
@@ -23,8 +24,11 @@ combine), the fused RMSNorm + quantize, and MXFP8 / MXFP6 products on the
 quantization variants (16-element E8M0 blocks, the OCP floor rule, naive
 per-tensor FP4, ...) with the reconstruction SNR of each.
 
-cpu_baseline: the CPU oracle (numpy, fp64) on a bounded sub-problem of the
-same step, timed on this host.
+Ceilings (`secondary.ceilings`): a plain streaming read of the GEMV's bytes
+and plain copies, the practical bounds beside the 8 TB/s peak.
+
+cpu_baseline: the CPU oracle (numpy, fp64) on the whole step, timed on this
+host's cores.
 """
 from __future__ import annotations
 
@@ -59,9 +63,10 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def load_traffic(name, kernel_files):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel source; else None."""
+def kernel_counter(name, kernel_files, kernel, grid, field):
+    """A derived figure (field, e.g. "mfma_busy_frac") of one kernel and grid
+    from a committed summary written by --summarize-pmc, if it was taken on
+    the current kernel source; else None."""
     path = os.path.join(PROFILES, name)
     if not os.path.exists(path):
         return None
@@ -72,10 +77,36 @@ def load_traffic(name, kernel_files):
             kv[k.strip()] = v.strip()
     if kv.get("source_hash") != source_hash(kernel_files):
         return None
-    try:
-        return float(kv["hbm_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+    for k, v in kv.items():
+        if k.startswith(f"mxk::{kernel}<") and k.endswith(f"@{grid}.{field}"):
+            return float(v)
+    return None
+
+
+def summarize_trace(dirs, out_path, title, command):
+    """Per kernel and grid: dispatch count and duration statistics from
+    rocprofv3 kernel-trace CSVs."""
+    import collections
+    import csv
+    import glob
+    import statistics
+    d = collections.defaultdict(list)
+    for dd in dirs:
+        for f in glob.glob(os.path.join(dd, "**", "*kernel_trace.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                k = (r["Kernel_Name"].split("(")[0].replace("void ", ""), r["Grid_Size"])
+                d[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    lines = [f"# {title}", "# Command (repository root, TMPDIR=/tmp, one MI355X):"]
+    lines += [f"#   {c}" for c in command]
+    lines += ["# Durations are End - Start per dispatch in microseconds (warm-up and graph-capture calls included).",
+              f"{'kernel':60s} {'grid':>9s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>9s}"]
+    for (name, grid), v in sorted(d.items()):
+        if not name.startswith("mxk::"):
+            continue
+        lines.append(f"{name:60s} {grid:>9s} {len(v):6d} {sum(v) / len(v):9.2f} {statistics.median(v):9.2f} "
+                     f"{min(v):9.2f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def capture(torch, fn, reps=1):
@@ -154,6 +185,18 @@ def bench_main(args, torch, mx, W):
         if n % 2:
             graphs[0].replay()
 
+    # Per-kernel durations first: events around graphs of back-to-back
+    # launches that alternate between the two input sets (each set's fp32
+    # inputs alone fill about half of the last-level cache).  These ~45 ms of
+    # full-load work also let the clock settle before the warmup steps.
+    R = 5
+
+    def alt(fn):
+        return lambda: [fn(*sets[i]) for i in (0, 1)]
+    qx_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(x, out=aq)), R), 2 * R, replays=20)
+    qw_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(wt, out=bq)), R), 2 * R, replays=20)
+    g_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_gemm(aq, bq, out=c)), R), 2 * R, replays=20)
+
     run(args.warmup)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -163,29 +206,24 @@ def bench_main(args, torch, mx, W):
     ms_step = wall * 1e3 / args.steps
     del graphs, pair
 
-    # per-kernel durations: events around graphs of back-to-back launches that
-    # alternate between the two input sets (each set's fp32 inputs alone fill
-    # about half of the last-level cache)
-    R = 5
-
-    def alt(fn):
-        return lambda: [fn(*sets[i]) for i in (0, 1)]
-    qx_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(x, out=aq)), R), 2 * R, replays=20)
-    qw_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_quantize(wt, out=bq)), R), 2 * R, replays=20)
-    g_ms = time_graph(torch, capture(torch, alt(lambda x, wt, aq, bq: mx.mx_gemm(aq, bq, out=c)), R), 2 * R, replays=20)
     flops = 2.0 * M * N * K
     qx_bytes = M * K * 4 + M * K // 2 + M * K // 32
     qw_bytes = N * K * 4 + N * K // 2 + N * K // 32
     gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * 2
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
-    traffic = load_traffic("mxfp4_gemm_4096x8192x8192_counters.txt", ["gemm_mxfp4.hip", "mx_device.h"])
+    gfiles = ["gemm_mxfp4.hip", "mx_device.h"]
+    gsum = "mxfp4_gemm_4096x8192x8192_counters.txt"
+    traffic = kernel_counter(gsum, gfiles, "k_gemm_mx_k256", 131072, "hbm_bytes")
     res = {
         "value": flops / (ms_step * 1e-3) / 1e12,
         "ms_per_step": ms_step,
         "roofline": {"bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_FP4_TFLOPS, "unit": "TFLOP/s",
                      "frac": gemm_tflops / PEAK_FP4_TFLOPS, "traffic": traffic,
                      "kernel": GEMM_KERNEL, "flops_per_launch": flops, "algorithmic_bytes_per_launch": gemm_bytes,
-                     "avg_launch_ms": g_ms},
+                     "avg_launch_ms": g_ms,
+                     "mfma_busy_frac": kernel_counter(gsum, gfiles, "k_gemm_mx_k256", 131072, "mfma_busy_frac"),
+                     "clock_ghz_under_profiler": kernel_counter(gsum, gfiles, "k_gemm_mx_k256", 131072, "clock_ghz"),
+                     "counters": f"profiles/{gsum}"},
         "kernels": {
             "quantize_x": {"avg_ms": qx_ms, "GB/s": qx_bytes / (qx_ms * 1e-3) / 1e9, "bytes": qx_bytes,
                            "frac_hbm": qx_bytes / (qx_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
@@ -222,6 +260,34 @@ def bench_gemv(args, torch, mx, W):
         gbs = byt / (ms * 1e-3) / 1e9
         out[f"M={M}"] = {"avg_ms": ms, "GB/s": gbs, "frac_hbm": gbs / PEAK_HBM_GBS, "bytes": byt,
                          "TFLOPS": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
+    # The same product on the vector ALU only: at K = 8224 (not a multiple
+    # of 256) mx_gemv runs its dot2 kernel for every M, so these lines show
+    # what the MFMA-free path reaches at M = 8 and 16 (0.4 % more K).
+    K2 = K + 32
+    w2 = torch.from_numpy(W.weights(N, K2)).to(dev)
+    ws2 = [mx.mx_quantize(w2) for _ in range(reps)]
+    del w2
+    for M in (8, 16):
+        x = torch.from_numpy(W.activations(M, K2)).to(torch.bfloat16).to(dev)
+        y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+        def batch2():
+            for i in range(reps):
+                mx.mx_gemv(x, ws2[i], out=y)
+        g = capture(torch, batch2, max(1, args.gemv_iters // reps))
+        ms = time_graph(torch, g, reps * max(1, args.gemv_iters // reps))
+        byt = N * K2 // 2 + N * K2 // 32 + 2 * M * K2 + 2 * M * N
+        out[f"M={M}_vector_alu_K{K2}"] = {"avg_ms": ms, "GB/s": byt / (ms * 1e-3) / 1e9,
+                                          "frac_hbm": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                          "note": "dot2 kernel (no matrix cores)"}
+    del ws2
+    for M, kern in ((1, "k_gemv_sk"), (8, "k_gemv_mf"), (16, "k_gemv_mf")):
+        g = out[f"M={M}"]
+        out[f"roofline_M{M}"] = {"bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": g["frac_hbm"],
+                                 "traffic": kernel_counter("gemv_8192x8192_counters.txt", ["gemv.hip", "mx_device.h"],
+                                                           f"{kern}<{M}" if kern == "k_gemv_mf" else kern,
+                                                           131072, "hbm_bytes")}
     return out
 
 
@@ -267,11 +333,16 @@ def bench_wide(args, torch, mx, W):
         qx = time_graph(torch, capture(torch, lambda: mx.mx_quantize(x, fa, out=aq), R), R)
         mx.mx_quantize(wt, fb, out=bq)
         g = time_graph(torch, capture(torch, lambda: mx.mx_gemm(aq, bq, out=c), R), R, replays=2)
+        gf = time_graph(torch, capture(torch, lambda: mx.mx_gemm(aq, bq, out=c, f8f6f4_matrix_cores=True), R), R,
+                        replays=2)
         flops = 2.0 * M * N * K
-        tf = flops / (g * 1e-3) / 1e12
+        tf, tff = flops / (g * 1e-3) / 1e12, flops / (gf * 1e-3) / 1e12
         peak = PEAK_FP8_TFLOPS if "mxfp8" in (fa + fb) else PEAK_FP4_TFLOPS
         qbytes = M * K * 2 + M * K * mx.element_bits(fa) // 8 + M * K // 32
-        res[f"{fa}_x_{fb}"] = {"gemm_avg_ms": g, "gemm_TFLOPS": tf, "gemm_peak_TFLOPS": peak, "gemm_frac": tf / peak,
+        res[f"{fa}_x_{fb}"] = {"exact_gemm_avg_ms": g, "exact_gemm_TFLOPS": tf,
+                               "exact_gemm_frac_bf16_peak": tf / PEAK_F16_TFLOPS,
+                               "f8f6f4_gemm_avg_ms": gf, "f8f6f4_gemm_TFLOPS": tff, "f8f6f4_gemm_peak_TFLOPS": peak,
+                               "f8f6f4_gemm_frac": tff / peak,
                                "quant_x_bf16_avg_ms": qx, "quant_x_GB/s": qbytes / (qx * 1e-3) / 1e9}
         del aq, bq
     return res
@@ -377,27 +448,166 @@ def bench_rmsnorm(args, torch, mx, W):
 
 
 def cpu_baseline(d):
-    """The oracle, as it stands, on a bounded sub-problem of the same step:
-    X rows 0..1023 and W rows 0..4095 (both quantized) and their GEMM."""
+    """The oracle, as it stands, on the whole step: quantize all of X and W
+    (row chunks on a thread pool with one worker per host core, at most 16;
+    the oracle's numpy steps release the GIL) and the fp64 GEMM (numpy's
+    BLAS, on its own threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = os.cpu_count() or 1
-    mr, nr, K = 1024, 4096, d["x"].shape[1]
-    x, w = d["x"][:mr], d["w"][:nr]
+    cores = min(16, os.cpu_count() or 1)
+    x, w = d["x"], d["w"]
+    M, K = x.shape
+    N = w.shape[0]
+
+    def quantize(t):
+        parts = [t[r:r + 128] for r in range(0, t.shape[0], 128)]
+        with ThreadPoolExecutor(cores) as ex:
+            outs = list(ex.map(O.mxfp4_quantize, parts))
+        return np.concatenate([o[0] for o in outs]), np.concatenate([o[1] for o in outs])
     t0 = time.perf_counter()
-    ca, sa = O.mxfp4_quantize(x)
-    cb, sb = O.mxfp4_quantize(w)
+    ca, sa = quantize(x)
+    cb, sb = quantize(w)
     y = O.gemm(O.dequantize("mxfp4", ca, sa), O.dequantize("mxfp4", cb, sb), out="bf16")
     dt = time.perf_counter() - t0
-    assert y.shape == (mr, nr)
-    return {"value": 2.0 * mr * nr * K / dt / 1e12, "unit": "TFLOPS", "cores": threads, "kind": "oracle",
-            "sample": f"sub-problem {mr}x{nr}x{K} of the step (quantize X rows, quantize W rows, fp64 GEMM); "
-                      f"{dt:.1f} s; quantization single-threaded numpy, GEMM via BLAS with {threads} threads",
+    assert y.shape == (M, N)
+    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+            "sample": f"the whole step {M}x{N}x{K} (quantize X, quantize W, fp64 GEMM), not extrapolated; "
+                      f"{dt:.1f} s; quantization on {cores} threads, GEMM in numpy's BLAS",
             "seconds": dt}
+
+
+def bench_ceilings(args, torch, mx, W):
+    """Practical ceilings beside the 8 TB/s peak: a plain streaming read of
+    the GEMV's weight bytes (35.7 MB, rotating over 16 buffers so every read
+    comes from HBM) and plain copies of the quantize inputs' sizes, by the
+    measurement-only kernels of libmx_ceiling.so (16-byte loads, four in
+    flight per lane); the best of 2, 4 and 8 workgroups per CU."""
+    import ctypes
+    L = ctypes.CDLL(os.path.join(ROOT, "microscaling_fp4_quantization_mx_amd", "libmx_ceiling.so"))
+    L.mxc_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    L.mxc_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    sink = torch.empty(256 * 8, dtype=torch.int32, device=dev)
+    out = {}
+    gemv_bytes = W.C2.N * W.C2.K // 2 + W.C2.N * W.C2.K // 32 + 2 * W.C2.K + 2 * W.C2.N
+    nb = (gemv_bytes + 255) // 256 * 256
+    bufs = [torch.ones(nb // 4, dtype=torch.int32, device=dev) for _ in range(16)]
+    best = None
+    for per_cu in (2, 4, 8):
+        def f():
+            st = torch.cuda.current_stream().cuda_stream     # the capturing stream
+            for b in bufs:
+                assert L.mxc_read(b.data_ptr(), nb, sink.data_ptr(), per_cu, st) == 0
+        ms = time_graph(torch, capture(torch, f, 8), 16 * 8)
+        gbs = nb / (ms * 1e-3) / 1e9
+        best = max(best or 0.0, gbs)
+    out["read_35.7MB_GB/s"] = best
+    del bufs
+    for name, nbytes in (("copy_128MiB_GB/s", 128 << 20), ("copy_256MiB_GB/s", 256 << 20)):
+        src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+        dsts = [torch.empty_like(src) for _ in range(2)]
+        best = None
+        for per_cu in (2, 4, 8):
+            def f():
+                st = torch.cuda.current_stream().cuda_stream
+                for dd in dsts:
+                    assert L.mxc_copy(src.data_ptr(), dd.data_ptr(), nbytes, per_cu, st) == 0
+            ms = time_graph(torch, capture(torch, f, 4), 2 * 4)
+            best = max(best or 0.0, 2 * nbytes / (ms * 1e-3) / 1e9)   # read + write
+        out[name] = best
+        del src, dsts
+    return out
+
+
+SECONDARY = {
+    "ceilings": (bench_ceilings, "ceilings"),
+    "gemv": (bench_gemv, "w4a16_gemv_8192x8192"),
+    "nvfp4": (bench_nvfp4, "nvfp4_2048x28672x8192"),
+    "wide": (bench_wide, "mx_wide_gemm_4096x8192x8192"),
+    "variants": (bench_variants, "variants_4096x8192_fp32"),
+    "grouped": (bench_grouped, "grouped_8x4096x14336_T8192"),
+    "rmsnorm": (bench_rmsnorm, "rmsnorm_quantize_8192x14336_bf16"),
+    "moe": (bench_moe, "moe_top2_8x4096x14336_T4096"),
+}
+SECONDARY_NAMES = tuple(SECONDARY)
+
+
+def summarize_pmc(dirs, out_path, title, command, kernel_files, algorithmic=None):
+    """Turn rocprofv3 counter-collection CSVs (one directory per pass) into a
+    committed summary: per kernel and grid, the mean of every counter per
+    dispatch, the kernel time from the dispatch timestamps, and derived
+    figures.  Calibration of the HBM byte counters: FETCH_SIZE x 2,
+    WRITE_SIZE x 1 (KiB), measured on a 512 MiB elementwise copy."""
+    import collections
+    import csv
+    import glob
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur = collections.defaultdict(list)
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                k = (r["Kernel_Name"].split("(")[0].replace("void ", ""), r["Grid_Size"])
+                agg[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r["Counter_Name"] in ("GRBM_GUI_ACTIVE", "FETCH_SIZE"):
+                    dur[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+    lines = [f"# {title}", "# Commands (repository root, TMPDIR=/tmp, one MI355X), one counter pass each:"]
+    lines += [f"#   {c}" for c in command]
+    lines += ["# Units: counters are means per dispatch.  GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the",
+              "# kernel's cycles are GRBM_GUI_ACTIVE / 8 and its clock that / the dispatch time.  MFMA busy",
+              "# fraction = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs); VALU busy = SQ_ACTIVE_INST_VALU x 4 /",
+              "# (cycles x 1024) (quad-cycles per wave summed per SIMD); LDS busy = SQ_LDS_IDX_ACTIVE / (cycles x 256).",
+              "# HBM bytes: FETCH_SIZE x 2 KiB and WRITE_SIZE x 1 KiB (calibrated on a 512 MiB copy).",
+              "# For dispatches of a few microseconds GRBM_GUI_ACTIVE includes a fixed window around the kernel, so",
+              "# the GRBM-derived clock and busy fractions are too high / too low there; the VALU issue fraction uses",
+              "# the dispatch time instead: SQ_INSTS_VALU / (dispatch time x 2.4 GHz x 1024 SIMDs / 4).",
+              f"# source_hash = sha256 of {', '.join(kernel_files)} (first 16 hex digits) when the counters were taken;",
+              "# bench.py reports these figures only while the kernel source still has this hash.",
+              f"source_hash={source_hash(kernel_files)}"]
+    for (name, grid), cs in sorted(agg.items()):
+        if not (name.startswith("mxk::") or "AUnaryFunctor" in name):   # library kernels and the calibration copy
+            continue
+        m = {c: sum(v) / len(v) for c, v in cs.items()}
+        t_us = sum(dur[(name, grid)]) / max(1, len(dur[(name, grid)]))
+        lines.append(f"# {name} grid {grid}: {len(next(iter(cs.values())))} dispatches per pass, {t_us:.2f} us "
+                     "per dispatch under the profiler")
+        for c in sorted(m):
+            lines.append(f"#   {c:34s} {m[c]:18.1f}")
+        if "GRBM_GUI_ACTIVE" in m:
+            cyc = m["GRBM_GUI_ACTIVE"] / 8
+            lines.append(f"#   kernel cycles {cyc:.0f}, clock {cyc / (t_us * 1e3):.3f} GHz")
+        key = f"{name}@{grid}"
+        if "GRBM_GUI_ACTIVE" in m:
+            cyc = m["GRBM_GUI_ACTIVE"] / 8
+            lines.append(f"{key}.clock_ghz={cyc / (t_us * 1e3):.4f}")
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                lines.append(f"{key}.mfma_busy_frac={m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.4f}")
+            if "SQ_ACTIVE_INST_VALU" in m:
+                lines.append(f"{key}.valu_busy_frac={m['SQ_ACTIVE_INST_VALU'] * 4 / (cyc * 1024):.4f}")
+            if "SQ_LDS_IDX_ACTIVE" in m:
+                lines.append(f"{key}.lds_busy_frac={m['SQ_LDS_IDX_ACTIVE'] / (cyc * 256):.4f}")
+            if "SQ_LDS_BANK_CONFLICT" in m:
+                lines.append(f"{key}.lds_bank_conflict_frac={m['SQ_LDS_BANK_CONFLICT'] / (cyc * 256):.4f}")
+            if "TA_TA_BUSY_sum" in m:
+                lines.append(f"{key}.ta_busy_frac={m['TA_TA_BUSY_sum'] / (cyc * 256):.4f}")
+        if "SQ_INSTS_VALU" in m:
+            # issue slots: one wave instruction per 4 clocks per SIMD, 1024 SIMDs, at the 2.4 GHz peak clock
+            # (an upper bound on the slots, so the fraction is a lower bound)
+            lines.append(f"{key}.valu_insts={m['SQ_INSTS_VALU']:.0f}")
+            lines.append(f"{key}.valu_issue_frac_at_2400MHz={m['SQ_INSTS_VALU'] / (t_us * 2400 * 256):.4f}")
+        if "FETCH_SIZE" in m:
+            lines.append(f"{key}.fetch_bytes={m['FETCH_SIZE'] * 2 * 1024:.0f}")
+        if "WRITE_SIZE" in m:
+            lines.append(f"{key}.write_bytes={m['WRITE_SIZE'] * 1024:.0f}")
+        if "FETCH_SIZE" in m and "WRITE_SIZE" in m:
+            hbm = m["FETCH_SIZE"] * 2 * 1024 + m["WRITE_SIZE"] * 1024
+            lines.append(f"{key}.hbm_bytes={hbm:.0f}")
+            if algorithmic and key in algorithmic:
+                lines.append(f"{key}.algorithmic_bytes={algorithmic[key]}")
+                lines.append(f"{key}.traffic_over_algorithmic={hbm / algorithmic[key]:.3f}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
 
 
 def main():
@@ -407,12 +617,29 @@ def main():
     ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps first; the clock needs tens of milliseconds of load to settle")
     ap.add_argument("--only-main", action="store_true", help="skip secondary measurements and the CPU baseline")
+    ap.add_argument("--only", default=None, choices=SECONDARY_NAMES,
+                    help="run the main step and one secondary measurement only (for profiler passes)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--gemv-iters", type=int, default=200)
     ap.add_argument("--side-iters", type=int, default=10)
+    ap.add_argument("--summarize-pmc", metavar="OUT", help="write a counter summary from rocprofv3 CSV directories")
+    ap.add_argument("--summarize-trace", metavar="OUT", help="write a kernel-trace summary from rocprofv3 CSV dirs")
+    ap.add_argument("--dirs", nargs="*", default=[], help="rocprofv3 output directories (with --summarize-*)")
+    ap.add_argument("--title", default="", help="summary title (with --summarize-*)")
+    ap.add_argument("--command", nargs="*", default=[], help="the commands that made the CSVs (--summarize-*)")
+    ap.add_argument("--sources", nargs="*", default=[], help="kernel sources hashed into the summary")
+    ap.add_argument("--algorithmic", nargs="*", default=[], help="KERNEL@GRID=BYTES algorithmic bytes per launch")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (counter calibration for rocprofv3 --pmc)")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        alg = dict(a.rsplit("=", 1) for a in args.algorithmic)
+        summarize_pmc(args.dirs, args.summarize_pmc, args.title, args.command, args.sources,
+                      {k: int(v) for k, v in alg.items()})
+        return
+    if args.summarize_trace:
+        summarize_trace(args.dirs, args.summarize_trace, args.title, args.command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the library has no multi-GPU path); --gpus {args.gpus} is not "
               f"supported", file=sys.stderr)
@@ -442,39 +669,20 @@ def main():
            "roofline": res["roofline"], "kernels": res["kernels"]}
     if not args.only_main:
         sec = {}
-        log("secondary: W4A16 GEMV")
-        sec["w4a16_gemv_8192x8192"] = bench_gemv(args, torch, mx, W)
-        g1 = sec["w4a16_gemv_8192x8192"]["M=1"]
-        sec["w4a16_gemv_8192x8192"]["roofline_M1"] = {"bound": "hbm", "achieved": g1["GB/s"], "peak": PEAK_HBM_GBS,
-                                                       "unit": "GB/s", "frac": g1["frac_hbm"],
-                                                       "traffic": load_traffic("gemv_m1_8192x8192_counters.txt",
-                                                                               ["gemv.hip", "mx_device.h"])}
-        g16 = sec["w4a16_gemv_8192x8192"]["M=16"]
-        sec["w4a16_gemv_8192x8192"]["roofline_M16"] = {"bound": "hbm", "achieved": g16["GB/s"], "peak": PEAK_HBM_GBS,
-                                                        "unit": "GB/s", "frac": g16["frac_hbm"],
-                                                        "traffic": load_traffic("gemv_m16_8192x8192_counters.txt",
-                                                                                ["gemv.hip", "mx_device.h"])}
-        torch.cuda.empty_cache()
-        log("secondary: NVFP4 quantize + GEMM")
-        sec["nvfp4_2048x28672x8192"] = bench_nvfp4(args, torch, mx, W)
-        torch.cuda.empty_cache()
-        log("secondary: MXFP8 / MXFP6 GEMM pairs")
-        sec["mx_wide_gemm_4096x8192x8192"] = bench_wide(args, torch, mx, W)
-        torch.cuda.empty_cache()
-        log("secondary: quantization variants and reconstruction SNR")
-        sec["variants_4096x8192_fp32"] = bench_variants(args, torch, mx, W)
-        torch.cuda.empty_cache()
-        log("secondary: fused dynamic-quantize grouped GEMM")
-        sec["grouped_8x4096x14336_T8192"] = bench_grouped(args, torch, mx, W)
-        torch.cuda.empty_cache()
-        log("secondary: fused RMSNorm + FP4 quantize")
-        sec["rmsnorm_quantize_8192x14336_bf16"] = bench_rmsnorm(args, torch, mx, W)
-        torch.cuda.empty_cache()
-        log("secondary: routed expert layer (top-2)")
-        sec["moe_top2_8x4096x14336_T4096"] = bench_moe(args, torch, mx, W)
-        torch.cuda.empty_cache()
+        for name in SECONDARY_NAMES:
+            if args.only and name != args.only:
+                continue
+            fn, key = SECONDARY[name]
+            log(f"secondary: {name}")
+            sec[key] = fn(args, torch, mx, W)
+            torch.cuda.empty_cache()
+        if "ceilings" in sec and "w4a16_gemv_8192x8192" in sec:
+            c = sec["ceilings"]["read_35.7MB_GB/s"]
+            for M in W.GEMV_M:
+                g = sec["w4a16_gemv_8192x8192"][f"M={M}"]
+                g["frac_read_ceiling"] = g["GB/s"] / c
         out["secondary"] = sec
-        if not args.no_cpu:
+        if not args.no_cpu and not args.only:
             log("cpu baseline (oracle)")
             out["cpu_baseline"] = cpu_baseline(d)
     print(json.dumps(out), flush=True)
