@@ -389,14 +389,18 @@ def bench_grouped(args, torch, mx, W):
     x = torch.from_numpy(d["x"]).to(torch.bfloat16).to(dev)
     offs = torch.from_numpy(d["offsets"]).to(dev)
     y = torch.empty(T, N, dtype=torch.bfloat16, device=dev)
-    wsz = T * K // 2 + T * K // 32 + 4096   # >= mx_workspace_bytes for the dynamic A operand
-    wsp = torch.empty(wsz, dtype=torch.uint8, device=dev)
     R = max(1, args.side_iters)
-    ms = time_graph(torch, capture(torch, lambda: mx.mx_gemm(x, wq, N=N, out=y, groups=G, offsets=offs,
-                                                             workspace=wsp), R), R, replays=3)
+    # the binding sizes the workspace (codes of the quantized tokens; with the
+    # fused kernel also its counters and partial tiles) with mx_workspace_bytes
+    ms = time_graph(torch, capture(torch, lambda: mx.mx_gemm(x, wq, N=N, out=y, groups=G, offsets=offs), R), R,
+                    replays=3)
+    ms_fused = time_graph(torch, capture(torch, lambda: mx.mx_gemm(x, wq, N=N, out=y, groups=G, offsets=offs,
+                                                                   fused_quantize=True), R), R, replays=3)
     flops = 2.0 * T * N * K
     return {"avg_ms": ms, "TFLOPS": flops / (ms * 1e-3) / 1e12, "frac_fp4_peak": flops / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS,
-            "note": "one mx_gemm call: MXFP4 quantization of the bf16 tokens + grouped W4A4 GEMM"}
+            "note": "one mx_gemm call: MXFP4 quantization of the bf16 tokens (its own launch) + grouped W4A4 GEMM",
+            "fused_avg_ms": ms_fused, "fused_TFLOPS": flops / (ms_fused * 1e-3) / 1e12,
+            "fused_note": "the same call with MX_GEMM_FUSED_QUANTIZE: quantization and GEMM in one persistent kernel"}
 
 
 def bench_moe(args, torch, mx, W):

@@ -20,7 +20,7 @@ __all__ = [
     "mx_status_string", "mx_version", "MX_OP_MOE_ROUTE", "mx_moe_route", "mx_quantize_rows", "mx_moe_combine",
     "moe_forward", "mx_rmsnorm_quantize", "MX_FMT_MXFP8_E4M3", "MX_FMT_MXFP8_E5M2", "MX_FMT_MXFP6_E2M3",
     "MX_FMT_MXFP6_E3M2", "element_bits", "MX_FMT_MXFP4_K16", "MX_FMT_FP4_TENSOR", "MX_QUANT_SCALE_FLOOR",
-    "padded_cols", "mx_quantize_noalloc", "MX_GEMM_F8F6F4_MATRIX_CORES",
+    "padded_cols", "mx_quantize_noalloc", "MX_GEMM_F8F6F4_MATRIX_CORES", "MX_GEMM_FUSED_QUANTIZE",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -32,7 +32,7 @@ MX_FMT_MXFP4_K16, MX_FMT_FP4_TENSOR = 6, 7
 MX_DT_F32, MX_DT_BF16 = 0, 1
 MX_QUANT_DEFAULT, MX_QUANT_STATIC_GLOBAL, MX_QUANT_SCALE_FLOOR = 0, 1, 2
 MX_OP_QUANTIZE, MX_OP_GEMM, MX_OP_MOE_ROUTE = 0, 1, 2
-MX_GEMM_F8F6F4_MATRIX_CORES = 1
+MX_GEMM_F8F6F4_MATRIX_CORES, MX_GEMM_FUSED_QUANTIZE = 1, 2
 STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_ALIGN", -4: "MX_ERR_DTYPE",
           -5: "MX_ERR_UNSUPPORTED", -6: "MX_ERR_HIP", -7: "MX_ERR_WORKSPACE", -8: "MX_ERR_FORMAT"}
 _FMT = {"mxfp4": MX_FMT_MXFP4, "nvfp4": MX_FMT_NVFP4, "mxfp8_e4m3": MX_FMT_MXFP8_E4M3,
@@ -248,13 +248,15 @@ def mx_dequantize(t: MXTensor, dtype=None, out=None):
 
 
 def mx_gemm(a, b: MXTensor, N: int | None = None, out_dtype=None, out=None, groups: int = 0, offsets=None,
-            a_codes_out=None, a_scales_out=None, workspace=None, f8f6f4_matrix_cores: bool = False):
+            a_codes_out=None, a_scales_out=None, workspace=None, f8f6f4_matrix_cores: bool = False,
+            fused_quantize: bool = False):
     """C[M, N] = A . B^T.  a is an MXTensor (W4A4) or a raw fp32/bf16 tensor
     (dynamic MXFP4 quantization inside the call).  Grouped: b holds `groups`
     stacked [N, K] matrices and offsets is an int32 CUDA tensor [groups+1].
     f8f6f4_matrix_cores: MX pairs with an FP8/FP6 operand run on the
     block-scaled matrix cores (faster, products truncated) instead of the
-    exact route."""
+    exact route.  fused_quantize: a raw A is quantized inside one persistent
+    kernel that also multiplies, instead of in a launch of its own first."""
     import torch
     out_dtype = out_dtype or torch.bfloat16
     if isinstance(a, MXTensor):
@@ -288,7 +290,8 @@ def mx_gemm(a, b: MXTensor, N: int | None = None, out_dtype=None, out=None, grou
     assert out.dim() == 2 and out.stride(1) == 1, "rows of out must be contiguous"
     args.c = out.data_ptr()
     args.c_dtype = _dt(out)
-    args.flags = MX_GEMM_F8F6F4_MATRIX_CORES if f8f6f4_matrix_cores else 0
+    args.flags = ((MX_GEMM_F8F6F4_MATRIX_CORES if f8f6f4_matrix_cores else 0) |
+                  (MX_GEMM_FUSED_QUANTIZE if fused_quantize else 0))
     args.ldc = out.stride(0)
     need = mx_workspace_bytes(MX_OP_GEMM, args)
     if need and workspace is None:

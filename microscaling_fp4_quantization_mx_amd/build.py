@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libmx.so")
 # a library of their own so that libmx exports only the C ABI of include/mx.h.
 CEILING_SRC = "ceiling.hip"
 CEILING_LIB = os.path.join(PKG, "libmx_ceiling.so")
-SOURCES = ["quantize.hip", "quantize_variant.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemm_mxw.hip", "gemv.hip", "moe.hip",
+SOURCES = ["quantize.hip", "quantize_variant.hip", "gemm_mxfp4.hip", "gemm_nvfp4.hip", "gemm_mxw.hip", "gemm_fused.hip", "gemv.hip", "moe.hip",
            "norm_quant.hip", "noalloc.hip", "mx_api.cpp"]
 ARCH = "gfx950"
 

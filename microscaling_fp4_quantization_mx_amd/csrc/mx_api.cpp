@@ -1,6 +1,7 @@
 // libmx C ABI: argument validation, workspace layout and kernel dispatch.
 // Every check runs on the host before any HIP call, so an invalid call
 // returns a negative status without touching the device.
+#include <mutex>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -68,6 +69,28 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HI
 
 size_t dyn_a_bytes(int64_t M, int64_t K) { return round256((size_t)(M * K / 2)) + round256((size_t)(M * K / 32)); }
 
+// The fused quantize + GEMM kernel splits its tiles over the 8 XCDs of a
+// 256-CU part (32 workgroups each).
+constexpr int kFusedCUs = 256;
+int device_cus() {
+  static std::mutex mu;
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cus[dev] && hipDeviceGetAttribute(&cus[dev], hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus[dev] = -1;
+  return cus[dev];
+}
+// Dynamic MXFP4 A with MX_GEMM_FUSED_QUANTIZE, of a shape the fused kernel
+// takes (the workspace reserves its counters and partial tiles whenever this
+// holds).
+bool fused_shape(const mx_gemm_args* a) {
+  return !a->a && (a->flags & MX_GEMM_FUSED_QUANTIZE) && a->b && a->b->fmt == MX_FMT_MXFP4 && (a->a_raw_dtype == MX_DT_F32 || a->a_raw_dtype == MX_DT_BF16) &&
+         a->M > 0 && a->N > 0 && a->K > 0 && a->lda_raw < (int64_t(1) << 24) &&   // 32-bit offsets over 32 rows
+         mxk::fused_fits(a->M, a->N, a->K, a->groups, kFusedCUs / 8);
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -100,8 +123,10 @@ size_t mx_workspace_bytes(int32_t op, const void* desc, int32_t flags) {
   }
   if (op == MX_OP_GEMM) {
     const mx_gemm_args* a = static_cast<const mx_gemm_args*>(desc);
-    if (!a->a && !(a->a_codes_out && a->a_scales_out) && a->M > 0 && a->K > 0) return dyn_a_bytes(a->M, a->K);
-    return 0;
+    size_t n = 0;
+    if (!a->a && !(a->a_codes_out && a->a_scales_out) && a->M > 0 && a->K > 0) n = dyn_a_bytes(a->M, a->K);
+    if (fused_shape(a)) n += round256(mxk::fused_workspace_bytes());
+    return n;
   }
   if (op == MX_OP_MOE_ROUTE) {
     const int32_t experts = *static_cast<const int32_t*>(desc);
@@ -205,7 +230,7 @@ int mx_dequantize(const mx_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, v
 
 int mx_gemm(const mx_gemm_args* a, void* stream) {
   if (!a) return MX_ERR_NULL;
-  if (a->flags & ~MX_GEMM_F8F6F4_MATRIX_CORES) return MX_ERR_SHAPE;
+  if (a->flags & ~(MX_GEMM_F8F6F4_MATRIX_CORES | MX_GEMM_FUSED_QUANTIZE)) return MX_ERR_SHAPE;
   if (a->M < 0 || a->N < 0 || a->K < 0 || a->M > kMaxDim || a->N > kMaxDim || a->K > kMaxDim) return MX_ERR_SHAPE;
   if (a->groups < 0) return MX_ERR_SHAPE;
   int st = check_tensor(a->b);
@@ -268,15 +293,26 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
     if (st) return st;
     if (a->M > kMaxElems / (a->K > 0 ? a->K : 1)) return MX_ERR_SHAPE;
     dynamic = true;
+    // the fused kernel's counters and partial tiles lead the workspace
+    const size_t fused_ws = fused_shape(a) ? round256(mxk::fused_workspace_bytes()) : 0;
     if (a->a_codes_out || a->a_scales_out) {
       if (!a->a_codes_out || !a->a_scales_out) return MX_ERR_NULL;
       if (!al16(a->a_codes_out) || !al16(a->a_scales_out)) return MX_ERR_ALIGN;
       a_codes = a->a_codes_out; a_scales = a->a_scales_out;
+      if (fused_ws && (!a->workspace || a->workspace_bytes < fused_ws || !al16(a->workspace))) return MX_ERR_WORKSPACE;
     } else if (a->M > 0 && a->K > 0) {
-      const size_t need = dyn_a_bytes(a->M, a->K);
+      const size_t need = fused_ws + dyn_a_bytes(a->M, a->K);
       if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace)) return MX_ERR_WORKSPACE;
-      a_codes = static_cast<const uint8_t*>(a->workspace);
-      a_scales = static_cast<const uint8_t*>(a->workspace) + round256((size_t)(a->M * a->K / 2));
+      a_codes = static_cast<const uint8_t*>(a->workspace) + fused_ws;
+      a_scales = a_codes + round256((size_t)(a->M * a->K / 2));
+    }
+    if (fused_ws && a->M > 0 && a->N > 0 && device_cus() == kFusedCUs) {
+      if (a->K > (int64_t(1) << 23)) return MX_ERR_UNSUPPORTED;
+      return hip_status(mxk::launch_gemm_mx_fused(a->a_raw, a->a_raw_dtype == MX_DT_BF16, a->lda_raw,
+                                                  const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales),
+                                                  a->b->codes, a->b->scales, a->c, a->c_dtype == MX_DT_BF16, a->ldc,
+                                                  a->M, a->N, a->K, a->groups, a->group_offsets, a->workspace,
+                                                  kFusedCUs / 8, as_stream(stream)));
     }
   }
   if (fmt == MX_FMT_NVFP4 && a->K % 32 != 0) return MX_ERR_UNSUPPORTED;

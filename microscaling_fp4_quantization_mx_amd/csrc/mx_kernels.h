@@ -22,6 +22,16 @@ hipError_t launch_dequant(bool nv, const uint8_t* codes, const uint8_t* scales, 
 hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                           const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
                           int groups, const int32_t* offsets, hipStream_t st);
+// Dynamic MXFP4 quantization fused with the (grouped) GEMM (gemm_fused.hip):
+// one persistent launch (after a one-workgroup counter reset) for K % 512 == 0
+// on a 256-CU device; the workspace holds fused_workspace_bytes() of counters
+// and split partial tiles.
+bool fused_fits(int64_t M, int64_t N, int64_t K, int groups, int wpl);
+size_t fused_workspace_bytes();
+hipError_t launch_gemm_mx_fused(const void* x, int x_bf16, int64_t ldx, uint8_t* a_codes, uint8_t* a_scales,
+                                const uint8_t* b_codes, const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc,
+                                int64_t M, int64_t N, int64_t K, int groups, const int32_t* offsets, void* ws,
+                                int wpl, hipStream_t st);
 hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_global, void* c, int c_bf16,
                           int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st);

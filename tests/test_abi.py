@@ -121,7 +121,7 @@ def test_gemm_validation():
     assert call_gemm(gemm_args(ldc=10)) == -2
     assert call_gemm(gemm_args(c_dtype=9)) == -4
     assert call_gemm(gemm_args(M=-1)) == -2
-    assert call_gemm(gemm_args(flags=2)) == -2                                  # unknown flag bit
+    assert call_gemm(gemm_args(flags=4)) == -2                                  # unknown flag bit
     bad = gemm_args()
     bad.b.contents.cols = 128                                 # K mismatch
     assert call_gemm(bad) == -2

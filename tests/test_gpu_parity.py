@@ -408,6 +408,90 @@ def test_grouped_dynamic_gemm(offs, xdt, nk):
     assert np.array_equal(host(y2.float()), y)
 
 
+# Dynamic quantization fused with the GEMM (K % 512 == 0): one persistent
+# kernel per call whose tiles are cut into eight per-XCD chunks; a chunk's
+# tail tiles are split along K into S parts whose fp32 partial tiles the last
+# part to arrive adds.  The shapes cover every part count the chunking gives:
+# all tiles split in 4 (A), dense and split in 2 (B), no split with one-row
+# experts (C), one tile split in 8 (D), whole tiles plus split tails (E),
+# whole-tile chunks beside a split-only chunk (F); chunks that start inside a
+# tile row quantize that row too (identical bytes).
+FUSED = [
+    ("A", 2000, 1000, 2048, [0, 300, 300, 1100, 2000], torch.bfloat16),
+    ("B", 600, 520, 1024, None, torch.float32),
+    ("C", 3000, 4096, 512, [0, 1, 2, 2999, 3000], torch.bfloat16),
+    ("D", 40, 300, 4608, [0, 40], torch.float32),
+    ("E", 4700, 4096, 1024, [0, 1500, 1500, 3100, 4700], torch.bfloat16),
+    ("F", 3333, 2500, 1536, [0, 1000, 2100, 3333], torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+def test_fused_dynamic_gemm(case):
+    name, M, N, K, offs, xdt = case
+    G = len(offs) - 1 if offs else 1
+    announce(f"fused dynamic gemm {name}: M={M} N={N} K={K} offsets={offs} x={xdt}")
+    rng = np.random.default_rng(M + N + K)
+    x = rng.standard_normal((M, K)).astype(np.float32)
+    x[:, 5] *= 30
+    x[M // 3, :] = 0.0
+    if xdt == torch.bfloat16:
+        x = bf16_values(x)
+    w = (rng.standard_normal((G, N, K)) * 0.02).astype(np.float32)
+    wq = mx_quant_gpu(w.reshape(G * N, K), torch.float32)
+    wc = host(wq.codes).reshape(G, N, K // 2)
+    ws = host(wq.scales).reshape(G, N, K // 32)
+    o = np.array(offs if offs else [0, M])
+    yref, ac, as_ = O.grouped_gemm(x, o, wc, ws)
+    # activations with a row pitch beyond K, C with a row pitch beyond N
+    xt = torch.zeros(M, K + 64, dtype=xdt, device=DEV)
+    xt[:, :K] = dev(x, xdt)
+    xin = xt[:, :K]
+    cbuf = torch.full((M, N + 8), -7.0, dtype=torch.bfloat16, device=DEV)
+    out = cbuf[:, :N]
+    kw = dict(groups=G, offsets=torch.tensor(offs, dtype=torch.int32, device=DEV)) if offs else {}
+    acodes = torch.empty(M, K // 2, dtype=torch.uint8, device=DEV)
+    ascales = torch.empty(M, K // 32, dtype=torch.uint8, device=DEV)
+    mx.mx_gemm(xin, wq, N=N, out=out, a_codes_out=acodes, a_scales_out=ascales, fused_quantize=True, **kw)
+    assert np.array_equal(host(acodes), ac) and np.array_equal(host(ascales), as_), "activation codes"
+    y = host(out.float())
+    assert np.all(host(cbuf[:, N:].float()) == -7.0), "write beyond N"
+    tol = np.zeros_like(yref, dtype=np.float64)
+    for g in range(G):
+        r0, r1 = int(o[g]), int(o[g + 1])
+        if r1 > r0:
+            ah = O.dequantize("mxfp4", ac[r0:r1], as_[r0:r1])
+            bh = O.dequantize("mxfp4", wc[g], ws[g])
+            tol[r0:r1] = O.gemm_tolerance(ah, bh, yref[r0:r1], out="bf16")
+    assert_within(y, yref, tol, f"fused {name}")
+    # through the workspace (no side outputs), twice: identical results
+    for _ in range(2):
+        y2 = mx.mx_gemm(xin, wq, N=N, fused_quantize=True, **kw)
+        assert np.array_equal(host(y2.float()), y), "repeat differs"
+    # the two-launch form (quantize, then the one-tile-per-workgroup GEMM)
+    y3 = host(mx.mx_gemm(xin, wq, N=N, **kw).float())
+    assert_within(y3, yref, tol, f"two launches {name}")
+
+
+def test_fused_quantize_exhaustive_bf16_sweep():
+    """The fused kernel's own quantizer (packed-bf16 conversion for bf16
+    input) on every finite bf16 bit pattern, alone in a block and in an
+    anchored block: the side-output codes and scale bytes are the oracle's."""
+    x = exhaustive_bf16_blocks()
+    x = x[np.abs(x).max(axis=1) <= 1.5 * 2.0 ** 127]
+    x = x[: x.shape[0] // 8 * 8].reshape(-1, 512)             # K = 512: the fused path
+    rc, rs = O.mxfp4_quantize(x)
+    w = mx_quant_gpu(np.full((8, 512), 0.25, np.float32), torch.float32)
+    for dtype in (torch.bfloat16, torch.float32):
+        announce(f"fused quantizer exhaustive bf16 sweep rows={x.shape[0]} dtype={dtype}")
+        acodes = torch.empty(x.shape[0], 256, dtype=torch.uint8, device=DEV)
+        ascales = torch.empty(x.shape[0], 16, dtype=torch.uint8, device=DEV)
+        mx.mx_gemm(dev(x, dtype), w, N=8, out_dtype=torch.float32, a_codes_out=acodes, a_scales_out=ascales,
+                   fused_quantize=True)
+        assert np.array_equal(host(ascales), rs)
+        assert np.array_equal(host(acodes), rc)
+
+
 # --------------------------------------------------------------------- GEMV
 @pytest.mark.parametrize("M", [1, 3, 4, 5, 8, 12, 16])
 @pytest.mark.parametrize("NK", [(300, 4096), (64, 96), (17, 8192), (40, 768)])
@@ -553,25 +637,51 @@ def test_full_nvfp4_gemm_2048x28672x8192():
     full_gemm_check(y, O.dequantize("nvfp4", ra, rsa, ga), O.dequantize("nvfp4", rb, rsb, gb), "full nvfp4 gemm")
 
 
-def test_full_grouped_dynamic_gemm():
-    d = W.make(W.C5)
-    announce("full fused dynamic-quantize grouped GEMM 8x4096x14336, 8192 tokens")
+_C5REF = {}
+
+
+def c5_reference():
+    """Oracle codes of the grouped workload's tokens and expert weights and the
+    fp64-accumulated outputs with their tolerances (computed once per
+    session, shared by both forms of the call)."""
+    if not _C5REF:
+        d = W.make(W.C5)
+        G, N = 8, 4096
+        ra, rsa = oracle_rows(O.mxfp4_quantize, d["x"])
+        offs = d["offsets"]
+        yref = np.zeros((8192, N), np.float32)
+        tol = np.zeros((8192, N), np.float64)
+        wcodes = []
+        for g in range(G):
+            rb, rsb = oracle_rows(O.mxfp4_quantize, d["w"][g])
+            wcodes.append((rb, rsb))
+            r0, r1 = int(offs[g]), int(offs[g + 1])
+            bh = O.dequantize("mxfp4", rb, rsb)
+            for q0 in range(r0, r1, 2048):
+                q1 = min(r1, q0 + 2048)
+                ah = O.dequantize("mxfp4", ra[q0:q1], rsa[q0:q1])
+                yref[q0:q1] = O.gemm(ah, bh, out="bf16")
+                tol[q0:q1] = O.gemm_tolerance(ah, bh, yref[q0:q1], out="bf16")
+        _C5REF.update(d=d, ra=ra, rsa=rsa, w=wcodes, yref=yref, tol=tol)
+    return _C5REF
+
+
+@pytest.mark.parametrize("fused", [False, True], ids=["two_launches", "fused_kernel"])
+def test_full_grouped_dynamic_gemm(fused):
+    ref = c5_reference()
+    d = ref["d"]
+    announce(f"full dynamic-quantize grouped GEMM 8x4096x14336, 8192 tokens, fused={fused}")
     G, N, K = 8, 4096, 14336
     wq = mx_quant_gpu(d["w"].reshape(G * N, K), torch.float32)
-    offs = d["offsets"]
-    offsets = torch.from_numpy(offs).to(DEV)
+    offsets = torch.from_numpy(d["offsets"]).to(DEV)
     acodes = torch.empty(8192, K // 2, dtype=torch.uint8, device=DEV)
     ascales = torch.empty(8192, K // 32, dtype=torch.uint8, device=DEV)
     y = mx.mx_gemm(dev(d["x"], torch.bfloat16), wq, N=N, out_dtype=torch.bfloat16, groups=G, offsets=offsets,
-                   a_codes_out=acodes, a_scales_out=ascales)
+                   a_codes_out=acodes, a_scales_out=ascales, fused_quantize=fused)
     yh = host(y.float())
-    ra, rsa = oracle_rows(O.mxfp4_quantize, d["x"])
-    assert_codes(host(acodes), host(ascales), ra, rsa, "tokens 8192x14336 bf16 (quantized inside the call)")
+    assert_codes(host(acodes), host(ascales), ref["ra"], ref["rsa"], "tokens 8192x14336 bf16 (quantized inside the call)")
     wch, wsh = host(wq.codes), host(wq.scales)
-    del wq
     for g in range(G):
-        rb, rsb = oracle_rows(O.mxfp4_quantize, d["w"][g])
+        rb, rsb = ref["w"][g]
         assert_codes(wch[g * N:(g + 1) * N], wsh[g * N:(g + 1) * N], rb, rsb, f"expert {g} weights 4096x14336")
-        r0, r1 = int(offs[g]), int(offs[g + 1])
-        full_gemm_check(yh[r0:r1], O.dequantize("mxfp4", ra[r0:r1], rsa[r0:r1]), O.dequantize("mxfp4", rb, rsb),
-                        f"grouped expert {g} ({r1 - r0} rows)")
+    assert_within(yh, ref["yref"], ref["tol"], f"grouped 8x4096x14336 all {yh.size} outputs (fused={fused})")
