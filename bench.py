@@ -63,6 +63,12 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
+# counter summary of the quantize kernels (X and W of the main step share one
+# grid size, so the figure is their mean over the dispatches of that grid)
+QSUM = "quantize_counters.txt"
+QFILES = ["quantize.hip", "nv_codes.h", "mx_device.h"]
+
+
 def kernel_counter(name, kernel_files, kernel, grid, field):
     """A derived figure (field, e.g. "mfma_busy_frac") of one kernel and grid
     from a committed summary written by --summarize-pmc, if it was taken on
@@ -77,8 +83,11 @@ def kernel_counter(name, kernel_files, kernel, grid, field):
             kv[k.strip()] = v.strip()
     if kv.get("source_hash") != source_hash(kernel_files):
         return None
+    # kernel: a name ("k_gemm_mx_k256": any instantiation) or a name with the
+    # start of its template arguments ("k_quant_mx<float")
+    prefixes = (f"mxk::{kernel}",) if "<" in kernel else (f"mxk::{kernel}<", f"mxk::{kernel}@")
     for k, v in kv.items():
-        if k.startswith(f"mxk::{kernel}<") and k.endswith(f"@{grid}.{field}"):
+        if k.startswith(prefixes) and k.endswith(f"@{grid}.{field}"):
             return float(v)
     return None
 
@@ -94,7 +103,8 @@ def summarize_trace(dirs, out_path, title, command):
     for dd in dirs:
         for f in glob.glob(os.path.join(dd, "**", "*kernel_trace.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                k = (r["Kernel_Name"].split("(")[0].replace("void ", ""), r["Grid_Size"])
+                grid = r["Grid_Size"] if "Grid_Size" in r else r["Grid_Size_X"]
+                k = (r["Kernel_Name"].split("(")[0].replace("void ", ""), grid)
                 d[k].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
     lines = [f"# {title}", "# Command (repository root, TMPDIR=/tmp, one MI355X):"]
     lines += [f"#   {c}" for c in command]
@@ -211,7 +221,7 @@ def bench_main(args, torch, mx, W):
     qw_bytes = N * K * 4 + N * K // 2 + N * K // 32
     gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * 2
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
-    gfiles = ["gemm_mxfp4.hip", "mx_device.h"]
+    gfiles = ["gemm_mxfp4.hip", "gemm_mx_tile.h", "mx_device.h"]
     gsum = "mxfp4_gemm_4096x8192x8192_counters.txt"
     traffic = kernel_counter(gsum, gfiles, "k_gemm_mx_k256", 131072, "hbm_bytes")
     res = {
@@ -226,9 +236,12 @@ def bench_main(args, torch, mx, W):
                      "counters": f"profiles/{gsum}"},
         "kernels": {
             "quantize_x": {"avg_ms": qx_ms, "GB/s": qx_bytes / (qx_ms * 1e-3) / 1e9, "bytes": qx_bytes,
-                           "frac_hbm": qx_bytes / (qx_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                           "frac_hbm": qx_bytes / (qx_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "traffic_mean_x_and_w": kernel_counter(QSUM, QFILES, "k_quant_mx<float", 1048576, "hbm_bytes"),
+                           "counters": f"profiles/{QSUM}"},
             "quantize_w": {"avg_ms": qw_ms, "GB/s": qw_bytes / (qw_ms * 1e-3) / 1e9, "bytes": qw_bytes,
-                           "frac_hbm": qw_bytes / (qw_ms * 1e-3) / 1e9 / PEAK_HBM_GBS},
+                           "frac_hbm": qw_bytes / (qw_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                           "counters": f"profiles/{QSUM}"},
             "gemm": {"avg_ms": g_ms, "TFLOPS": gemm_tflops, "bytes": gemm_bytes},
         },
     }
