@@ -120,6 +120,10 @@ enum {
      of a quantize launch followed by the GEMM (see mx_gemm). */
   MX_GEMM_FUSED_QUANTIZE = 2
 };
+/* Bits 4-7 of mx_gemm_args.flags: the element format a dynamic A is
+   quantized to (MX_FMT_MXFP4, MX_FMT_MXFP8_* or MX_FMT_MXFP6_*); without it
+   A takes the format of B. */
+#define MX_GEMM_DYNAMIC_A_FORMAT(fmt) ((int32_t)(((fmt) + 1) << 4))
 
 /* mx_workspace_bytes operations */
 enum { MX_OP_QUANTIZE = 0, MX_OP_GEMM = 1, MX_OP_MOE_ROUTE = 2 };
@@ -216,11 +220,16 @@ int mx_dequantize(const mx_tensor *in, void *y, int32_t y_dtype, int64_t ld_y, v
  * `group_offsets` is a device int32 array of groups + 1 non-decreasing
  * entries with off[0] = 0 and off[groups] = M (entries are clamped to [0, M]
  * on the device, so malformed offsets cannot index out of bounds).
- * Dynamic activation quantization (MXFP4 only): pass a == NULL and
- * a_raw (bf16/fp32 [M, K], pitch lda_raw elements); A is quantized to MXFP4
- * once (as mx_quantize would) into a_codes_out/a_scales_out if given, else
- * into the workspace, then multiplied: a quantize launch, then the GEMM.
- * With flags MX_GEMM_FUSED_QUANTIZE (K % 512 == 0, lda_raw < 2^24, a
+ * Dynamic activation quantization: pass a == NULL and a_raw (bf16/fp32
+ * [M, K], pitch lda_raw elements, K % 32 == 0); A is quantized once (as
+ * mx_quantize would) to the format of B, or to the MX format that
+ * MX_GEMM_DYNAMIC_A_FORMAT(fmt) in flags names (e.g. MXFP8 E4M3 activations
+ * against MXFP4 weights), into a_codes_out [M, K*b/8] / a_scales_out
+ * [M, K/32] if given, else into the workspace, then multiplied: a quantize
+ * launch, then the GEMM.  Not for NVFP4 B (MX_ERR_UNSUPPORTED); a format
+ * outside the five MX formats, or one given while a != NULL, is
+ * MX_ERR_FORMAT.
+ * With flags MX_GEMM_FUSED_QUANTIZE (MXFP4 A and B, K % 512 == 0, lda_raw < 2^24, a
  * 256-CU device; otherwise the two launches run) one persistent kernel does
  * both, XCD by XCD: each XCD's workgroups quantize the rows of their share
  * of the output tiles, then multiply them, the last round of tiles split
@@ -246,10 +255,10 @@ int mx_dequantize(const mx_tensor *in, void *y, int32_t y_dtype, int64_t ld_y, v
  * truncate each product of a group of 8 consecutive K to 13
  * bits below the largest product of the group (measured on gfx950): per
  * output the error grows by at most 8 * 2^(L_g - 12) per group g, L_g the
- * binary exponent of that largest product;
- * dense, pre-quantized A only (MX_ERR_UNSUPPORTED for grouped or dynamic
- * calls), padded K % 128 == 0 and K <= 2^22 (else MX_ERR_UNSUPPORTED).  NVFP4
- * pairs only with NVFP4 (else MX_ERR_FORMAT).  Pre-quantized MX operands
+ * binary exponent of that largest product.  These pairs take the grouped
+ * form and a dynamic A too; padded K % 128 == 0 and K <= 2^22 (else
+ * MX_ERR_UNSUPPORTED).  NVFP4 pairs only with NVFP4 (else MX_ERR_FORMAT) and
+ * has no grouped form (MX_ERR_UNSUPPORTED).  Pre-quantized MX operands
  * with K % 32 != 0 (zero-padded rows) multiply over the padded length, which
  * gives the same product.  MXFP4_K16 and FP4_TENSOR operands are not
  * provided (MX_ERR_UNSUPPORTED: their scales do not map onto the matrix
@@ -268,7 +277,7 @@ typedef struct mx_gemm_args {
   int32_t c_dtype;
   int32_t flags;                 /* MX_GEMM_* bits, or 0                    */
   int64_t ldc;                   /* elements                                */
-  uint8_t *a_codes_out;          /* optional [M, K/2] (dynamic path)        */
+  uint8_t *a_codes_out;          /* optional [M, K*b/8] (dynamic path)      */
   uint8_t *a_scales_out;         /* optional [M, K/32] (dynamic path)       */
   void *workspace;
   size_t workspace_bytes;
@@ -283,13 +292,17 @@ int mx_gemm(const mx_gemm_args *args, void *stream);
  * fp32 accumulation ("Extreme Quantization and Precision Engineering", section
  * "Key points", W4A16).  Every weight is expanded on chip to the exact bf16
  * value q * 2^e, so each product is exact and only the fp32 summation order
- * varies.  Which unit takes the products:
+ * varies.  Which unit takes the products (MXFP4 weights):
  *   M <= 3, or any M when K % 256 != 0: the vector ALU (v_dot2_f32_bf16);
  *     no matrix cores;
  *   4 <= M <= 16 with K % 256 == 0: the bf16 matrix cores
  *     (v_mfma_f32_16x16x32_bf16, activation rows zero-padded to 16), because
  *     one dot2 per weight pair and activation row makes the vector ALU, not
  *     the weight stream, the bound from M = 4 on.
+ * MXFP8 (E4M3 / E5M2) and MXFP6 (E2M3 / E3M2) weights (W8A16, W6A16) are
+ * expanded the same way (exact: at most 4 significant bits, in bf16's normal
+ * range for every tensor the quantizer writes) and take the vector ALU for
+ * every M.  A scale byte 0 gives a zero block.
  * 1 <= M <= 16; x bf16 [M, K] pitch ld_x; y bf16 [M, N] pitch ld_y.
  * Requires K % 32 == 0.
  */

@@ -21,6 +21,7 @@ __all__ = [
     "moe_forward", "mx_rmsnorm_quantize", "MX_FMT_MXFP8_E4M3", "MX_FMT_MXFP8_E5M2", "MX_FMT_MXFP6_E2M3",
     "MX_FMT_MXFP6_E3M2", "element_bits", "MX_FMT_MXFP4_K16", "MX_FMT_FP4_TENSOR", "MX_QUANT_SCALE_FLOOR",
     "padded_cols", "mx_quantize_noalloc", "MX_GEMM_F8F6F4_MATRIX_CORES", "MX_GEMM_FUSED_QUANTIZE",
+    "MX_GEMM_DYNAMIC_A_FORMAT",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -33,6 +34,13 @@ MX_DT_F32, MX_DT_BF16 = 0, 1
 MX_QUANT_DEFAULT, MX_QUANT_STATIC_GLOBAL, MX_QUANT_SCALE_FLOOR = 0, 1, 2
 MX_OP_QUANTIZE, MX_OP_GEMM, MX_OP_MOE_ROUTE = 0, 1, 2
 MX_GEMM_F8F6F4_MATRIX_CORES, MX_GEMM_FUSED_QUANTIZE = 1, 2
+
+
+def MX_GEMM_DYNAMIC_A_FORMAT(fmt: int) -> int:
+    """mx_gemm flag bits naming the format a dynamic A is quantized to."""
+    return (fmt + 1) << 4
+
+
 STATUS = {0: "MX_OK", -1: "MX_ERR_NULL", -2: "MX_ERR_SHAPE", -3: "MX_ERR_ALIGN", -4: "MX_ERR_DTYPE",
           -5: "MX_ERR_UNSUPPORTED", -6: "MX_ERR_HIP", -7: "MX_ERR_WORKSPACE", -8: "MX_ERR_FORMAT"}
 _FMT = {"mxfp4": MX_FMT_MXFP4, "nvfp4": MX_FMT_NVFP4, "mxfp8_e4m3": MX_FMT_MXFP8_E4M3,
@@ -249,10 +257,11 @@ def mx_dequantize(t: MXTensor, dtype=None, out=None):
 
 def mx_gemm(a, b: MXTensor, N: int | None = None, out_dtype=None, out=None, groups: int = 0, offsets=None,
             a_codes_out=None, a_scales_out=None, workspace=None, f8f6f4_matrix_cores: bool = False,
-            fused_quantize: bool = False):
+            fused_quantize: bool = False, a_format=None):
     """C[M, N] = A . B^T.  a is an MXTensor (W4A4) or a raw fp32/bf16 tensor
-    (dynamic MXFP4 quantization inside the call).  Grouped: b holds `groups`
-    stacked [N, K] matrices and offsets is an int32 CUDA tensor [groups+1].
+    (dynamic quantization inside the call, to b's format or to `a_format`,
+    e.g. "mxfp8_e4m3").  Grouped: b holds `groups` stacked [N, K] matrices
+    and offsets is an int32 CUDA tensor [groups+1].
     f8f6f4_matrix_cores: MX pairs with an FP8/FP6 operand run on the
     block-scaled matrix cores (faster, products truncated) instead of the
     exact route.  fused_quantize: a raw A is quantized inside one persistent
@@ -292,6 +301,8 @@ def mx_gemm(a, b: MXTensor, N: int | None = None, out_dtype=None, out=None, grou
     args.c_dtype = _dt(out)
     args.flags = ((MX_GEMM_F8F6F4_MATRIX_CORES if f8f6f4_matrix_cores else 0) |
                   (MX_GEMM_FUSED_QUANTIZE if fused_quantize else 0))
+    if a_format is not None:
+        args.flags |= MX_GEMM_DYNAMIC_A_FORMAT(_FMT[a_format] if isinstance(a_format, str) else a_format)
     args.ldc = out.stride(0)
     need = mx_workspace_bytes(MX_OP_GEMM, args)
     if need and workspace is None:
@@ -304,7 +315,8 @@ def mx_gemm(a, b: MXTensor, N: int | None = None, out_dtype=None, out=None, grou
 
 
 def mx_gemv(x, w: MXTensor, out=None):
-    """W4A16: y[M, N] = x[M, K] (bf16) . dequant(w)[N, K]^T, bf16 out, M <= 16."""
+    """W4A16 (W8A16 / W6A16 for MXFP8 / MXFP6 weights): y[M, N] =
+    x[M, K] (bf16) . dequant(w)[N, K]^T, bf16 out, M <= 16."""
     import torch
     M, K = x.shape
     if out is None:

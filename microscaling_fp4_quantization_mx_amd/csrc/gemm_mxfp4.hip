@@ -18,15 +18,12 @@
 // fragment reads of 8 or 16 consecutive rows hit distinct LDS banks.
 //
 // Grouped (mixture-of-experts) form: row ranges [off[g], off[g+1]) of A use
-// the g-th [N, K] matrix of B; tiles never straddle groups.
-//
-// Workgroup -> tile mapping is XCD-aware: consecutive workgroup ids go to
-// different XCDs round-robin, so id i is remapped to logical tile
-// (i % 8) * ceil(T/8) + i / 8 and each XCD walks a contiguous range of tiles,
-// rasterized in groups of GROUP_M tile rows so that concurrently running
-// tiles on one XCD share A and B panels in that XCD's L2.
+// the g-th [N, K] matrix of B; tiles never straddle groups.  The
+// workgroup -> tile mapping (XCD-aware, GROUP_M tile rows at a time) is
+// gemm_tiles.h's.
 #include "mx_device.h"
 #include "gemm_mx_tile.h"
+#include "gemm_tiles.h"
 #include "mx_kernels.h"
 
 namespace mxk {
@@ -70,48 +67,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx(MxGemmPa
   const int wy = wave / NWX, wx = wave % NWX;
 
   // ---- tile selection
-  const int tn_count = (p.N + BN - 1) / BN;
-  int g = 0, m_begin = 0, m_end = p.M, tm, tn;
-  {
-    int total;
-    if (p.groups == 0) {
-      total = ((p.M + BM - 1) / BM) * tn_count;
-    } else {
-      total = 0;
-      for (int i = 0; i < p.groups; ++i) {
-        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
-        int rows = o1 > o0 ? o1 - o0 : 0;
-        total += ((rows + BM - 1) / BM) * tn_count;
-      }
-    }
-    const int per_xcd = (total + 7) / 8;
-    const int bid = blockIdx.x;
-    const int local = bid / 8;
-    if (local >= per_xcd) return;
-    const int t = (bid % 8) * per_xcd + local;
-    if (t >= total) return;
-    int tl = t;  // tile index within its group
-    if (p.groups != 0) {
-      for (int i = 0; i < p.groups; ++i) {
-        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
-        int rows = o1 > o0 ? o1 - o0 : 0;
-        int nt = ((rows + BM - 1) / BM) * tn_count;
-        if (tl < nt) { g = i; m_begin = o0; m_end = o1; break; }
-        tl -= nt;
-      }
-    }
-    const int tm_count = (m_end - m_begin + BM - 1) / BM;
-    // grouped raster: GROUP_M tile rows at a time, walking all tile columns
-    const int per_group = GROUP_M * tn_count;
-    const int grp = tl / per_group;
-    const int first_m = grp * GROUP_M;
-    const int gm = min(tm_count - first_m, GROUP_M);
-    const int in_grp = tl % per_group;
-    tm = first_m + in_grp % gm;
-    tn = in_grp / gm;
-  }
-  const int m0 = m_begin + tm * BM;
-  const int n0 = tn * BN;
+  GemmTile tile;
+  if (!gemm_tile<BM, BN, GROUP_M>(blockIdx.x, p.M, p.N, p.groups, p.offsets, tile)) return;
+  const int g = tile.g, m_end = tile.m_end, m0 = tile.m0, n0 = tile.n0;
   const int KB = p.K / 2;          // bytes per code row
   const int KS = p.K / 32;         // scale bytes per row
   const uint8_t* Ac = p.a_codes;
@@ -282,48 +240,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_ring(MxG
   const int wave = tid >> 6;
   const int wy = wave / NWX, wx = wave % NWX;
 
-  // ---- tile selection (as in the generic kernel)
-  const int tn_count = (p.N + BN - 1) / BN;
-  int g = 0, m_begin = 0, m_end = p.M, tm, tn;
-  {
-    int total;
-    if (p.groups == 0) {
-      total = ((p.M + BM - 1) / BM) * tn_count;
-    } else {
-      total = 0;
-      for (int i = 0; i < p.groups; ++i) {
-        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
-        int rows = o1 > o0 ? o1 - o0 : 0;
-        total += ((rows + BM - 1) / BM) * tn_count;
-      }
-    }
-    const int per_xcd = (total + 7) / 8;
-    const int bid = blockIdx.x;
-    const int local = bid / 8;
-    if (local >= per_xcd) return;
-    const int t = (bid % 8) * per_xcd + local;
-    if (t >= total) return;
-    int tl = t;
-    if (p.groups != 0) {
-      for (int i = 0; i < p.groups; ++i) {
-        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
-        int rows = o1 > o0 ? o1 - o0 : 0;
-        int nt = ((rows + BM - 1) / BM) * tn_count;
-        if (tl < nt) { g = i; m_begin = o0; m_end = o1; break; }
-        tl -= nt;
-      }
-    }
-    const int tm_count = (m_end - m_begin + BM - 1) / BM;
-    const int per_group = GROUP_M * tn_count;
-    const int grp = tl / per_group;
-    const int first_m = grp * GROUP_M;
-    const int gm = min(tm_count - first_m, GROUP_M);
-    const int in_grp = tl % per_group;
-    tm = first_m + in_grp % gm;
-    tn = in_grp / gm;
-  }
-  const int m0 = m_begin + tm * BM;
-  const int n0 = tn * BN;
+  // ---- tile selection
+  GemmTile tile;
+  if (!gemm_tile<BM, BN, GROUP_M>(blockIdx.x, p.M, p.N, p.groups, p.offsets, tile)) return;
+  const int g = tile.g, m_end = tile.m_end, m0 = tile.m0, n0 = tile.n0;
   const int KB = p.K / 2, KS = p.K / 32;
   const int a_rows = min(BM, m_end - m0), b_rows = min(BN, p.N - n0);
 
@@ -547,47 +467,9 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
   static_assert(BM == T::BM && BN == T::BN && WM == T::WM && WN == T::WN, "one tile shape");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::SMEM];
 
-  const int tn_count = (p.N + BN - 1) / BN;
-  int g = 0, m_begin = 0, m_end = p.M, tm, tn;
-  {
-    int total;
-    if (p.groups == 0) {
-      total = ((p.M + BM - 1) / BM) * tn_count;
-    } else {
-      total = 0;
-      for (int i = 0; i < p.groups; ++i) {
-        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
-        int rows = o1 > o0 ? o1 - o0 : 0;
-        total += ((rows + BM - 1) / BM) * tn_count;
-      }
-    }
-    const int per_xcd = (total + 7) / 8;
-    const int bid = blockIdx.x;
-    const int local = bid / 8;
-    if (local >= per_xcd) return;
-    const int t = (bid % 8) * per_xcd + local;
-    if (t >= total) return;
-    int tl = t;
-    if (p.groups != 0) {
-      for (int i = 0; i < p.groups; ++i) {
-        int o0 = min(max(p.offsets[i], 0), p.M), o1 = min(max(p.offsets[i + 1], 0), p.M);
-        int rows = o1 > o0 ? o1 - o0 : 0;
-        int nt = ((rows + BM - 1) / BM) * tn_count;
-        if (tl < nt) { g = i; m_begin = o0; m_end = o1; break; }
-        tl -= nt;
-      }
-    }
-    const int tm_count = (m_end - m_begin + BM - 1) / BM;
-    const int per_group = GROUP_M * tn_count;
-    const int grp = tl / per_group;
-    const int first_m = grp * GROUP_M;
-    const int gm = min(tm_count - first_m, GROUP_M);
-    const int in_grp = tl % per_group;
-    tm = first_m + in_grp % gm;
-    tn = in_grp / gm;
-  }
-  const int m0 = m_begin + tm * BM;
-  const int n0 = tn * BN;
+  GemmTile tile;
+  if (!gemm_tile<BM, BN, GROUP_M>(blockIdx.x, p.M, p.N, p.groups, p.offsets, tile)) return;
+  const int g = tile.g, m_end = tile.m_end, m0 = tile.m0, n0 = tile.n0;
   const MxTileSrc src = mx_tile_src(p.a_codes, p.a_scales, p.b_codes, p.b_scales, p.K, (size_t)m0,
                                     min(BM, m_end - m0), (size_t)g * p.N + n0, min(BN, p.N - n0));
   f32x16 acc[T::TI][T::TJ];
@@ -611,9 +493,7 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
   p.a_codes = a_codes; p.a_scales = a_scales; p.b_codes = b_codes; p.b_scales = b_scales;
   p.c = c; p.ldc = ldc; p.M = (int)M; p.N = (int)N; p.K = (int)K;
   p.groups = groups; p.offsets = offsets; p.c_bf16 = c_bf16;
-  const int64_t tn = (N + GBN - 1) / GBN;
-  const int64_t tm_upper = (M + GBM - 1) / GBM + (groups > 0 ? groups : 0);
-  int64_t tiles = tm_upper * tn;
+  const int64_t tiles = gemm_tile_bound(M, N, GBM, GBN, groups);
   int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   constexpr int NT = (GBM / GWM) * (GBN / GWN) * 64;

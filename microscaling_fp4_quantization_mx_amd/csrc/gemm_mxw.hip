@@ -26,7 +26,12 @@
 // of 8 consecutive rows hit distinct banks.  Two LDS slots: while the two
 // 32x32x64 segments of stage s run, stage s + 1 lands, and the refill for
 // stage s + 2 is issued as soon as every wave holds stage s's fragments.
+//
+// Grouped form: rows [off[g], off[g+1]) of A and C use the g-th stacked
+// [N, K] matrix of B (tiles as in gemm_tiles.h), as for MXFP4.
 #include "mx_device.h"
+#include "gemm_tiles.h"
+#include "mx_expand.h"
 #include "mx_kernels.h"
 
 namespace mxk {
@@ -75,12 +80,14 @@ struct MxwOp {
 struct MxwParams {
   const uint8_t* a_codes;   // [M, K * bitsA / 8]
   const uint8_t* a_scales;  // [M, K / 32]
-  const uint8_t* b_codes;   // [N, K * bitsB / 8]
-  const uint8_t* b_scales;  // [N, K / 32]
+  const uint8_t* b_codes;   // [G * N, K * bitsB / 8] (G = 1 dense)
+  const uint8_t* b_scales;  // [G * N, K / 32]
   void* c;
   int64_t ldc;
   int M, N, K;
   int c_bf16;
+  int groups;               // 0 = dense
+  const int32_t* offsets;   // [groups + 1]
 };
 
 constexpr int MXW_GROUP_M = 4;
@@ -109,32 +116,23 @@ __global__ __launch_bounds__(256) void k_gemm_mxw(MxwParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets stay scalar
   const int wy = wave >> 1, wx = wave & 1;
 
-  // ---- tile: XCD-aware remap (consecutive ids go to different XCDs), then
-  // MXW_GROUP_M tile rows at a time across all tile columns
-  const int tn_count = (p.N + BN - 1) / BN, tm_count = (p.M + BM - 1) / BM;
-  const int total = tn_count * tm_count;
-  const int per_xcd = (total + 7) / 8;
-  const int local = blockIdx.x / 8;
-  if (local >= per_xcd) return;
-  const int t = (blockIdx.x % 8) * per_xcd + local;
-  if (t >= total) return;
-  const int per_group = MXW_GROUP_M * tn_count;
-  const int first_m = (t / per_group) * MXW_GROUP_M;
-  const int gm = min(tm_count - first_m, MXW_GROUP_M);
-  const int tm = first_m + (t % per_group) % gm, tn = (t % per_group) / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
+  // ---- tile (XCD-aware, MXW_GROUP_M tile rows at a time; grouped rows)
+  GemmTile tile;
+  if (!gemm_tile<BM, BN, MXW_GROUP_M>(blockIdx.x, p.M, p.N, p.groups, p.offsets, tile)) return;
+  const int m0 = tile.m0, n0 = tile.n0, m_end = tile.m_end;
   const int KBA = p.K / 8 * OA::BITS, KBB = p.K / 8 * OB::BITS, KS = p.K / 32;
-  const int a_rows = min(BM, p.M - m0), b_rows = min(BN, p.N - n0);
+  const int a_rows = min(BM, m_end - m0), b_rows = min(BN, p.N - n0);
+  const size_t b_row0 = (size_t)tile.g * p.N + n0;
 
   // buffer descriptors over the tile's valid rows: reads beyond return zero
   const __amdgpu_buffer_rsrc_t ra =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_codes + (size_t)m0 * KBA), 0, a_rows * KBA, 0x00020000);
   const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_codes + (size_t)n0 * KBB), 0, b_rows * KBB, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_codes + b_row0 * KBB), 0, b_rows * KBB, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsa =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.a_scales + (size_t)m0 * KS), 0, a_rows * KS, 0x00020000);
   const __amdgpu_buffer_rsrc_t rsb =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + (size_t)n0 * KS), 0, b_rows * KS, 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.b_scales + b_row0 * KS), 0, b_rows * KS, 0x00020000);
 
   // Per-lane source offsets of the direct-to-LDS loads (stage 0).  LDS 16-byte
   // unit q = (wave * DMA + j) * 64 + lane of an operand holds row q / PCH,
@@ -290,7 +288,7 @@ __global__ __launch_bounds__(256) void k_gemm_mxw(MxwParams p) {
       const int lr = 2 * t2 + h;
       const int row = m0 + wy * WM + half * (WM / 2) + lr;
       const f32x4 v = *reinterpret_cast<const f32x4*>(&ep[lr * EP_PITCH + cl]);
-      if (row < p.M) {
+      if (row < m_end) {
         if (p.c_bf16) {
           uint16_t* dst = reinterpret_cast<uint16_t*>(p.c) + (size_t)row * p.ldc + col;
           if (vec_ok && col + 3 < p.N) {
@@ -346,46 +344,6 @@ __device__ __forceinline__ int mxx_swz(int row) { return (row & 7) ^ ((row >> 3)
 __device__ __forceinline__ float mxx_scale(uint32_t e) { return ffrom(min(max(e, 1u), 254u) << 23); }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x32_t __attribute__((ext_vector_type(32)));
-typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
-
-// The 32 codes of one MX block (W dwords: 4 FP4, 6 FP6, 8 FP8) -> 16 dwords of
-// bf16 pairs, element order kept.
-template <int F>
-__device__ __forceinline__ void mxx_expand(const uint32_t* w, float sc, uint32_t (&o)[16]) {
-  if constexpr (F == 4) {                 // E2M1: 8 codes per dword
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      bf16x2 v[4];
-      v[0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], sc, 0);
-      v[1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], sc, 1);
-      v[2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], sc, 2);
-      v[3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], sc, 3);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) __builtin_memcpy(&o[4 * d + q], &v[q], 4);
-    }
-  } else if constexpr (F == 0 || F == 1) {   // E4M3 / E5M2: 4 codes per dword
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      bf16x2 lo, hi;
-      if constexpr (F == 0) {
-        lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], sc, false);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[d], sc, true);
-      } else {
-        lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[d], sc, false);
-        hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w[d], sc, true);
-      }
-      __builtin_memcpy(&o[2 * d], &lo, 4);
-      __builtin_memcpy(&o[2 * d + 1], &hi, 4);
-    }
-  } else {                                    // E2M3 / E3M2: 32 codes in 6 dwords
-    const u32x6 v = {w[0], w[1], w[2], w[3], w[4], w[5]};
-    bf16x32_t r;
-    if constexpr (F == 2) r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_fp6(v, sc);
-    else r = __builtin_amdgcn_cvt_scalef32_pk32_bf16_bf6(v, sc);
-    __builtin_memcpy(&o[0], &r, 64);
-  }
-}
 
 template <int FA, int FB>
 __global__ __launch_bounds__(256) void k_gemm_mxx(MxwParams p) {
@@ -398,24 +356,11 @@ __global__ __launch_bounds__(256) void k_gemm_mxx(MxwParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wy = wave >> 1, wx = wave & 1;
-  const int tn_count = (p.N + BN - 1) / BN, tm_count = (p.M + BM - 1) / BM;
-  int tm, tn;
-  {
-    const int total = tm_count * tn_count;
-    const int per_xcd = (total + 7) / 8;
-    const int local = blockIdx.x / 8;
-    if (local >= per_xcd) return;
-    const int t = (blockIdx.x % 8) * per_xcd + local;
-    if (t >= total) return;
-    const int per_group = MXW_GROUP_M * tn_count;
-    const int grp = t / per_group;
-    const int first_m = grp * MXW_GROUP_M;
-    const int gm = min(tm_count - first_m, MXW_GROUP_M);
-    const int in_grp = t % per_group;
-    tm = first_m + in_grp % gm;
-    tn = in_grp / gm;
-  }
-  const int m0 = tm * BM, n0 = tn * BN;
+  GemmTile tile;
+  if (!gemm_tile<BM, BN, MXW_GROUP_M>(blockIdx.x, p.M, p.N, p.groups, p.offsets, tile)) return;
+  const int m0 = tile.m0, n0 = tile.n0, m_end = tile.m_end;
+  const uint8_t* b_codes = p.b_codes + (size_t)tile.g * p.N * (p.K / 8 * WB);
+  const uint8_t* b_scales = p.b_scales + (size_t)tile.g * p.N * (p.K / 32);
   const int KBA = p.K / 8 * WA, KBB = p.K / 8 * WB, KS = p.K / 32;   // code bytes per row = K * bits / 8
 
   // segment q = tid + i*NT of a stage: row q >> 1, MX block q & 1 of the stage
@@ -424,15 +369,15 @@ __global__ __launch_bounds__(256) void k_gemm_mxx(MxwParams p) {
 #pragma unroll
     for (int i = 0; i < SEG; ++i) {
       const int q = tid + i * NT, row = q >> 1, blk = s * 2 + (q & 1);
-      const bool oka = m0 + row < p.M && blk < KS, okb = n0 + row < p.N && blk < KS;
+      const bool oka = m0 + row < m_end && blk < KS, okb = n0 + row < p.N && blk < KS;
       const uint32_t* pa = reinterpret_cast<const uint32_t*>(p.a_codes + (size_t)(m0 + row) * KBA + (size_t)blk * WA * 4);
-      const uint32_t* pb = reinterpret_cast<const uint32_t*>(p.b_codes + (size_t)(n0 + row) * KBB + (size_t)blk * WB * 4);
+      const uint32_t* pb = reinterpret_cast<const uint32_t*>(b_codes + (size_t)(n0 + row) * KBB + (size_t)blk * WB * 4);
 #pragma unroll
       for (int d = 0; d < WA; ++d) ca[i][d] = oka ? pa[d] : 0u;
 #pragma unroll
       for (int d = 0; d < WB; ++d) cb[i][d] = okb ? pb[d] : 0u;
       sa[i] = oka ? p.a_scales[(size_t)(m0 + row) * KS + blk] : 127u;
-      sb[i] = okb ? p.b_scales[(size_t)(n0 + row) * KS + blk] : 127u;
+      sb[i] = okb ? b_scales[(size_t)(n0 + row) * KS + blk] : 127u;
     }
   };
   auto store_stage = [&](int buf) {
@@ -440,12 +385,12 @@ __global__ __launch_bounds__(256) void k_gemm_mxx(MxwParams p) {
     for (int i = 0; i < SEG; ++i) {
       const int q = tid + i * NT, row = q >> 1, h = q & 1;
       uint32_t o[16];
-      mxx_expand<FA>(ca[i], mxx_scale(sa[i]), o);
+      expand_block_bf16<FA>(ca[i], mxx_scale(sa[i]), o);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<u32x4*>(&sA[buf][row * MXX_ROWB + (((4 * h + c) ^ mxx_swz(row)) << 4)]) =
             u32x4{o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]};
-      mxx_expand<FB>(cb[i], mxx_scale(sb[i]), o);
+      expand_block_bf16<FB>(cb[i], mxx_scale(sb[i]), o);
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<u32x4*>(&sB[buf][row * MXX_ROWB + (((4 * h + c) ^ mxx_swz(row)) << 4)]) =
@@ -500,7 +445,7 @@ __global__ __launch_bounds__(256) void k_gemm_mxx(MxwParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = m0 + wy * WM + i * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-        if (row < p.M && col < p.N) {
+        if (row < m_end && col < p.N) {
           if (p.c_bf16)
             reinterpret_cast<uint16_t*>(p.c)[(size_t)row * p.ldc + col] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
           else
@@ -512,11 +457,12 @@ __global__ __launch_bounds__(256) void k_gemm_mxx(MxwParams p) {
 
 hipError_t launch_gemm_mxw(int fa, int fb, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                            const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           hipStream_t st, bool exact) {
+                           int groups, const int32_t* offsets, hipStream_t st, bool exact) {
   MxwParams p;
   p.a_codes = a_codes; p.a_scales = a_scales; p.b_codes = b_codes; p.b_scales = b_scales;
   p.c = c; p.ldc = ldc; p.M = (int)M; p.N = (int)N; p.K = (int)K; p.c_bf16 = c_bf16;
-  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  p.groups = groups; p.offsets = offsets;
+  const int64_t tiles = gemm_tile_bound(M, N, 256, 256, groups);
   const int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
   if (fa < 0 || fa > 4 || fb < 0 || fb > 4) return hipErrorInvalidValue;

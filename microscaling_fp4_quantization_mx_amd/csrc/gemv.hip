@@ -18,7 +18,11 @@
 //    in LDS once per workgroup and window.
 //  * M = 4 .. 16: one dot2 per weight pair and activation row would make the
 //    VALU the bound, so the matrix cores take the products (bf16 MFMA).
+// Weights in the wider MX elements (MXFP8 E4M3 / E5M2, MXFP6 E2M3 / E3M2:
+// W8A16 / W6A16) take the second kernel for every M, with the block's 32 /
+// 24 code bytes expanded by the matching scaled conversion (mx_expand.h).
 #include "mx_device.h"
+#include "mx_expand.h"
 #include "mx_kernels.h"
 
 namespace mxk {
@@ -159,13 +163,15 @@ __global__ __launch_bounds__(GV_T) void k_gemv_sk(const uint16_t* __restrict__ x
   }
 }
 
-// Moderate M (VALU-bound).  A workgroup of 8 waves owns 8 x RB weight rows
-// (RB per wave) and walks the windows of K together.  Per window:
+// Moderate M (VALU-bound), and every M for the wider elements.  A workgroup
+// of 8 waves owns 8 x RB weight rows (RB per wave) and walks the windows of K
+// together.  Per window:
 //  * the activations of all M rows (M x 4 KiB) are copied into LDS by the
 //    LDS-DMA path (buffer_load ... lds), one buffer ahead, in a layout where
 //    chunk q (16 bytes) of lane l's block sits at (q * 64 + l) * 16, so the
 //    ds_read_b128 of a given q across the wave is conflict-free;
-//  * each wave loads its RB code vectors and scale bytes one window ahead;
+//  * each wave loads its RB blocks' codes (16 / 24 / 32 bytes for E2M1 /
+//    FP6 / FP8 elements) and scale bytes one window ahead;
 //  * each lane converts its RB blocks once (RB x 16 bf16 pairs in registers)
 //    and then, per activation row m, reads its 64 activation bytes from LDS
 //    and issues RB x 16 dot2.
@@ -177,17 +183,24 @@ constexpr int GV_LG_MIN_M = 2;         // smallest M that takes the large-M kern
 
 
 
-template <int M, int RB>
+// F: element format (E4M3 0, E5M2 1, E2M3 2, E3M2 3, E2M1 4).  MT: activation
+// rows the kernel is built for; E2M1 instantiates every M exactly (M = MT),
+// the wider formats round M up to MT in {1, 2, 4, 8, 16} and take the rows
+// count at run time (m_rows; rows m >= m_rows are staged as zeros and skipped).
+template <int F, int MT, int RB>
 __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
                                                   const uint8_t* __restrict__ ws, int N, int K,
-                                                  uint16_t* __restrict__ y, int64_t ldy) {
-  constexpr int MP = (M + 1) & ~1;                 // staged rows, even: every wave issues MP / 2 copies
+                                                  uint16_t* __restrict__ y, int64_t ldy, int m_rows) {
+  constexpr int MP = (MT + 1) & ~1;                // staged rows, even: every wave issues MP / 2 copies
   constexpr int XCH = MP * 4;                      // 1 KiB copies per window (4 per activation row)
   constexpr int XPW = XCH / 8;                     // copies per wave
+  constexpr int DW = MxElem<F>::DW;                // code dwords of one 32-element block
+  constexpr int CB = DW * 4;                       // ... bytes
+  const int M = F == 4 ? MT : m_rows;
   __shared__ __attribute__((aligned(16))) uint8_t sx[2][MP * 4096];
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * (8 * RB) + wave * RB;
-  const int KB = K / 2, KS = K / 32;
+  const int KB = K / 32 * CB, KS = K / 32;
   const int nwin = (K + GV_WIN - 1) / GV_WIN;
   const int rows_ok = __builtin_amdgcn_readfirstlane(max(0, min(RB, N - n0)));
   const size_t nb = n0 < N ? (size_t)n0 : 0;
@@ -202,7 +215,7 @@ __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x
       const int c = wave * XPW + i;                // uniform
       const int m = c >> 2, q = c & 3;
       const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-          (void*)(x + (size_t)(m < M ? m : 0) * ldx), 0, m < M ? K * 2 : 0, 0x00020000);
+          (void*)(x + (size_t)(m < M ? m : 0) * ldx), 0, __builtin_amdgcn_readfirstlane(m < M ? K * 2 : 0), 0x00020000);
       // LDS chunk q * 64 + lane holds window chunk 4 * lane + q
       const int k = w * GV_WIN + (4 * lane + q) * 8;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(&sx[b][(m * 256 + q * 64) * 16]), 16,
@@ -210,36 +223,47 @@ __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x
     }
   };
   uint32_t sc[2][RB];
-  u32x4 cw[2][RB];
+  uint32_t cw[2][RB][DW];
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   auto issue = [&](int b, int w) {
     const int kb = w * 64 + lane;
     const bool kok = kb < KS;
 #pragma unroll
     for (int r = 0; r < RB; ++r) sc[b][r] = __builtin_amdgcn_raw_buffer_load_b8(rws, kok ? r * KS + kb : oob, 0, GV_NT);
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
-      cw[b][r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwc, kok ? r * KB + kb * 16 : oob, 0, GV_NT));
+    for (int r = 0; r < RB; ++r) {
+      const int o0 = kok ? r * KB + kb * CB : oob, o1 = kok ? r * KB + kb * CB + 16 : oob;
+      const u32x4 v0 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwc, o0, 0, GV_NT));
+#pragma unroll
+      for (int d = 0; d < 4; ++d) cw[b][r][d] = v0[d];
+      if constexpr (DW == 8) {
+        const u32x4 v1 = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rwc, o1, 0, GV_NT));
+#pragma unroll
+        for (int d = 0; d < 4; ++d) cw[b][r][4 + d] = v1[d];
+      } else if constexpr (DW == 6) {
+        const u32x2 v1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rwc, o1, 0, GV_NT));
+        cw[b][r][4] = v1[0];
+        cw[b][r][5] = v1[1];
+      }
+    }
   };
-  constexpr int LOADS = XPW + 2 * RB;              // vector-memory ops per window and wave
+  constexpr int LOADS = XPW + (DW == 4 ? 2 : 3) * RB;   // vector-memory ops per window and wave
 
-  float acc[RB][M];
+  float acc[RB][MT];
 #pragma unroll
   for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.0f;
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
 
   auto compute = [&](int b) {
     bf16x2 wv[RB][16];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       const float s = pow2f((int)sc[b][r] - 127);   // byte 0 (zero block) gives +0.0
+      uint32_t o[16];
+      expand_block_bf16<F>(cw[b][r], s, o);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        wv[r][q * 4 + 0] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[b][r][q], s, 0);
-        wv[r][q * 4 + 1] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[b][r][q], s, 1);
-        wv[r][q * 4 + 2] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[b][r][q], s, 2);
-        wv[r][q * 4 + 3] = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw[b][r][q], s, 3);
-      }
+      for (int i = 0; i < 16; ++i) __builtin_memcpy(&wv[r][i], &o[i], 4);
     }
     // activation rows one at a time, the next one's LDS reads in flight
     // (the barriers below keep the compiler from hoisting all of them)
@@ -250,7 +274,8 @@ __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x
     };
     read_x(0, 0);
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
+    for (int m = 0; m < MT; ++m) {
+      if (m >= M) break;                           // uniform (wider formats: rows counted at run time)
       if (m + 1 < M) read_x((m + 1) & 1, m + 1);
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
@@ -292,16 +317,16 @@ __global__ __launch_bounds__(GL_T) void k_gemv_lg(const uint16_t* __restrict__ x
   }
   wait_vmcnt<0>();
 
-  // reduce the RB x M sums over the wave; lane l ends up owning one of them
-  constexpr int V = (RB * M <= 8) ? 8 : (RB * M <= 16) ? 16 : (RB * M <= 32) ? 32 : 64;
-  static_assert(RB * M <= 64, "at most 64 sums per wave");
+  // reduce the RB x MT sums over the wave; lane l ends up owning one of them
+  constexpr int V = (RB * MT <= 8) ? 8 : (RB * MT <= 16) ? 16 : (RB * MT <= 32) ? 32 : 64;
+  static_assert(RB * MT <= 64, "at most 64 sums per wave");
   float v[V];
 #pragma unroll
-  for (int i = 0; i < V; ++i) v[i] = i < RB * M ? acc[i / M][i % M] : 0.0f;
+  for (int i = 0; i < V; ++i) v[i] = i < RB * MT ? acc[i / MT][i % MT] : 0.0f;
   int id;
   const float tot = wave_transpose_sum<V>(v, lane, &id);
-  const int r = id / M, m = id - r * M;
-  if ((lane & (64 / V - 1)) == 0 && id < RB * M && n0 + r < N)
+  const int r = id / MT, m = id - r * MT;
+  if ((lane & (64 / V - 1)) == 0 && id < RB * MT && m < M && n0 + r < N)
     y[(size_t)m * ldy + n0 + r] = (uint16_t)f32_to_bf16_rne(tot);
 }
 
@@ -443,9 +468,25 @@ __global__ __launch_bounds__(GM_T) void k_gemv_mf(const uint16_t* __restrict__ x
   if (i < M && n < N) y[(size_t)i * ldy + n] = (uint16_t)f32_to_bf16_rne(sum);
 }
 
-hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
+hipError_t launch_gemv(int fmt, const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st) {
   if (N == 0) return hipSuccess;
+  if (fmt < 0 || fmt > 4 || M < 1 || M > 16) return hipErrorInvalidValue;
+  if (fmt != 4) {
+    constexpr int RB = GV_LG_RB;
+    const int grid = (int)((N + 8 * RB - 1) / (8 * RB));
+    const int mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16;
+#define MX_GVW(FF, MM) \
+  case MM: hipLaunchKernelGGL((k_gemv_lg<FF, MM, RB>), dim3(grid), dim3(GL_T), 0, st, (const uint16_t*)x, ldx, wc, ws, (int)N, (int)K, (uint16_t*)y, ldy, (int)M); break;
+#define MX_GVWF(FF)                                                                            \
+  case FF:                                                                                     \
+    switch (mt) { MX_GVW(FF, 1) MX_GVW(FF, 2) MX_GVW(FF, 4) MX_GVW(FF, 8) MX_GVW(FF, 16) }     \
+    break;
+    switch (fmt) { MX_GVWF(0) MX_GVWF(1) MX_GVWF(2) MX_GVWF(3) }
+#undef MX_GVWF
+#undef MX_GVW
+    return hipGetLastError();
+  }
   if (M < GV_LG_MIN_M) {
     constexpr int RB = GV_SK_RB;
     const int grid = (int)((N + RB - 1) / RB);
@@ -470,7 +511,7 @@ hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc,
   }
   constexpr int RB = GV_LG_RB;
   const int grid = (int)((N + 8 * RB - 1) / (8 * RB));
-#define MX_GVL(MM) case MM: hipLaunchKernelGGL((k_gemv_lg<MM, RB>), dim3(grid), dim3(GL_T), 0, st, (const uint16_t*)x, ldx, wc, ws, (int)N, (int)K, (uint16_t*)y, ldy); break;
+#define MX_GVL(MM) case MM: hipLaunchKernelGGL((k_gemv_lg<4, MM, RB>), dim3(grid), dim3(GL_T), 0, st, (const uint16_t*)x, ldx, wc, ws, (int)N, (int)K, (uint16_t*)y, ldy, (int)M); break;
   switch ((int)M) {
     MX_GVL(2) MX_GVL(3) MX_GVL(4) MX_GVL(5) MX_GVL(6) MX_GVL(7) MX_GVL(8)
     MX_GVL(9) MX_GVL(10) MX_GVL(11) MX_GVL(12) MX_GVL(13) MX_GVL(14) MX_GVL(15) MX_GVL(16)

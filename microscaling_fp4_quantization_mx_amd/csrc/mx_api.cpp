@@ -67,7 +67,25 @@ int check_dense_input(const void* x, int32_t dt, int64_t ld, int64_t rows, int64
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_ERR_HIP; }
 
-size_t dyn_a_bytes(int64_t M, int64_t K) { return round256((size_t)(M * K / 2)) + round256((size_t)(M * K / 32)); }
+inline int elem_bits(int32_t fmt) {
+  return fmt == MX_FMT_MXFP8_E4M3 || fmt == MX_FMT_MXFP8_E5M2 ? 8 : (fmt == MX_FMT_MXFP6_E2M3 || fmt == MX_FMT_MXFP6_E3M2 ? 6 : 4);
+}
+// Element format of a dynamically quantized A: flags bits 4-7 hold the format
+// + 1, or 0 for the format of B.
+constexpr int32_t kDynShift = 4;
+constexpr int32_t kDynMask = 0xF << kDynShift;
+inline int32_t dyn_a_fmt(const mx_gemm_args* a) {
+  const int32_t sel = (a->flags & kDynMask) >> kDynShift;
+  return sel ? sel - 1 : (a->b ? a->b->fmt : MX_FMT_MXFP4);
+}
+// MX formats a dynamic A can take: E2M1, E4M3, E5M2, E2M3, E3M2 elements with
+// E8M0 scales over 32-element blocks
+inline bool dyn_fmt_ok(int32_t fmt) { return fmt == MX_FMT_MXFP4 || fmt_wide(fmt); }
+// codes then scale bytes of a dynamic A [M, K] (K % 32 == 0)
+size_t dyn_codes_bytes(int32_t fmt, int64_t M, int64_t K) { return (size_t)(M * (K / 8 * elem_bits(fmt))); }
+size_t dyn_a_bytes(int32_t fmt, int64_t M, int64_t K) {
+  return round256(dyn_codes_bytes(fmt, M, K)) + round256((size_t)(M * K / 32));
+}
 
 // The fused quantize + GEMM kernel splits its tiles over the 8 XCDs of a
 // 256-CU part (32 workgroups each).
@@ -86,7 +104,8 @@ int device_cus() {
 // takes (the workspace reserves its counters and partial tiles whenever this
 // holds).
 bool fused_shape(const mx_gemm_args* a) {
-  return !a->a && (a->flags & MX_GEMM_FUSED_QUANTIZE) && a->b && a->b->fmt == MX_FMT_MXFP4 && (a->a_raw_dtype == MX_DT_F32 || a->a_raw_dtype == MX_DT_BF16) &&
+  return !a->a && (a->flags & MX_GEMM_FUSED_QUANTIZE) && a->b && a->b->fmt == MX_FMT_MXFP4 &&
+         dyn_a_fmt(a) == MX_FMT_MXFP4 && (a->a_raw_dtype == MX_DT_F32 || a->a_raw_dtype == MX_DT_BF16) &&
          a->M > 0 && a->N > 0 && a->K > 0 && a->lda_raw < (int64_t(1) << 24) &&   // 32-bit offsets over 32 rows
          mxk::fused_fits(a->M, a->N, a->K, a->groups, kFusedCUs / 8);
 }
@@ -124,7 +143,8 @@ size_t mx_workspace_bytes(int32_t op, const void* desc, int32_t flags) {
   if (op == MX_OP_GEMM) {
     const mx_gemm_args* a = static_cast<const mx_gemm_args*>(desc);
     size_t n = 0;
-    if (!a->a && !(a->a_codes_out && a->a_scales_out) && a->M > 0 && a->K > 0) n = dyn_a_bytes(a->M, a->K);
+    if (!a->a && !(a->a_codes_out && a->a_scales_out) && a->M > 0 && a->K > 0 && dyn_fmt_ok(dyn_a_fmt(a)))
+      n = dyn_a_bytes(dyn_a_fmt(a), a->M, a->K);
     if (fused_shape(a)) n += round256(mxk::fused_workspace_bytes());
     return n;
   }
@@ -230,7 +250,7 @@ int mx_dequantize(const mx_tensor* in, void* y, int32_t y_dtype, int64_t ld_y, v
 
 int mx_gemm(const mx_gemm_args* a, void* stream) {
   if (!a) return MX_ERR_NULL;
-  if (a->flags & ~(MX_GEMM_F8F6F4_MATRIX_CORES | MX_GEMM_FUSED_QUANTIZE)) return MX_ERR_SHAPE;
+  if (a->flags & ~(MX_GEMM_F8F6F4_MATRIX_CORES | MX_GEMM_FUSED_QUANTIZE | kDynMask)) return MX_ERR_SHAPE;
   if (a->M < 0 || a->N < 0 || a->K < 0 || a->M > kMaxDim || a->N > kMaxDim || a->K > kMaxDim) return MX_ERR_SHAPE;
   if (a->groups < 0) return MX_ERR_SHAPE;
   int st = check_tensor(a->b);
@@ -239,6 +259,7 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
   if (a->b->cols != a->K) return MX_ERR_SHAPE;
   if (fmt == MX_FMT_MXFP4_K16 || fmt == MX_FMT_FP4_TENSOR) return MX_ERR_UNSUPPORTED;
   if (a->a && (a->a->fmt == MX_FMT_MXFP4_K16 || a->a->fmt == MX_FMT_FP4_TENSOR)) return MX_ERR_UNSUPPORTED;
+  if (a->a && (a->flags & kDynMask)) return MX_ERR_FORMAT;   // a format for a dynamic A, but A is given
   // a row length that is not a multiple of 32 is stored zero-padded: the
   // product over the padded length is the same
   const int64_t Kp = fmt == MX_FMT_NVFP4 ? a->K : pad_to(a->K, 32);
@@ -247,84 +268,86 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
   } else {
     if (a->b->rows != (int64_t)a->groups * a->N) return MX_ERR_SHAPE;
     if (!a->group_offsets) return MX_ERR_NULL;
-    if (fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;
+    if (fmt == MX_FMT_NVFP4) return MX_ERR_UNSUPPORTED;
   }
-  // MX element pairs other than E2M1 x E2M1 (MXFP8 / MXFP6, mixed pairs)
-  if (a->a && (fmt_wide(fmt) || fmt_wide(a->a->fmt))) {
-    st = check_tensor(a->a);
-    if (st) return st;
-    if (a->a->fmt == MX_FMT_NVFP4 || fmt == MX_FMT_NVFP4) return MX_ERR_FORMAT;
-    if (a->groups != 0) return MX_ERR_UNSUPPORTED;
-    if (a->a->rows != a->M || a->a->cols != a->K) return MX_ERR_SHAPE;
-    if (!dtype_ok(a->c_dtype)) return MX_ERR_DTYPE;
-    if (a->ldc < a->N) return MX_ERR_SHAPE;
-    if (a->M > 0 && a->N > 0) {
-      if (!a->c) return MX_ERR_NULL;
-      if (!al16(a->c)) return MX_ERR_ALIGN;
-    }
-    if (Kp % 128 != 0 || Kp > (int64_t(1) << 22)) return MX_ERR_UNSUPPORTED;
-    if (a->M == 0 || a->N == 0) return MX_OK;
-    return hip_status(mxk::launch_gemm_mxw(mfma_fmt(a->a->fmt), mfma_fmt(fmt), a->a->codes, a->a->scales,
-                                           a->b->codes, a->b->scales, a->c, a->c_dtype == MX_DT_BF16, a->ldc,
-                                           a->M, a->N, Kp, as_stream(stream),
-                                           !(a->flags & MX_GEMM_F8F6F4_MATRIX_CORES)));
-  }
-  if (fmt_wide(fmt)) return MX_ERR_UNSUPPORTED;   // dynamic activation quantization is MXFP4 only
   if (!dtype_ok(a->c_dtype)) return MX_ERR_DTYPE;
   if (a->ldc < a->N) return MX_ERR_SHAPE;
   if (a->M > 0 && a->N > 0) {
     if (!a->c) return MX_ERR_NULL;
     if (!al16(a->c)) return MX_ERR_ALIGN;
   }
+  hipStream_t s = as_stream(stream);
+  const int cbf = a->c_dtype == MX_DT_BF16;
+
+  // A: pre-quantized, or quantized here (dynamic) into the side outputs or the
+  // workspace (after the fused kernel's counters when that kernel runs)
+  const int32_t afmt = a->a ? a->a->fmt : dyn_a_fmt(a);
   const uint8_t* a_codes = nullptr;
   const uint8_t* a_scales = nullptr;
   const float* a_global = nullptr;
   bool dynamic = false;
+  size_t fused_ws = 0;
   if (a->a) {
     st = check_tensor(a->a);
     if (st) return st;
-    if (a->a->fmt != fmt) return MX_ERR_FORMAT;
     if (a->a->rows != a->M || a->a->cols != a->K) return MX_ERR_SHAPE;
     a_codes = a->a->codes; a_scales = a->a->scales; a_global = a->a->global_scale;
   } else {
-    if (fmt != MX_FMT_MXFP4) return MX_ERR_UNSUPPORTED;   // dynamic path quantizes A to MXFP4
-    if (a->K % 32 != 0) return MX_ERR_UNSUPPORTED;        // ... with whole blocks only
+    if (fmt == MX_FMT_NVFP4) return MX_ERR_UNSUPPORTED;    // dynamic A takes an MX format
+    if (!dyn_fmt_ok(afmt)) return MX_ERR_FORMAT;
+    if (a->K % 32 != 0) return MX_ERR_UNSUPPORTED;         // ... with whole blocks only
     st = check_dense_input(a->a_raw, a->a_raw_dtype, a->lda_raw, a->M, a->K);
     if (st) return st;
     if (a->M > kMaxElems / (a->K > 0 ? a->K : 1)) return MX_ERR_SHAPE;
     dynamic = true;
-    // the fused kernel's counters and partial tiles lead the workspace
-    const size_t fused_ws = fused_shape(a) ? round256(mxk::fused_workspace_bytes()) : 0;
+    fused_ws = fused_shape(a) ? round256(mxk::fused_workspace_bytes()) : 0;
     if (a->a_codes_out || a->a_scales_out) {
       if (!a->a_codes_out || !a->a_scales_out) return MX_ERR_NULL;
       if (!al16(a->a_codes_out) || !al16(a->a_scales_out)) return MX_ERR_ALIGN;
       a_codes = a->a_codes_out; a_scales = a->a_scales_out;
       if (fused_ws && (!a->workspace || a->workspace_bytes < fused_ws || !al16(a->workspace))) return MX_ERR_WORKSPACE;
     } else if (a->M > 0 && a->K > 0) {
-      const size_t need = fused_ws + dyn_a_bytes(a->M, a->K);
+      const size_t need = fused_ws + dyn_a_bytes(afmt, a->M, a->K);
       if (!a->workspace || a->workspace_bytes < need || !al16(a->workspace)) return MX_ERR_WORKSPACE;
       a_codes = static_cast<const uint8_t*>(a->workspace) + fused_ws;
-      a_scales = a_codes + round256((size_t)(a->M * a->K / 2));
+      a_scales = a_codes + round256(dyn_codes_bytes(afmt, a->M, a->K));
     }
-    if (fused_ws && a->M > 0 && a->N > 0 && device_cus() == kFusedCUs) {
-      if (a->K > (int64_t(1) << 23)) return MX_ERR_UNSUPPORTED;
-      return hip_status(mxk::launch_gemm_mx_fused(a->a_raw, a->a_raw_dtype == MX_DT_BF16, a->lda_raw,
-                                                  const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales),
-                                                  a->b->codes, a->b->scales, a->c, a->c_dtype == MX_DT_BF16, a->ldc,
-                                                  a->M, a->N, a->K, a->groups, a->group_offsets, a->workspace,
-                                                  kFusedCUs / 8, as_stream(stream)));
+  }
+
+  // MX element pairs other than E2M1 x E2M1 (MXFP8 / MXFP6, mixed pairs)
+  if (fmt_wide(fmt) || fmt_wide(afmt)) {
+    if (afmt == MX_FMT_NVFP4 || fmt == MX_FMT_NVFP4) return MX_ERR_FORMAT;
+    if (Kp % 128 != 0 || Kp > (int64_t(1) << 22)) return MX_ERR_UNSUPPORTED;
+    if (a->M == 0 || a->N == 0) return MX_OK;
+    if (dynamic) {
+      const hipError_t e =
+          afmt == MX_FMT_MXFP4
+              ? mxk::launch_quant_mx(a->a_raw, a->a_raw_dtype == MX_DT_BF16, a->lda_raw, a->M, a->K,
+                                     const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), s)
+              : mxk::launch_quant_wide(mfma_fmt(afmt), a->a_raw, a->a_raw_dtype == MX_DT_BF16, a->lda_raw, a->M, a->K,
+                                       const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), s);
+      if (e != hipSuccess) return MX_ERR_HIP;
     }
+    return hip_status(mxk::launch_gemm_mxw(mfma_fmt(afmt), mfma_fmt(fmt), a_codes, a_scales, a->b->codes,
+                                           a->b->scales, a->c, cbf, a->ldc, a->M, a->N, Kp, a->groups,
+                                           a->group_offsets, s, !(a->flags & MX_GEMM_F8F6F4_MATRIX_CORES)));
+  }
+  if (afmt != fmt) return MX_ERR_FORMAT;
+  if (dynamic && fused_ws && a->M > 0 && a->N > 0 && device_cus() == kFusedCUs) {
+    if (a->K > (int64_t(1) << 23)) return MX_ERR_UNSUPPORTED;
+    return hip_status(mxk::launch_gemm_mx_fused(a->a_raw, a->a_raw_dtype == MX_DT_BF16, a->lda_raw,
+                                                const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales),
+                                                a->b->codes, a->b->scales, a->c, cbf, a->ldc, a->M, a->N, a->K,
+                                                a->groups, a->group_offsets, a->workspace, kFusedCUs / 8, s));
   }
   if (fmt == MX_FMT_NVFP4 && a->K % 32 != 0) return MX_ERR_UNSUPPORTED;
   if (a->K > (int64_t(1) << 23)) return MX_ERR_UNSUPPORTED;   // tile byte offsets stay below 2^30
   if (a->M == 0 || a->N == 0) return MX_OK;
-  hipStream_t s = as_stream(stream);
   if (dynamic && a->K > 0) {
     hipError_t e = mxk::launch_quant_mx(a->a_raw, a->a_raw_dtype == MX_DT_BF16, a->lda_raw, a->M, a->K,
                                         const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), s);
     if (e != hipSuccess) return MX_ERR_HIP;
   }
-  const int cbf = a->c_dtype == MX_DT_BF16;
   if (fmt == MX_FMT_MXFP4)
     return hip_status(mxk::launch_gemm_mx(a_codes, a_scales, a->b->codes, a->b->scales, a->c, cbf, a->ldc, a->M, a->N,
                                           Kp, a->groups, a->group_offsets, s));
@@ -403,7 +426,7 @@ int mx_gemv(const void* x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_te
   int st = check_tensor(w);
   if (st) return st;
   if (x_dtype != MX_DT_BF16 || y_dtype != MX_DT_BF16) return MX_ERR_DTYPE;
-  if (w->fmt != MX_FMT_MXFP4 || w->cols % 32 != 0) return MX_ERR_UNSUPPORTED;
+  if ((w->fmt != MX_FMT_MXFP4 && !fmt_wide(w->fmt)) || w->cols % 32 != 0) return MX_ERR_UNSUPPORTED;
   if (M < 0) return MX_ERR_SHAPE;
   if (M > 16) return MX_ERR_UNSUPPORTED;
   const int64_t N = w->rows, K = w->cols;
@@ -413,7 +436,7 @@ int mx_gemv(const void* x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_te
   if (M == 0 || N == 0) return MX_OK;
   if (!y) return MX_ERR_NULL;
   if (!al16(y)) return MX_ERR_ALIGN;
-  return hip_status(mxk::launch_gemv(x, ld_x, M, w->codes, w->scales, N, K, y, ld_y, as_stream(stream)));
+  return hip_status(mxk::launch_gemv(mfma_fmt(w->fmt), x, ld_x, M, w->codes, w->scales, N, K, y, ld_y, as_stream(stream)));
 }
 
 }  // extern "C"

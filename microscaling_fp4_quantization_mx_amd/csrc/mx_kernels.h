@@ -44,9 +44,10 @@ hipError_t launch_dequant_wide(int fmt, const uint8_t* codes, const uint8_t* sca
 // exact: codes expanded to exact bf16 values for the bf16 matrix cores;
 // otherwise the block-scaled FP8/FP6/FP4 matrix cores (faster; they truncate
 // products with FP8 or FP6 operands).
+// groups / offsets: the grouped form, as for launch_gemm_mx (0: dense).
 hipError_t launch_gemm_mxw(int fa, int fb, const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                            const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                           hipStream_t st, bool exact);
+                           int groups, const int32_t* offsets, hipStream_t st, bool exact);
 // Emulation variants (quantize_variant.hip): block 16 or 32, the OCP floor
 // rule, a per-tensor scale g (NULL = 1), rows of any length (zero-padded to
 // whole blocks); naive per-tensor FP4.
@@ -59,7 +60,8 @@ hipError_t launch_quant_naive(const void* x, int xdt_bf16, int64_t ldx, int64_t 
                               float* s, uint32_t* partial, int max_partials, hipStream_t st);
 hipError_t launch_dequant_naive(const uint8_t* codes, const float* s, int64_t rows, int64_t cols, void* y, bool out_bf16,
                                 int64_t ldy, hipStream_t st);
-hipError_t launch_gemv(const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
+// fmt: the weights' element format as the matrix-core code above (E2M1 4).
+hipError_t launch_gemv(int fmt, const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st);
 hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int experts, int32_t* offsets,
                             int32_t* dest_row, int32_t* src_token, int32_t* cnt, hipStream_t st);

@@ -266,8 +266,9 @@ def test_variant_format_validation():
 
 def test_wide_format_validation():
     """MXFP8 / MXFP6 descriptors: quantize and dequantize accept them, the
-    GEMM takes any MX pair (dense, pre-quantized A, K % 128 == 0) and every
-    other entry point reports them unsupported."""
+    GEMM takes any MX pair (dense or grouped, pre-quantized or dynamic A,
+    K % 128 == 0), the GEMV takes them as weights, and the remaining entry
+    points report them unsupported."""
     L = mx.lib()
     for f in (2, 3, 4, 5):
         assert quant(t=T(fmt=f), flags=1) == -5                            # no static-scale flag
@@ -285,15 +286,35 @@ def test_wide_format_validation():
     g.a.contents.fmt = 1
     g.a.contents.global_scale = FAKE
     assert call_gemm(g) == -8                                              # NVFP4 x MXFP6
+    # grouped wide pairs: the grouped checks apply
+    g = gemm_args(K=256, fmt=3, groups=2)
+    assert call_gemm(g) == -1                                              # offsets missing
     g = gemm_args(K=256, fmt=3, groups=2, group_offsets=FAKE)
-    assert call_gemm(g) == -5                                              # grouped wide not provided
-    g = gemm_args(K=256, fmt=5, a=False, a_raw=FAKE, a_raw_dtype=1, lda_raw=256)
-    assert call_gemm(g) == -5                                              # dynamic path: MXFP4 only
-    g = gemm_args(K=1 << 23, fmt=2)
-    g.a.contents.rows = 1
+    g.b.contents.rows = 128
+    assert call_gemm(g) == -2                                              # b rows != groups * N
+    assert call_gemm(gemm_args(M=0, fmt=3, groups=2, group_offsets=FAKE)) == 0
+    # dynamic A to a wide format (B's, or the one named in flags)
+    dyn = dict(a=False, a_raw=FAKE, a_raw_dtype=1, lda_raw=256)
+    assert call_gemm(gemm_args(K=256, fmt=5, **dyn, workspace=None)) == -7  # needs a workspace
+    g = gemm_args(K=256, fmt=5, **dyn)
+    need = L.mx_workspace_bytes(mx.MX_OP_GEMM, ctypes.cast(ctypes.pointer(g), ctypes.c_void_p), 0)
+    assert need == 64 * 256 * 6 // 8 + 64 * 256 // 32                        # E3M2 codes + scale bytes
+    g = gemm_args(K=256, fmt=0, **dyn, flags=mx.MX_GEMM_DYNAMIC_A_FORMAT(2))
+    need = L.mx_workspace_bytes(mx.MX_OP_GEMM, ctypes.cast(ctypes.pointer(g), ctypes.c_void_p), 0)
+    assert need == 64 * 256 + 64 * 256 // 32                                 # E4M3 activations
+    assert call_gemm(gemm_args(K=250, fmt=2, **dyn, ldc=128)) == -5         # whole blocks only
+    assert call_gemm(gemm_args(K=256, fmt=0, **dyn, flags=mx.MX_GEMM_DYNAMIC_A_FORMAT(1))) == -8   # NVFP4
+    assert call_gemm(gemm_args(K=256, fmt=0, **dyn, flags=mx.MX_GEMM_DYNAMIC_A_FORMAT(6))) == -8   # K16 variant
+    assert call_gemm(gemm_args(K=256, fmt=0, flags=mx.MX_GEMM_DYNAMIC_A_FORMAT(2))) == -8          # A given
     assert call_gemm(gemm_args(M=0, fmt=2)) == 0
-    w = T(3, 512, 256)
+    # GEMV: MXFP8 / MXFP6 weights, whole blocks; not the variants
+    w = T(3, 512, 250)
     assert L.mx_gemv(FAKE, 1, 1, 256, ctypes.byref(w), FAKE, 1, 512, None) == -5
+    w = T(6, 512, 256)
+    assert L.mx_gemv(FAKE, 1, 1, 256, ctypes.byref(w), FAKE, 1, 512, None) == -5
+    w = T(4, 512, 256)
+    assert L.mx_gemv(FAKE, 1, 17, 256, ctypes.byref(w), FAKE, 1, 512, None) == -5   # M <= 16
+    assert L.mx_gemv(FAKE, 1, 0, 256, ctypes.byref(w), FAKE, 1, 512, None) == 0
     t = T(fmt=4, rows=16, cols=256)
     assert L.mx_rmsnorm_quantize(FAKE, 1, 256, FAKE, 0, ctypes.c_float(1e-6), ctypes.byref(t), 0, None) == -5
     assert L.mx_quantize_rows(FAKE, 0, 256, 10, FAKE, ctypes.byref(t), None) == -5

@@ -245,3 +245,137 @@ def test_wide_gemm_exact_structured(fa, fb, fast):
     assert np.array_equal(O.dequantize_fmt(fb, host(qb.codes), host(qb.scales)), b)
     c = host(mx.mx_gemm(qa, qb, out_dtype=torch.float32, f8f6f4_matrix_cores=fast)).astype(np.float64)
     assert np.array_equal(c, a.astype(np.float64) @ b.astype(np.float64).T)
+
+
+# ---------------------------------------------------------------- grouped form
+def _grouped_ref(ah, bh_stack, offsets, N, out):
+    """Rows [off[g], off[g+1]) of A against matrix g of the stack (oracle gemm
+    per group), with the per-element tolerance of each group's product."""
+    M = ah.shape[0]
+    ref = np.zeros((M, N), np.float64)
+    tol = np.zeros((M, N), np.float64)
+    for g in range(len(offsets) - 1):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 <= r0:
+            continue
+        bg = bh_stack[g * N:(g + 1) * N]
+        y = O.gemm(ah[r0:r1], bg, out=out)
+        ref[r0:r1] = y
+        tol[r0:r1] = O.gemm_tolerance(ah[r0:r1], bg, y, out=out)
+    return ref, tol
+
+
+GROUPED_PAIRS = [("mxfp8_e4m3", "mxfp4"), ("mxfp6_e2m3", "mxfp6_e2m3"), ("mxfp4", "mxfp8_e5m2"),
+                 ("mxfp8_e5m2", "mxfp6_e3m2")]
+
+
+@pytest.mark.parametrize("fast", [False, True])
+@pytest.mark.parametrize("fa,fb", GROUPED_PAIRS)
+def test_wide_grouped_gemm(fa, fb, fast):
+    """Four groups with ragged row counts (one empty, one spanning two tile
+    rows plus a tail): every row against its own group's matrix."""
+    G, N, K = 4, 200, 384
+    counts = [300, 0, 41, 260]
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offsets[-1])
+    announce(f"wide grouped gemm {fa} x {fb} G={G} M={M} N={N} K={K} f8f6f4={fast}")
+    rng = np.random.default_rng(ALL.index(fa) * 7 + ALL.index(fb))
+    a = (rng.standard_normal((M, K)) * np.exp2(rng.integers(-4, 4, (M, 1)))).astype(np.float32)
+    b = (rng.standard_normal((G * N, K)) * 0.05).astype(np.float32)
+    qa = mx.mx_quantize(torch.from_numpy(a).to(DEV), fa)
+    qb = mx.mx_quantize(torch.from_numpy(b).to(DEV), fb)
+    off = torch.from_numpy(offsets).to(DEV)
+    c = mx.mx_gemm(qa, qb, N=N, out_dtype=torch.float32, groups=G, offsets=off, f8f6f4_matrix_cores=fast)
+    ah = O.dequantize_fmt(fa, host(qa.codes), host(qa.scales))
+    bh = O.dequantize_fmt(fb, host(qb.codes), host(qb.scales))
+    ref, tol = _grouped_ref(ah, bh, offsets, N, "f32")
+    if fast:
+        for g in range(G):
+            r0, r1 = offsets[g], offsets[g + 1]
+            if r1 > r0:
+                tol[r0:r1] += mfma_truncation_bound(ah[r0:r1], bh[g * N:(g + 1) * N])
+    got = host(c).astype(np.float64)
+    bad = np.abs(got - ref) > tol
+    assert not bad.any(), (np.argwhere(bad)[:5], np.abs(got - ref).max())
+
+
+# ------------------------------------------------ dynamic activation quantize
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("afmt,bfmt", [(None, "mxfp8_e4m3"), (None, "mxfp6_e3m2"), ("mxfp8_e4m3", "mxfp4"),
+                                       ("mxfp6_e2m3", "mxfp8_e5m2"), ("mxfp4", "mxfp6_e2m3")])
+def test_wide_dynamic_gemm(afmt, bfmt, dtype):
+    """Raw activations quantized inside the call, to B's format or to the
+    named one: the side-output codes and scale bytes equal the oracle's
+    quantization bit for bit, and C is the oracle product of those operands
+    (dense, then grouped with the same rows)."""
+    fa = afmt or bfmt
+    M, N, K = 130, 96, 512
+    announce(f"wide dynamic gemm A {fa} (raw {dtype}) x B {bfmt} {M}x{N}x{K}")
+    rng = np.random.default_rng(ALL.index(fa) * 11 + ALL.index(bfmt))
+    a = hard_inputs(M, K, 5, fa) if dtype == torch.float32 else bf16_values(hard_inputs(M, K, 5, fa))
+    a = np.clip(a, -2.0 ** 100, 2.0 ** 100).astype(np.float32)
+    b = (rng.standard_normal((2 * N, K)) * 0.05).astype(np.float32)
+    qb = mx.mx_quantize(torch.from_numpy(b).to(DEV), bfmt)
+    at = torch.from_numpy(a).to(dtype).to(DEV)
+    bits = mx.element_bits(mx._FMT[fa])
+    codes = torch.empty(M, K * bits // 8, dtype=torch.uint8, device=DEV)
+    scales = torch.empty(M, K // 32, dtype=torch.uint8, device=DEV)
+    rc, rs = O.mx_quantize_fmt(a, fa)
+    ah = O.dequantize_fmt(fa, rc, rs)
+    bh = O.dequantize_fmt(bfmt, host(qb.codes), host(qb.scales))
+    # dense, against the first N rows of B
+    qb_dense = mx.MXTensor(qb.fmt, N, K, qb.codes[:N], qb.scales[:N])
+    c = mx.mx_gemm(at, qb_dense, out_dtype=torch.float32, a_codes_out=codes, a_scales_out=scales, a_format=afmt)
+    assert np.array_equal(host(scales), rs)
+    assert np.array_equal(host(codes), rc)
+    ref = O.gemm(ah, bh[:N])
+    assert np.all(np.abs(host(c) - ref) <= O.gemm_tolerance(ah, bh[:N]))
+    # grouped, A in the workspace
+    offsets = np.array([0, 57, M], np.int32)
+    c2 = mx.mx_gemm(at, qb, N=N, out_dtype=torch.bfloat16, groups=2, offsets=torch.from_numpy(offsets).to(DEV),
+                    a_format=afmt)
+    ref2, tol2 = _grouped_ref(ah, bh, offsets, N, "bf16")
+    got2 = host(c2.float()).astype(np.float64)
+    assert np.all(np.abs(got2 - ref2) <= tol2), np.abs(got2 - ref2).max()
+
+
+# ----------------------------------------------------------- W8A16 / W6A16 GEMV
+@pytest.mark.parametrize("fmt", WIDE)
+@pytest.mark.parametrize("M", [1, 2, 3, 5, 8, 16])
+def test_wide_gemv(fmt, M):
+    """MXFP8 / MXFP6 weights with bf16 activations: N = 300 (a ragged last
+    workgroup of 32 rows), K = 4160 (two full 2048-element windows and a
+    partial third)."""
+    N, K = 300, 4160
+    announce(f"wide gemv {fmt} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 13 + WIDE.index(fmt))
+    x = bf16_values(rng.standard_normal((M, K)).astype(np.float32) * 2)
+    w = hard_inputs(N, K, M + 1, fmt) * np.float32(1e-3)
+    wq = mx.mx_quantize(torch.from_numpy(w).to(DEV), fmt)
+    wh = O.dequantize_fmt(fmt, host(wq.codes), host(wq.scales))
+    y = host(mx.mx_gemv(torch.from_numpy(x).to(torch.bfloat16).to(DEV), wq).float()).astype(np.float64)
+    yref = O.gemm(x, wh, out="bf16")
+    tol = O.gemm_tolerance(x, wh, yref, out="bf16")
+    bad = np.abs(y - yref) > tol
+    assert not bad.any(), (np.argwhere(bad)[:5], np.abs(y - yref).max())
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8_e4m3", "mxfp6_e3m2"])
+def test_wide_gemv_strided(fmt):
+    """Activation and output rows as column slices of wider tensors."""
+    M, N, K = 8, 64, 1024
+    announce(f"wide gemv strided {fmt}")
+    rng = np.random.default_rng(99)
+    x = bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    w = (rng.standard_normal((N, K)) * 0.05).astype(np.float32)
+    wq = mx.mx_quantize(torch.from_numpy(w).to(DEV), fmt)
+    wh = O.dequantize_fmt(fmt, host(wq.codes), host(wq.scales))
+    xw = torch.zeros(M, K + 128, dtype=torch.bfloat16, device=DEV)
+    xw[:, :K] = torch.from_numpy(x).to(torch.bfloat16).to(DEV)
+    xw[:, K:] = float("nan")                      # never read
+    yw = torch.full((M, N + 32), -1.0, dtype=torch.bfloat16, device=DEV)
+    mx.mx_gemv(xw[:, :K], wq, out=yw[:, :N])
+    got = host(yw.float()).astype(np.float64)
+    yref = O.gemm(x, wh, out="bf16")
+    assert np.all(np.abs(got[:, :N] - yref) <= O.gemm_tolerance(x, wh, yref, out="bf16"))
+    assert np.all(got[:, N:] == -1.0)
