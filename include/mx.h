@@ -330,8 +330,13 @@ int mx_gemv(const void *x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_te
  *   src_token  device int32 [tokens * topk] out: token of sorted row r for
  *              r < offsets[experts] (entries beyond are not written)
  *   workspace  device, >= mx_workspace_bytes(MX_OP_MOE_ROUTE, &experts) bytes
+ *              (per-expert totals and per-chunk counts: 4 * (experts +
+ *              max(1, 65536 / experts) * experts) bytes, at most 512 KiB)
  * Pairs of one expert keep their flat order t * topk + s, so the result is
- * unique.  1 <= topk, 1 <= experts <= 65536, tokens * topk < 2^31.
+ * unique.  Four launches, each linear in the pairs plus the chunk counts:
+ * per-chunk counts, their prefix per expert, the expert offsets, and one
+ * wave per chunk that gives its pairs their rows in order.
+ * 1 <= topk, 1 <= experts <= 65536, tokens * topk < 2^31.
  */
 int mx_moe_route(const int32_t *topk_ids, int64_t tokens, int32_t topk, int32_t experts,
                  int32_t *offsets, int32_t *dest_row, int32_t *src_token,

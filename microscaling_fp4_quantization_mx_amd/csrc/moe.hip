@@ -10,89 +10,141 @@
 //   combine : out[t] = sum_s w[t, s] * y[row(t, s)]
 // Every step is deterministic: the sort is stable (pairs of one expert keep
 // their flat order t * topk + s) and the combine sums the slots in order.
+#include <algorithm>
+
 #include "mx_device.h"
 #include "mx_kernels.h"
 
 namespace mxk {
 
-constexpr int RT = 256;   // threads per workgroup of the routing kernels
+constexpr int RT = 256;   // threads per workgroup of the counting kernels
 
-// Workgroup g counts the pairs routed to expert g.
-__global__ __launch_bounds__(RT) void k_route_count(const int32_t* __restrict__ ids, int npairs, int32_t* __restrict__ cnt) {
-  __shared__ int red[RT / 64];
-  const int g = blockIdx.x;
-  int c = 0;
-  for (int p = threadIdx.x; p < npairs; p += RT) c += ids[p] == g;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) c += __shfl_xor(c, m, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = c;
+// The pairs are cut into C chunks of `ch` consecutive pairs (ch a multiple of
+// 64, at least kRouteChunkMin unless there are fewer pairs), with
+// C * experts <= kRouteTable, so that the per-chunk counts fit a workspace
+// whose size depends on the expert count only.  Every pass is linear in the
+// pairs plus C * experts: one counting pass over the pairs, a scan over the
+// counts, one assignment pass over the pairs.
+constexpr int kRouteTable = 1 << 16;
+constexpr int kRouteChunkMin = 1024;
+
+int route_max_chunks(int experts) { return experts >= kRouteTable ? 1 : kRouteTable / experts; }
+
+// Workgroup c counts the pairs of chunk c per expert: hist[c][e].
+__global__ __launch_bounds__(RT) void k_route_hist(const int32_t* __restrict__ ids, int npairs, int experts, int ch,
+                                                   int32_t* __restrict__ hist) {
+  const int c = blockIdx.x;
+  int32_t* row = hist + (size_t)c * experts;
+  for (int e = threadIdx.x; e < experts; e += RT) row[e] = 0;
+  __threadfence();   // the zeros are in memory before any lane's increment
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int t = 0;
-#pragma unroll
-    for (int w = 0; w < RT / 64; ++w) t += red[w];
-    cnt[g] = t;
+  const int64_t p0 = (int64_t)c * ch, p1 = min((int64_t)npairs, p0 + ch);
+  for (int64_t p = p0 + threadIdx.x; p < p1; p += RT) {
+    const int e = ids[p];
+    if (e >= 0 && e < experts) atomicAdd(&row[e], 1);
   }
 }
 
-// Workgroup g < experts: offsets[g] = sum of the counts before g, then the
-// pairs of expert g in flat order get rows offsets[g], offsets[g] + 1, ...
-// (chunks of 256 pairs; a pair's rank inside a chunk is a ballot popcount
-// plus the counts of the waves before it).  Workgroup `experts` marks pairs
-// whose expert id is out of range with row -1 and writes offsets[experts].
-__global__ __launch_bounds__(RT) void k_route_assign(const int32_t* __restrict__ ids, int npairs, int topk, int experts,
-                                                     const int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token) {
-  __shared__ int wsum[RT / 64];
-  __shared__ int base_sh;
-  const int g = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (g == experts) {
-    int total = 0;
-    for (int e = 0; e < experts; ++e) total += cnt[e];
-    if (tid == 0) offsets[experts] = total;
-    for (int p = tid; p < npairs; p += RT) {
-      const int e = ids[p];
-      if (e < 0 || e >= experts) dest_row[p] = -1;
-    }
-    return;
+// Thread e: hist[c][e] <- pairs of expert e in chunks before c (exclusive
+// prefix down the column), tot[e] <- all pairs of expert e.
+__global__ __launch_bounds__(RT) void k_route_colscan(int chunks, int experts, int32_t* __restrict__ hist,
+                                                      int32_t* __restrict__ tot) {
+  const int e = blockIdx.x * RT + threadIdx.x;
+  if (e >= experts) return;
+  int run = 0;
+  for (int c = 0; c < chunks; ++c) {
+    const int h = hist[(size_t)c * experts + e];
+    hist[(size_t)c * experts + e] = run;
+    run += h;
   }
-  if (tid == 0) {
-    int off = 0;
-    for (int e = 0; e < g; ++e) off += cnt[e];
-    base_sh = off;
-    offsets[g] = off;
-  }
+  tot[e] = run;
+}
+
+// One workgroup: offsets[g] = sum_{e < g} tot[e] for g = 0 .. experts.
+constexpr int RO_T = 1024;
+__global__ __launch_bounds__(RO_T) void k_route_offsets(int experts, const int32_t* __restrict__ tot,
+                                                        int32_t* __restrict__ offsets) {
+  __shared__ int part[RO_T];
+  const int t = threadIdx.x;
+  const int per = (experts + RO_T - 1) / RO_T;
+  const int e0 = min(experts, t * per), e1 = min(experts, e0 + per);
+  int s = 0;
+  for (int e = e0; e < e1; ++e) s += tot[e];
+  part[t] = s;
   __syncthreads();
-  int base = base_sh;
-  for (int p0 = 0; p0 < npairs; p0 += RT) {
-    const int p = p0 + tid;
-    const bool hit = p < npairs && ids[p] == g;
-    const uint64_t bal = __ballot(hit);
-    const int before = __popcll(bal & ((uint64_t(1) << lane) - 1));
-    if (lane == 0) wsum[wave] = __popcll(bal);
+  // inclusive scan of the per-thread sums (Hillis-Steele)
+  for (int d = 1; d < RO_T; d <<= 1) {
+    const int v = t >= d ? part[t - d] : 0;
     __syncthreads();
-    int woff = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < RT / 64; ++w) {
-      woff += w < wave ? wsum[w] : 0;
-      tot += wsum[w];
-    }
-    if (hit) {
-      const int row = base + woff + before;
-      dest_row[p] = row;
-      src_token[row] = p / topk;
-    }
-    base += tot;
-    __syncthreads();   // wsum is rewritten by the next chunk
+    part[t] += v;
+    __syncthreads();
   }
+  int run = t ? part[t - 1] : 0;
+  for (int e = e0; e < e1; ++e) {
+    offsets[e] = run;
+    run += tot[e];
+  }
+  if (t == RO_T - 1) offsets[experts] = part[RO_T - 1];
+}
+
+// One wave per chunk walks its pairs in order, 64 at a time.  The lanes
+// holding the same expert v form a ballot mask; their rows are
+// offsets[v] + (pairs of v before this chunk and before these 64 pairs)
+// + the lane's rank in the mask, so every expert's pairs keep their flat
+// order.  hist[c][v] (the count before this chunk) advances by the mask's
+// popcount as the chunk proceeds; only this wave touches row c.
+__global__ __launch_bounds__(64) void k_route_assign(const int32_t* __restrict__ ids, int npairs, int topk, int experts,
+                                                     int ch, const int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ hist, int32_t* __restrict__ dest_row,
+                                                     int32_t* __restrict__ src_token) {
+  const int c = blockIdx.x, lane = threadIdx.x;
+  int32_t* row = hist + (size_t)c * experts;
+  const int64_t p0 = (int64_t)c * ch, p1 = min((int64_t)npairs, p0 + ch);
+  for (int64_t q = p0; q < p1; q += 64) {
+    const int64_t p = q + lane;
+    const bool in = p < p1;
+    const int e = in ? ids[p] : -1;
+    const bool valid = in && e >= 0 && e < experts;
+    if (in && !valid) dest_row[p] = -1;
+    uint64_t todo = __ballot(valid);
+    while (todo) {
+      const int leader = __builtin_ctzll(todo);
+      const int v = __shfl(e, leader, 64);
+      const uint64_t mask = __ballot(valid && e == v);
+      int before = 0;
+      if (lane == leader) before = atomicAdd(&row[v], __popcll(mask));
+      before = __shfl(before, leader, 64);
+      if ((mask >> lane) & 1) {
+        const int r = offsets[v] + before + __popcll(mask & ((uint64_t(1) << lane) - 1));
+        dest_row[p] = r;
+        src_token[r] = (int)(p / topk);
+      }
+      todo &= ~mask;
+    }
+  }
+}
+
+size_t route_workspace_bytes(int experts) {
+  return ((size_t)experts + (size_t)route_max_chunks(experts) * experts) * sizeof(int32_t);
 }
 
 hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int experts, int32_t* offsets,
-                            int32_t* dest_row, int32_t* src_token, int32_t* cnt, hipStream_t st) {
-  hipLaunchKernelGGL(k_route_count, dim3(experts), dim3(RT), 0, st, ids, (int)npairs, cnt);
-  hipLaunchKernelGGL(k_route_assign, dim3(experts + 1), dim3(RT), 0, st, ids, (int)npairs, topk, experts, cnt, offsets,
-                     dest_row, src_token);
+                            int32_t* dest_row, int32_t* src_token, int32_t* ws, hipStream_t st) {
+  const int np = (int)npairs;
+  int chunks = 0, ch = 64;
+  if (np > 0) {
+    chunks = (int)std::min<int64_t>((npairs + kRouteChunkMin - 1) / kRouteChunkMin, route_max_chunks(experts));
+    ch = (int)(((npairs + chunks - 1) / chunks + 63) / 64 * 64);
+    chunks = (int)((npairs + ch - 1) / ch);
+  }
+  int32_t* tot = ws;
+  int32_t* hist = ws + experts;
+  if (chunks > 0) hipLaunchKernelGGL(k_route_hist, dim3(chunks), dim3(RT), 0, st, ids, np, experts, ch, hist);
+  hipLaunchKernelGGL(k_route_colscan, dim3((experts + RT - 1) / RT), dim3(RT), 0, st, chunks, experts, hist, tot);
+  hipLaunchKernelGGL(k_route_offsets, dim3(1), dim3(RO_T), 0, st, experts, tot, offsets);
+  if (chunks > 0)
+    hipLaunchKernelGGL(k_route_assign, dim3(chunks), dim3(64), 0, st, ids, np, topk, experts, ch, offsets, hist,
+                       dest_row, src_token);
   return hipGetLastError();
 }
 

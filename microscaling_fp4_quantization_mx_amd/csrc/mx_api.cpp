@@ -150,7 +150,7 @@ size_t mx_workspace_bytes(int32_t op, const void* desc, int32_t flags) {
   }
   if (op == MX_OP_MOE_ROUTE) {
     const int32_t experts = *static_cast<const int32_t*>(desc);
-    return experts > 0 ? round256((size_t)experts * 4) : 0;
+    return experts > 0 && experts <= kMaxExperts ? round256(mxk::route_workspace_bytes(experts)) : 0;
   }
   return 0;
 }
@@ -363,7 +363,7 @@ int mx_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t 
   if (!offsets) return MX_ERR_NULL;
   if (npairs > 0 && (!topk_ids || !dest_row || !src_token)) return MX_ERR_NULL;
   if (!al4(offsets) || (npairs > 0 && (!al4(topk_ids) || !al4(dest_row) || !al4(src_token)))) return MX_ERR_ALIGN;
-  if (!workspace || workspace_bytes < (size_t)experts * 4 || !al4(workspace)) return MX_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < mxk::route_workspace_bytes(experts) || !al4(workspace)) return MX_ERR_WORKSPACE;
   return hip_status(mxk::launch_moe_route(topk_ids, npairs, topk, experts, offsets, dest_row, src_token,
                                           static_cast<int32_t*>(workspace), as_stream(stream)));
 }

@@ -199,9 +199,12 @@ def test_moe_validation():
     assert L.mx_moe_route(FAKE + 2, 10, 2, 8, FAKE, FAKE, FAKE, ws, 4096, None) == -3    # misaligned ids
     assert L.mx_moe_route(FAKE, 10, 2, 8, FAKE, FAKE, FAKE, None, 0, None) == -7         # no workspace
     assert L.mx_moe_route(FAKE, 10, 2, 8, FAKE, FAKE, FAKE, ws, 16, None) == -7          # too small
-    e = ctypes.c_int32(300)
-    need = L.mx_workspace_bytes(mx.MX_OP_MOE_ROUTE, ctypes.cast(ctypes.pointer(e), ctypes.c_void_p), 0)
-    assert need >= 1200 and need % 256 == 0
+    for experts, chunks in ((300, 65536 // 300), (8, 8192), (1 << 16, 1)):
+        e = ctypes.c_int32(experts)
+        need = L.mx_workspace_bytes(mx.MX_OP_MOE_ROUTE, ctypes.cast(ctypes.pointer(e), ctypes.c_void_p), 0)
+        assert need == (4 * (experts + chunks * experts) + 255) // 256 * 256       # totals + per-chunk counts
+        exact = 4 * (experts + chunks * experts)
+        assert L.mx_moe_route(FAKE, 10, 2, experts, FAKE, FAKE, FAKE, ws, exact - 4, None) == -7
     # mx_quantize_rows(x, dtype, ld, x_rows, row_index, out, stream)
     t = T(rows=16, cols=256)
     assert L.mx_quantize_rows(FAKE, 0, 256, 10, None, ctypes.byref(t), None) == -1

@@ -43,8 +43,12 @@ def ulp_bf16(v):
 
 
 @pytest.mark.parametrize("T,k,G,bad", [(0, 2, 4, 0), (1, 1, 1, 0), (37, 2, 4, 3), (1000, 2, 8, 10),
-                                       (513, 4, 300, 5), (64, 1, 3, 64)])
+                                       (513, 4, 300, 5), (64, 1, 3, 64), (30000, 2, 8, 100),
+                                       (600, 4, 1024, 20), (20, 2, 65536, 2), (4096, 2, 8, 0)])
 def test_route_bit_exact(T, k, G, bad):
+    """Stable expert order, including several chunks of pairs (2000 pairs and
+    more), more experts than one counting workgroup's threads, and the largest
+    expert count (a single chunk)."""
     announce(f"route T={T} topk={k} experts={G} invalid={bad}")
     rng = np.random.default_rng(T * 7 + G)
     ids = rng.integers(0, G, size=(T, k)).astype(np.int32)
