@@ -20,9 +20,10 @@ quantize + GEMM 2048x28672x8192, the fused dynamic-quantize grouped GEMM
 (8 experts, N=4096, K=14336, 8192 tokens), the routed expert layer
 around it (4096 tokens, top-2: route, gathered quantize, grouped GEMM,
 combine), the fused RMSNorm + quantize, and MXFP8 / MXFP6 products on the
-4096x8192x8192 shape (FP8 x FP4, FP8 x FP8, FP6 x FP6), and the
+4096x8192x8192 shape (FP8 x FP4, FP8 x FP8, FP6 x FP6), the
 quantization variants (16-element E8M0 blocks, the OCP floor rule, naive
-per-tensor FP4, ...) with the reconstruction SNR of each.
+per-tensor FP4, ...) with the reconstruction SNR of each, and the vendor
+library's MXFP4 GEMM (hipBLASLt) on the headline shape beside libmx's.
 
 Ceilings (`secondary.ceilings`): a plain streaming read of the GEMV's bytes
 and plain copies, the practical bounds beside the 8 TB/s peak.
@@ -111,7 +112,8 @@ def summarize_trace(dirs, out_path, title, command):
     lines += ["# Durations are End - Start per dispatch in microseconds (warm-up and graph-capture calls included).",
               f"{'kernel':60s} {'grid':>9s} {'calls':>6s} {'avg_us':>9s} {'median_us':>9s} {'min_us':>9s}"]
     for (name, grid), v in sorted(d.items()):
-        if not name.startswith("mxk::"):
+        # libmx's kernels, and the vendor library's GEMM timed beside them
+        if not (name.startswith("mxk::") or "GEMM" in name or "Cijk" in name):
             continue
         lines.append(f"{name:60s} {grid:>9s} {len(v):6d} {sum(v) / len(v):9.2f} {statistics.median(v):9.2f} "
                      f"{min(v):9.2f}")
@@ -221,7 +223,7 @@ def bench_main(args, torch, mx, W):
     qw_bytes = N * K * 4 + N * K // 2 + N * K // 32
     gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * 2
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
-    gfiles = ["gemm_mxfp4.hip", "gemm_mx_tile.h", "mx_device.h"]
+    gfiles = ["gemm_mxfp4.hip", "gemm_mx_tile.h", "gemm_tiles.h", "mx_device.h"]
     gsum = "mxfp4_gemm_4096x8192x8192_counters.txt"
     traffic = kernel_counter(gsum, gfiles, "k_gemm_mx_k256", 131072, "hbm_bytes")
     res = {
@@ -294,11 +296,30 @@ def bench_gemv(args, torch, mx, W):
                                           "frac_hbm": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                                           "note": "dot2 kernel (no matrix cores)"}
     del ws2
+    # W8A16 / W6A16: the same product with MXFP8 E4M3 / MXFP6 E2M3 weights
+    # (the dot2 kernel for every M; 2x / 1.5x the weight bytes of MXFP4)
+    wt = torch.from_numpy(d["w"]).to(dev)
+    for fmt, bits in (("mxfp8_e4m3", 8), ("mxfp6_e2m3", 6)):
+        wsf = [mx.mx_quantize(wt, fmt) for _ in range(reps)]
+        for M in (1, 16):
+            x = torch.from_numpy(d["x"][:M]).to(torch.bfloat16).to(dev)
+            y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+            def batch3():
+                for i in range(reps):
+                    mx.mx_gemv(x, wsf[i], out=y)
+            g = capture(torch, batch3, max(1, args.gemv_iters // reps))
+            ms = time_graph(torch, g, reps * max(1, args.gemv_iters // reps))
+            byt = N * K * bits // 8 + N * K // 32 + 2 * M * K + 2 * M * N
+            out[f"{fmt}_M={M}"] = {"avg_ms": ms, "GB/s": byt / (ms * 1e-3) / 1e9,
+                                   "frac_hbm": byt / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "bytes": byt}
+        del wsf
+    del wt
     for M, kern in ((1, "k_gemv_sk"), (8, "k_gemv_mf"), (16, "k_gemv_mf")):
         g = out[f"M={M}"]
         out[f"roofline_M{M}"] = {"bound": "hbm", "achieved": g["GB/s"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": g["frac_hbm"],
-                                 "traffic": kernel_counter("gemv_8192x8192_counters.txt", ["gemv.hip", "mx_device.h"],
+                                 "traffic": kernel_counter("gemv_8192x8192_counters.txt", ["gemv.hip", "mx_expand.h", "mx_device.h"],
                                                            f"{kern}<{M}" if kern == "k_gemv_mf" else kern,
                                                            131072, "hbm_bytes")}
     return out
@@ -538,6 +559,99 @@ def bench_ceilings(args, torch, mx, W):
     return out
 
 
+def bench_vendor(args, torch, mx, W):
+    """The vendor library's MXFP4 GEMM on the headline shape, for context:
+    torch._scaled_mm on float4_e2m1fn_x2 operands with E8M0 scale bytes,
+    which ROCm's torch hands to hipBLASLt (its kernel name is in the kernel
+    trace summary).  Both GEMMs run on the same seeded random codes, eagerly
+    and back to back (no graph: the library call is not captured), libmx
+    through its C entry point with prebuilt arguments; HIP events on the
+    current stream; the two alternate in rounds after a warm-up and each
+    reports its best round (the clock settles over the first tens of
+    milliseconds of load).  Every scale byte is 127 (2^0): the result then
+    does not depend on the library's scale layout, and every fp32 partial sum
+    of E2M1 products is exact (multiples of 1/4 below 2^22), so libmx's fp32
+    output is the exact product; the bf16 outputs are compared with its
+    round-to-nearest-even and its truncation."""
+    import ctypes
+    w = W.C3
+    M, N, K = w.M, w.N, w.K
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260)
+    sets = []
+    for _ in range(2):
+        a = mx.empty_quantized(M, K, "mxfp4", dev)
+        b = mx.empty_quantized(N, K, "mxfp4", dev)
+        for t in (a, b):
+            t.codes.copy_(torch.randint(0, 256, t.codes.shape, dtype=torch.uint8, device=dev, generator=gen))
+            t.scales.fill_(127)
+        sets.append((a, b))
+    c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+
+    def vendor(a, b):
+        return torch._scaled_mm(a.codes.view(torch.float4_e2m1fn_x2), b.codes.view(torch.float4_e2m1fn_x2).t(),
+                                a.scales.view(torch.float8_e8m0fnu).flatten(),
+                                b.scales.view(torch.float8_e8m0fnu).flatten(), out_dtype=torch.bfloat16)
+    out = {"library": "hipBLASLt through torch._scaled_mm (float4_e2m1fn_x2, E8M0 scales)",
+           "shape": [M, N, K]}
+    try:
+        y = vendor(*sets[0])
+    except Exception as ex:   # torch or library without MXFP4 support
+        out["error"] = f"{type(ex).__name__}: {str(ex)[:200]}"
+        return out
+    exact = mx.mx_gemm(*sets[0], out_dtype=torch.float32)
+    mx.mx_gemm(*sets[0], out=c)
+    torch.cuda.synchronize()
+    rne = exact.to(torch.bfloat16)
+    trunc = (exact.view(torch.int32) & ~0xFFFF).view(torch.float32).to(torch.bfloat16)
+    out["libmx_bf16_equals_rne_of_exact"] = bool(torch.equal(c, rne))
+    out["vendor_bf16_equals_rne_of_exact_frac"] = float((y == rne).float().mean())
+    out["vendor_bf16_equals_truncation_of_exact_frac"] = float((y == trunc).float().mean())
+    del y, exact, rne, trunc
+    stream = torch.cuda.current_stream()
+    flops = 2.0 * M * N * K
+    L = mx.lib()
+    descs, cargs = [], []
+    for a, b in sets:
+        ad, bd = a.desc(), b.desc()
+        g = mx.CMxGemmArgs()
+        g.M, g.N, g.K = M, N, K
+        g.a, g.b = ctypes.pointer(ad), ctypes.pointer(bd)
+        g.c, g.c_dtype, g.ldc = c.data_ptr(), mx.MX_DT_BF16, N
+        descs += [ad, bd]
+        cargs.append(g)
+    sp = stream.cuda_stream
+
+    def libmx(i):
+        assert L.mx_gemm(ctypes.byref(cargs[i % 2]), sp) == 0
+
+    def vend(i):
+        vendor(*sets[i % 2])
+    reps = max(20, args.side_iters * 5)
+    for i in range(200):          # about 60 ms of load before the first timed round
+        libmx(i)
+        vend(i)
+    torch.cuda.synchronize()
+    best = {}
+    for _ in range(3):
+        for name, fn in (("libmx", libmx), ("vendor", vend)):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            for i in range(reps):
+                fn(i)
+            e.record(stream)
+            torch.cuda.synchronize()
+            best[name] = min(best.get(name, 1e30), s.elapsed_time(e) / reps)
+    for name, ms in best.items():
+        out[f"{name}_avg_ms"] = ms
+        out[f"{name}_TFLOPS"] = flops / (ms * 1e-3) / 1e12
+        out[f"{name}_frac_fp4_peak"] = flops / (ms * 1e-3) / 1e12 / PEAK_FP4_TFLOPS
+    out["libmx_speedup_over_vendor"] = best["vendor"] / best["libmx"]
+    del sets
+    return out
+
+
 SECONDARY = {
     "ceilings": (bench_ceilings, "ceilings"),
     "gemv": (bench_gemv, "w4a16_gemv_8192x8192"),
@@ -547,6 +661,7 @@ SECONDARY = {
     "grouped": (bench_grouped, "grouped_8x4096x14336_T8192"),
     "rmsnorm": (bench_rmsnorm, "rmsnorm_quantize_8192x14336_bf16"),
     "moe": (bench_moe, "moe_top2_8x4096x14336_T4096"),
+    "vendor": (bench_vendor, "vendor_mxfp4_gemm_4096x8192x8192"),
 }
 SECONDARY_NAMES = tuple(SECONDARY)
 
