@@ -437,6 +437,12 @@ def bench_grouped(args, torch, mx, W):
             "fused_note": "the same call with MX_GEMM_FUSED_QUANTIZE: quantization and GEMM in one persistent kernel"}
 
 
+def route_ws_bytes(mx, experts):
+    import ctypes
+    e = ctypes.c_int32(experts)
+    return int(mx.lib().mx_workspace_bytes(mx.MX_OP_MOE_ROUTE, ctypes.cast(ctypes.pointer(e), ctypes.c_void_p), 0))
+
+
 def bench_moe(args, torch, mx, W):
     """Routed expert layer: route (top-2 of 8) + gathered MXFP4 quantize of the
     bf16 tokens + grouped W4A4 GEMM (bf16 y) + weighted combine, one graph."""
@@ -452,7 +458,7 @@ def bench_moe(args, torch, mx, W):
     bufs = {"offsets": torch.empty(G + 1, dtype=torch.int32, device=dev),
             "dest_row": torch.empty(P, dtype=torch.int32, device=dev),
             "src_token": torch.empty(P, dtype=torch.int32, device=dev),
-            "route_ws": torch.empty(4096, dtype=torch.uint8, device=dev),
+            "route_ws": torch.empty(route_ws_bytes(mx, G), dtype=torch.uint8, device=dev),
             "aq": mx.empty_quantized(P, K, "mxfp4", dev),
             "y": torch.empty(P, N, dtype=torch.bfloat16, device=dev),
             "out": torch.empty(T, N, dtype=torch.bfloat16, device=dev)}

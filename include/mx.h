@@ -330,12 +330,12 @@ int mx_gemv(const void *x, int32_t x_dtype, int64_t M, int64_t ld_x, const mx_te
  *   src_token  device int32 [tokens * topk] out: token of sorted row r for
  *              r < offsets[experts] (entries beyond are not written)
  *   workspace  device, >= mx_workspace_bytes(MX_OP_MOE_ROUTE, &experts) bytes
- *              (per-expert totals and per-chunk counts: 4 * (experts +
- *              max(1, 65536 / experts) * experts) bytes, at most 512 KiB)
+ *              (per-chunk counts: 4 * max(1, 65536 / experts) * experts
+ *              bytes, at most 256 KiB)
  * Pairs of one expert keep their flat order t * topk + s, so the result is
- * unique.  Four launches, each linear in the pairs plus the chunk counts:
- * per-chunk counts, their prefix per expert, the expert offsets, and one
- * wave per chunk that gives its pairs their rows in order.
+ * unique.  Three launches, each linear in the pairs plus the chunk counts:
+ * counts per chunk of consecutive pairs, one prefix over them (expert by
+ * expert), and one wave per chunk that gives its pairs their rows in order.
  * 1 <= topk, 1 <= experts <= 65536, tokens * topk < 2^31.
  */
 int mx_moe_route(const int32_t *topk_ids, int64_t tokens, int32_t topk, int32_t experts,

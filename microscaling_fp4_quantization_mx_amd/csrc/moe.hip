@@ -17,88 +17,98 @@
 
 namespace mxk {
 
-constexpr int RT = 256;   // threads per workgroup of the counting kernels
+constexpr int RT = 256;   // threads per workgroup of the counting kernel
 
 // The pairs are cut into C chunks of `ch` consecutive pairs (ch a multiple of
-// 64, at least kRouteChunkMin unless there are fewer pairs), with
+// 64, at least kRouteChunk unless there are fewer pairs), with
 // C * experts <= kRouteTable, so that the per-chunk counts fit a workspace
-// whose size depends on the expert count only.  Every pass is linear in the
-// pairs plus C * experts: one counting pass over the pairs, a scan over the
-// counts, one assignment pass over the pairs.
+// whose size depends on the expert count only.  Each pass is linear in the
+// pairs plus C * experts: per-chunk counts, one scan over the counts, one
+// assignment pass over the pairs.  Counts live in LDS for up to
+// kRouteLdsExperts experts (global atomics beyond).
 constexpr int kRouteTable = 1 << 16;
-constexpr int kRouteChunkMin = 1024;
+constexpr int kRouteChunk = 256;
+constexpr int kRouteLdsExperts = 8192;
 
 int route_max_chunks(int experts) { return experts >= kRouteTable ? 1 : kRouteTable / experts; }
 
-// Workgroup c counts the pairs of chunk c per expert: hist[c][e].
+// Workgroup c: hist[c][e] = pairs of chunk c routed to expert e.
+template <bool LDS>
 __global__ __launch_bounds__(RT) void k_route_hist(const int32_t* __restrict__ ids, int npairs, int experts, int ch,
                                                    int32_t* __restrict__ hist) {
+  __shared__ int cnt[LDS ? kRouteLdsExperts : 1];
   const int c = blockIdx.x;
   int32_t* row = hist + (size_t)c * experts;
-  for (int e = threadIdx.x; e < experts; e += RT) row[e] = 0;
-  __threadfence();   // the zeros are in memory before any lane's increment
+  int* ctr = LDS ? cnt : row;
+  for (int e = threadIdx.x; e < experts; e += RT) ctr[e] = 0;
+  if (!LDS) __threadfence();   // the zeros are in memory before any lane's increment
   __syncthreads();
   const int64_t p0 = (int64_t)c * ch, p1 = min((int64_t)npairs, p0 + ch);
   for (int64_t p = p0 + threadIdx.x; p < p1; p += RT) {
     const int e = ids[p];
-    if (e >= 0 && e < experts) atomicAdd(&row[e], 1);
+    if (e >= 0 && e < experts) atomicAdd(&ctr[e], 1);
+  }
+  if (LDS) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < experts; e += RT) row[e] = cnt[e];
   }
 }
 
-// Thread e: hist[c][e] <- pairs of expert e in chunks before c (exclusive
-// prefix down the column), tot[e] <- all pairs of expert e.
-__global__ __launch_bounds__(RT) void k_route_colscan(int chunks, int experts, int32_t* __restrict__ hist,
-                                                      int32_t* __restrict__ tot) {
-  const int e = blockIdx.x * RT + threadIdx.x;
-  if (e >= experts) return;
-  int run = 0;
-  for (int c = 0; c < chunks; ++c) {
-    const int h = hist[(size_t)c * experts + e];
-    hist[(size_t)c * experts + e] = run;
-    run += h;
-  }
-  tot[e] = run;
-}
-
-// One workgroup: offsets[g] = sum_{e < g} tot[e] for g = 0 .. experts.
-constexpr int RO_T = 1024;
-__global__ __launch_bounds__(RO_T) void k_route_offsets(int experts, const int32_t* __restrict__ tot,
-                                                        int32_t* __restrict__ offsets) {
-  __shared__ int part[RO_T];
+// One workgroup: exclusive prefix of the counts taken expert by expert and,
+// within an expert, chunk by chunk; hist[c][e] becomes the first row of the
+// pairs of expert e in chunk c, offsets[e] the first row of expert e, and
+// offsets[experts] the number of routed pairs.
+constexpr int RS_T = 1024;
+__global__ __launch_bounds__(RS_T) void k_route_scan(int chunks, int experts, int32_t* __restrict__ hist,
+                                                     int32_t* __restrict__ offsets) {
+  __shared__ int part[RS_T];
   const int t = threadIdx.x;
-  const int per = (experts + RO_T - 1) / RO_T;
-  const int e0 = min(experts, t * per), e1 = min(experts, e0 + per);
+  const int n = chunks * experts;
+  if (n == 0) {   // no pairs: every expert is empty
+    for (int e = t; e <= experts; e += RS_T) offsets[e] = 0;
+    return;
+  }
+  const int per = (n + RS_T - 1) / RS_T;
+  const int i0 = min(n, t * per), i1 = min(n, i0 + per);
+  auto at = [&](int i) -> int32_t& { return hist[(size_t)(i % chunks) * experts + i / chunks]; };   // i = e * C + c
   int s = 0;
-  for (int e = e0; e < e1; ++e) s += tot[e];
+  for (int i = i0; i < i1; ++i) s += at(i);
   part[t] = s;
   __syncthreads();
-  // inclusive scan of the per-thread sums (Hillis-Steele)
-  for (int d = 1; d < RO_T; d <<= 1) {
+  for (int d = 1; d < RS_T; d <<= 1) {   // inclusive scan of the per-thread sums
     const int v = t >= d ? part[t - d] : 0;
     __syncthreads();
     part[t] += v;
     __syncthreads();
   }
   int run = t ? part[t - 1] : 0;
-  for (int e = e0; e < e1; ++e) {
-    offsets[e] = run;
-    run += tot[e];
+  for (int i = i0; i < i1; ++i) {
+    const int h = at(i);
+    at(i) = run;
+    if (i % chunks == 0) offsets[i / chunks] = run;
+    run += h;
   }
-  if (t == RO_T - 1) offsets[experts] = part[RO_T - 1];
+  if (t == RS_T - 1) offsets[experts] = part[RS_T - 1];
 }
 
 // One wave per chunk walks its pairs in order, 64 at a time.  The lanes
-// holding the same expert v form a ballot mask; their rows are
-// offsets[v] + (pairs of v before this chunk and before these 64 pairs)
-// + the lane's rank in the mask, so every expert's pairs keep their flat
-// order.  hist[c][v] (the count before this chunk) advances by the mask's
-// popcount as the chunk proceeds; only this wave touches row c.
+// holding the same expert v form a ballot mask; their rows are the next
+// free row of v in this chunk plus the lane's rank in the mask, so every
+// expert's pairs keep their flat order.  The chunk's next free rows start
+// from the scanned counts and advance by the masks' popcounts (in LDS, or
+// in the chunk's own workspace row with atomics beyond kRouteLdsExperts
+// experts).
+template <bool LDS>
 __global__ __launch_bounds__(64) void k_route_assign(const int32_t* __restrict__ ids, int npairs, int topk, int experts,
-                                                     int ch, const int32_t* __restrict__ offsets,
-                                                     int32_t* __restrict__ hist, int32_t* __restrict__ dest_row,
+                                                     int ch, int32_t* __restrict__ hist, int32_t* __restrict__ dest_row,
                                                      int32_t* __restrict__ src_token) {
+  __shared__ int nxt[LDS ? kRouteLdsExperts : 1];
   const int c = blockIdx.x, lane = threadIdx.x;
   int32_t* row = hist + (size_t)c * experts;
+  if (LDS) {
+    for (int e = lane; e < experts; e += 64) nxt[e] = row[e];
+    __syncthreads();
+  }
   const int64_t p0 = (int64_t)c * ch, p1 = min((int64_t)npairs, p0 + ch);
   for (int64_t q = p0; q < p1; q += 64) {
     const int64_t p = q + lane;
@@ -111,11 +121,18 @@ __global__ __launch_bounds__(64) void k_route_assign(const int32_t* __restrict__
       const int leader = __builtin_ctzll(todo);
       const int v = __shfl(e, leader, 64);
       const uint64_t mask = __ballot(valid && e == v);
-      int before = 0;
-      if (lane == leader) before = atomicAdd(&row[v], __popcll(mask));
-      before = __shfl(before, leader, 64);
+      int first = 0;
+      if (lane == leader) {
+        if (LDS) {
+          first = nxt[v];
+          nxt[v] = first + __popcll(mask);
+        } else {
+          first = atomicAdd(&row[v], __popcll(mask));
+        }
+      }
+      first = __shfl(first, leader, 64);
       if ((mask >> lane) & 1) {
-        const int r = offsets[v] + before + __popcll(mask & ((uint64_t(1) << lane) - 1));
+        const int r = first + __popcll(mask & ((uint64_t(1) << lane) - 1));
         dest_row[p] = r;
         src_token[r] = (int)(p / topk);
       }
@@ -125,7 +142,7 @@ __global__ __launch_bounds__(64) void k_route_assign(const int32_t* __restrict__
 }
 
 size_t route_workspace_bytes(int experts) {
-  return ((size_t)experts + (size_t)route_max_chunks(experts) * experts) * sizeof(int32_t);
+  return (size_t)route_max_chunks(experts) * experts * sizeof(int32_t);
 }
 
 hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int experts, int32_t* offsets,
@@ -133,18 +150,24 @@ hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int ex
   const int np = (int)npairs;
   int chunks = 0, ch = 64;
   if (np > 0) {
-    chunks = (int)std::min<int64_t>((npairs + kRouteChunkMin - 1) / kRouteChunkMin, route_max_chunks(experts));
+    chunks = (int)std::min<int64_t>((npairs + kRouteChunk - 1) / kRouteChunk, route_max_chunks(experts));
     ch = (int)(((npairs + chunks - 1) / chunks + 63) / 64 * 64);
     chunks = (int)((npairs + ch - 1) / ch);
   }
-  int32_t* tot = ws;
-  int32_t* hist = ws + experts;
-  if (chunks > 0) hipLaunchKernelGGL(k_route_hist, dim3(chunks), dim3(RT), 0, st, ids, np, experts, ch, hist);
-  hipLaunchKernelGGL(k_route_colscan, dim3((experts + RT - 1) / RT), dim3(RT), 0, st, chunks, experts, hist, tot);
-  hipLaunchKernelGGL(k_route_offsets, dim3(1), dim3(RO_T), 0, st, experts, tot, offsets);
-  if (chunks > 0)
-    hipLaunchKernelGGL(k_route_assign, dim3(chunks), dim3(64), 0, st, ids, np, topk, experts, ch, offsets, hist,
-                       dest_row, src_token);
+  const bool lds = experts <= kRouteLdsExperts;
+  if (chunks > 0) {
+    if (lds) hipLaunchKernelGGL(k_route_hist<true>, dim3(chunks), dim3(RT), 0, st, ids, np, experts, ch, ws);
+    else hipLaunchKernelGGL(k_route_hist<false>, dim3(chunks), dim3(RT), 0, st, ids, np, experts, ch, ws);
+  }
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(RS_T), 0, st, chunks, experts, ws, offsets);
+  if (chunks > 0) {
+    if (lds)
+      hipLaunchKernelGGL(k_route_assign<true>, dim3(chunks), dim3(64), 0, st, ids, np, topk, experts, ch, ws, dest_row,
+                         src_token);
+    else
+      hipLaunchKernelGGL(k_route_assign<false>, dim3(chunks), dim3(64), 0, st, ids, np, topk, experts, ch, ws,
+                         dest_row, src_token);
+  }
   return hipGetLastError();
 }
 

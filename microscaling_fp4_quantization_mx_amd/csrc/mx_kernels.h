@@ -63,7 +63,7 @@ hipError_t launch_dequant_naive(const uint8_t* codes, const float* s, int64_t ro
 // fmt: the weights' element format as the matrix-core code above (E2M1 4).
 hipError_t launch_gemv(int fmt, const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st);
-// ws: route_workspace_bytes(experts) bytes (per-expert totals, per-chunk counts)
+// ws: route_workspace_bytes(experts) bytes (per-chunk counts)
 size_t route_workspace_bytes(int experts);
 hipError_t launch_moe_route(const int32_t* ids, int64_t npairs, int topk, int experts, int32_t* offsets,
                             int32_t* dest_row, int32_t* src_token, int32_t* ws, hipStream_t st);

@@ -202,8 +202,8 @@ def test_moe_validation():
     for experts, chunks in ((300, 65536 // 300), (8, 8192), (1 << 16, 1)):
         e = ctypes.c_int32(experts)
         need = L.mx_workspace_bytes(mx.MX_OP_MOE_ROUTE, ctypes.cast(ctypes.pointer(e), ctypes.c_void_p), 0)
-        assert need == (4 * (experts + chunks * experts) + 255) // 256 * 256       # totals + per-chunk counts
-        exact = 4 * (experts + chunks * experts)
+        assert need == (4 * chunks * experts + 255) // 256 * 256                  # per-chunk counts
+        exact = 4 * chunks * experts
         assert L.mx_moe_route(FAKE, 10, 2, experts, FAKE, FAKE, FAKE, ws, exact - 4, None) == -7
     # mx_quantize_rows(x, dtype, ld, x_rows, row_index, out, stream)
     t = T(rows=16, cols=256)
