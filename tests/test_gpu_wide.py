@@ -379,3 +379,19 @@ def test_wide_gemv_strided(fmt):
     yref = O.gemm(x, wh, out="bf16")
     assert np.all(np.abs(got[:, :N] - yref) <= O.gemm_tolerance(x, wh, yref, out="bf16"))
     assert np.all(got[:, N:] == -1.0)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp8_e5m2", "mxfp6_e3m2"])
+@pytest.mark.parametrize("M,N,K", [(1, 1, 32), (4, 33, 64), (16, 7, 2080)])
+def test_wide_gemv_edges(fmt, M, N, K):
+    """One-block rows, a single output column, N below one workgroup's rows,
+    K one block past a 2048-element window."""
+    announce(f"wide gemv edges {fmt} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 7 + N + K)
+    x = bf16_values(rng.standard_normal((M, K)).astype(np.float32))
+    w = (rng.standard_normal((N, K)) * 0.1).astype(np.float32)
+    wq = mx.mx_quantize(torch.from_numpy(w).to(DEV), fmt)
+    wh = O.dequantize_fmt(fmt, host(wq.codes), host(wq.scales))
+    y = host(mx.mx_gemv(torch.from_numpy(x).to(torch.bfloat16).to(DEV), wq).float()).astype(np.float64)
+    yref = O.gemm(x, wh, out="bf16")
+    assert np.all(np.abs(y - yref) <= O.gemm_tolerance(x, wh, yref, out="bf16")), np.abs(y - yref).max()
