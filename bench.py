@@ -540,7 +540,9 @@ def bench_ceilings(args, torch, mx, W):
     the GEMV's weight bytes (35.7 MB, rotating over 16 buffers so every read
     comes from HBM) and plain copies of the quantize inputs' sizes, by the
     measurement-only kernels of libmx_ceiling.so (16-byte loads, four in
-    flight per lane); the best of 2, 4 and 8 workgroups per CU."""
+    flight per lane); the best of 2, 4 and 8 workgroups per CU.  Beside the
+    10.1 PF FP4 peak: the FP4 matrix-core rate of a register-only loop, and
+    the LDS rate of 16-byte fragment reads."""
     import ctypes
     L = ctypes.CDLL(os.path.join(ROOT, "microscaling_fp4_quantization_mx_amd", "libmx_ceiling.so"))
     L.mxc_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
@@ -575,6 +577,27 @@ def bench_ceilings(args, torch, mx, W):
             best = max(best or 0.0, 2 * nbytes / (ms * 1e-3) / 1e9)   # read + write
         out[name] = best
         del src, dsts
+    # on-chip rates of the GEMM's K loop: the FP4 matrix cores with operands in
+    # registers (two waves per SIMD), and 16-byte LDS fragment reads
+    L.mxc_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.mxc_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    grid, iters = 512, 2000
+    sinkf = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+
+    def fm():
+        assert L.mxc_mfma(sinkf.data_ptr(), grid, iters, torch.cuda.current_stream().cuda_stream) == 0
+    ms = time_graph(torch, capture(torch, fm, 4), 4)
+    out["mfma_fp4_32x32x64_register_loop_TFLOPS"] = grid * 4 * iters * 4 * 131072.0 / (ms * 1e-3) / 1e12
+    grid, iters = 256, 2000
+    sinku = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+
+    def fl():
+        assert L.mxc_lds(sinku.data_ptr(), grid, iters, torch.cuda.current_stream().cuda_stream) == 0
+    ms = time_graph(torch, capture(torch, fl, 4), 4)
+    lds_bytes = grid * 4 * iters * 8 * 1024.0
+    out["lds_read_b128_TB/s"] = lds_bytes / (ms * 1e-3) / 1e12
+    out["lds_read_b128_B_per_clk_per_CU_at_2.4GHz"] = lds_bytes / (ms * 1e-3) / 256 / 2.4e9
+    del sinkf, sinku
     return out
 
 
