@@ -8,8 +8,8 @@
 // cache line, which roughly doubles the per-CU L2 -> LDS rate over 64-byte
 // slices.  A stage is four K = 64 MFMA segments; each segment reads the next
 // segment's fragments while its 16 MFMAs run, and the refill of the slot just
-// consumed is issued before the last segment, so it has a whole stage of MFMA
-// time to land.
+// consumed is spread over the last two segments (one load per MFMA), so it
+// has about a stage of MFMA time to land.
 //
 // SP (K % 512 == 0): the scale bytes of two stages (16 per row) travel
 // together, one lane per row, into a three-entry ring of their own.  Loading a
@@ -38,6 +38,7 @@ struct MxTile {
   static constexpr int SCL_BUF = (BM + BN) * 16;
   static constexpr int SMEM = SP ? SCL_OFF + 3 * SCL_BUF : 2 * SLOT;   // 155648 / 139264
   static constexpr int LPS = SP ? 17 : 20;          // loads per wave per stage
+  static constexpr int LA = LPS - 8;                // of which A codes and scale bytes
 };
 
 // The four operand streams of one tile: codes and scale bytes of its A rows
@@ -69,7 +70,7 @@ __device__ __forceinline__ void mx_tile_mainloop(uint8_t* smem, const MxTileSrc&
   using C = MxTile<SP>;
   constexpr int BM = C::BM, BN = C::BN, WM = C::WM, WN = C::WN, NWX = C::NWX, TI = C::TI, TJ = C::TJ;
   constexpr int SLOT_A = C::SLOT_A, OFF_SA = C::OFF_SA, OFF_SB = C::OFF_SB, SLOT = C::SLOT;
-  constexpr int SCL_OFF = C::SCL_OFF, SCL_BUF = C::SCL_BUF, LPS = C::LPS;
+  constexpr int SCL_OFF = C::SCL_OFF, SCL_BUF = C::SCL_BUF, LPS = C::LPS, LA = C::LA;
   // opaque to the optimizer, so that in a persistent caller the per-thread
   // offsets below are formed per tile instead of held in registers across
   // the caller's whole job loop
@@ -99,17 +100,24 @@ __device__ __forceinline__ void mx_tile_mainloop(uint8_t* smem, const MxTileSrc&
                                              in ? srow + P * 16 : 0x7ffffff0, 0, 0, 0);
   };
   // All offsets in voffset (range checked); stages past the range load zeros.
-  auto issue = [&](int st) {
+  // A stage's loads go out in two parts: the A codes with the scale bytes
+  // (LA loads per wave), then the B codes (8).
+  auto issue_b = [&](int st) {
+    uint8_t* slot = smem + (st & 1) * SLOT;
+    const bool in = st < s1;
+    const int kb0 = st * BKB2;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rb, (lds_ptr_t)(slot + SLOT_A + (wave * 8 + j) * 1024), 16,
+                                               in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
+  };
+  auto issue_a = [&](int st) {
     uint8_t* slot = smem + (st & 1) * SLOT;
     const bool in = st < s1;
     const int kb0 = st * BKB2;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(t.ra, (lds_ptr_t)(slot + (wave * 8 + j) * 1024), 16,
-                                               in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(t.rb, (lds_ptr_t)(slot + SLOT_A + (wave * 8 + j) * 1024), 16,
                                                in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
     if (SP) {
       // scale pair (st + 1) / 2, half (st + 1) % 2 (A rows, then B rows)
@@ -123,6 +131,10 @@ __device__ __forceinline__ void mx_tile_mainloop(uint8_t* smem, const MxTileSrc&
                                                  in ? srow + st * 8 + h * 4 : 0x7ffffff0, 0, 0, 0);
       }
     }
+  };
+  auto issue = [&](int st) {
+    issue_a(st);
+    issue_b(st);
   };
 
   const int lrow = lane & 31;
@@ -217,33 +229,42 @@ __device__ __forceinline__ void mx_tile_mainloop(uint8_t* smem, const MxTileSrc&
     read_frag(3, cur);
     MX_SEG(1, 2)
     MX_INTERLEAVE(TI + TJ)
-    // B1: every wave has read all of `cur`; refill it with stage s+2
-    // The 20 refill loads are spread between the segment-3 MFMAs: issued as
-    // one burst they fill the texture-address queue and block the wave (and
-    // with it the MFMA stream) until the queue drains.
+    // B1: every wave has read all of `cur`; refill it with stage s+2, one
+    // load after each MFMA of segments 2 and 3 (A part, then B part): the
+    // direct-to-LDS loads of the four waves take the texture unit about
+    // 16 cycles each, so issued in a burst they fill its queue and block the
+    // wave, and with it the MFMA stream, until the queue drains.
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     block_barrier();
-    issue(s + 2);
+    issue_a(s + 2);
     MX_SEG(2, 0)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < LA; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, TI * TJ - LA, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    // B2: this wave's loads of stage s+1 have landed (only the LA loads of
+    // stage s+2 issued above may still be in flight); after the barrier
+    // every wave's have.
+    wait_vmcnt<LA>();
+    block_barrier();
+    read_scales(0, nxt, s + 1);
+    read_frag(0, nxt);
+    issue_b(s + 2);
+    MX_SEG(3, 2)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
 #pragma unroll
-    for (int q = 4; q < TI * TJ; ++q) {
+    for (int q = 0; q < 8; ++q) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    // B2: this wave's loads of stage s+1 have landed (only stage s+2's LPS may
-    // still be in flight); after the barrier every wave's have.
-    wait_vmcnt<LPS>();
-    block_barrier();
-    read_scales(0, nxt, s + 1);
-    read_frag(0, nxt);
-    MX_SEG(3, 2)
-    MX_INTERLEAVE(TI + TJ + 4)
   }
 #undef MX_SEG
 #undef MX_INTERLEAVE
