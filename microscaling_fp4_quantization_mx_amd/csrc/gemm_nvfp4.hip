@@ -319,25 +319,35 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
   for (int u = 0; u < 4; ++u) soff[u] = (64 * wave + 16 * u + (lane >> 2)) * KS + (lane & 3) * 4;
   const int nst = p.K / NVK_BK;
 
-  auto issue = [&](int st) {
+  // The 24 loads of a stage per wave (16 code copies, 8 scale copies), in
+  // four parts of six: the refill of a slot goes out over four MFMA steps, so
+  // the four waves never ask the texture unit for a whole stage at once.
+  auto issue_part = [&](int st, int part) {
     uint8_t* slot = smem + (st & 1) * SLOT;
     const bool in = st < nst;
     const int kb0 = st * NVK_BKB, ks0 = st * NVK_BKS;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (wave * 8 + j) * 1024), 16,
-                                               in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + SLOT_A + (wave * 8 + j) * 1024), 16,
-                                               in ? voff[j] + kb0 : 0x7ffffff0, 0, 0, 0);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(slot + OFF_SA + (wave * 4 + u) * 256), 4,
-                                               in ? soff[u] + ks0 : 0x7ffffff0, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(slot + OFF_SB + (wave * 4 + u) * 256), 4,
-                                               in ? soff[u] + ks0 : 0x7ffffff0, 0, 0, 0);
+    for (int idx = 6 * part; idx < 6 * part + 6; ++idx) {
+      if (idx < 8) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (wave * 8 + idx) * 1024), 16,
+                                                 in ? voff[idx] + kb0 : 0x7ffffff0, 0, 0, 0);
+      } else if (idx < 16) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(slot + SLOT_A + (wave * 8 + idx - 8) * 1024), 16,
+                                                 in ? voff[idx - 8] + kb0 : 0x7ffffff0, 0, 0, 0);
+      } else {
+        const int u = (idx - 16) >> 1;
+        if ((idx & 1) == 0)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(slot + OFF_SA + (wave * 4 + u) * 256), 4,
+                                                   in ? soff[u] + ks0 : 0x7ffffff0, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(slot + OFF_SB + (wave * 4 + u) * 256), 4,
+                                                   in ? soff[u] + ks0 : 0x7ffffff0, 0, 0, 0);
+      }
     }
+  };
+  auto issue = [&](int st) {
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue_part(st, part);
   };
 
   f32x16 acc[TI][TJ];
@@ -411,8 +421,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
       if (t == 12) {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");   // stage s+1 landed; reads of `cur` done
         block_barrier();
-        issue(s + 2);
+        issue_part(s + 2, 0);
         read_kk(0, nxt, 0);
+      } else if (t > 12) {
+        issue_part(s + 2, t - 12);
       } else if (d == 0 && kk < 3) {
         read_kk((kk + 1) & 1, cur, kk + 1);
       }
@@ -427,13 +439,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
         for (int j = 0; j < TJ; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(oa[t & 1][i], ob[t & 1][j], acc[i][j], 0, 0, 0);
       // one MFMA, then a quarter of the next step's conversions, and the
-      // step's LDS reads / refill loads spread between the MFMAs
+      // step's LDS reads / refill loads spread between the MFMAs (a refill
+      // load after every other MFMA)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);
+        if (q & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
