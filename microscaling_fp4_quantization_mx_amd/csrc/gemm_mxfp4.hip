@@ -45,6 +45,10 @@ struct MxGemmParams {
   int groups;              // 0 = dense
   const int32_t* offsets;  // [groups + 1]
   int c_bf16;
+  // split of the last round along K (k_gemm_mx_k256 only; split_max < 2: none)
+  int split_max;
+  int cus;                 // workgroup slots of the device (one per CU)
+  float* part;             // fp32 partial tiles, cus x 65536 floats
 };
 
 template <int BM, int BN, int WM, int WN>
@@ -467,8 +471,26 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
   static_assert(BM == T::BM && BN == T::BN && WM == T::WM && WN == T::WN, "one tile shape");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[T::SMEM];
 
+  // Whole tiles take workgroups [0, nfull) (XCD-remapped); with a split, the
+  // K parts of the last round's tiles follow, part-major within a tile.
+  const int nst = p.K / BK2;
+  const int total = gemm_tile_count<BM, BN>(p.M, p.N, p.groups, p.offsets);
+  const GemmSplit sp = gemm_split(total, p.cus, p.split_max, SP ? nst / 2 : nst);
+  const int nfull = (sp.full + 7) / 8 * 8;
+  const int bid = blockIdx.x;
+  int t, u = 0, part = 0;
+  if (bid < nfull) {
+    t = gemm_tile_remap(bid, sp.full);
+    if (t < 0) return;
+  } else {
+    const int j = bid - nfull;
+    if (j >= sp.r * sp.S) return;
+    u = j / sp.S;
+    part = j % sp.S;
+    t = sp.full + u;
+  }
   GemmTile tile;
-  if (!gemm_tile<BM, BN, GROUP_M>(blockIdx.x, p.M, p.N, p.groups, p.offsets, tile)) return;
+  gemm_tile_at<BM, BN, GROUP_M>(t, p.M, p.N, p.groups, p.offsets, tile);
   const int g = tile.g, m_end = tile.m_end, m0 = tile.m0, n0 = tile.n0;
   const MxTileSrc src = mx_tile_src(p.a_codes, p.a_scales, p.b_codes, p.b_scales, p.K, (size_t)m0,
                                     min(BM, m_end - m0), (size_t)g * p.N + n0, min(BN, p.N - n0));
@@ -479,16 +501,114 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
     for (int j = 0; j < T::TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  mx_tile_mainloop<SP>(smem, src, 0, p.K / BK2, acc);
-  mx_tile_store<SP>(smem, p.c, p.ldc, p.c_bf16, p.N, m0, m_end, n0, acc);
+  // a whole tile: all stages; K part `part` of S: stages [s0, s1) (SP: whole
+  // stage pairs)
+  int s0 = 0, s1 = nst;
+  if (bid >= nfull) {
+    if (SP) {
+      const int np = nst / 2;
+      s0 = 2 * (part * np / sp.S);
+      s1 = 2 * ((part + 1) * np / sp.S);
+    } else {
+      s0 = part * nst / sp.S;
+      s1 = (part + 1) * nst / sp.S;
+    }
+  }
+  mx_tile_mainloop<SP>(smem, src, s0, s1, acc);
+  if (bid < nfull) {
+    mx_tile_store<SP>(smem, p.c, p.ldc, p.c_bf16, p.N, m0, m_end, n0, acc);
+    return;
+  }
+  // the partial tile, in the accumulators' own layout: 16 bytes per lane and
+  // store, consecutive lanes consecutive
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4* mine = reinterpret_cast<f32x4*>(p.part) + (size_t)(u * sp.S + part) * (BM * BN / 4);
+#pragma unroll
+  for (int i = 0; i < T::TI; ++i)
+#pragma unroll
+    for (int j = 0; j < T::TJ; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        __builtin_nontemporal_store(f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
+                                    mine + (((wave * T::TI + i) * T::TJ + j) * 4 + q) * 64 + lane);
+}
+
+// C of the split tiles: the S partial tiles added in part order (so C does not
+// depend on which part finished first), then rounded as the whole-tile
+// epilogue rounds.  Sixteen workgroups per tile, each a sixteenth of the
+// partial slots, 4 float4 per thread (consecutive threads consecutive slots,
+// the loads of a part all in flight at once).  Partial slot idx holds
+// accumulator registers 4q .. 4q + 3 of tile (i, j) of a wave's 128 x 128
+// block, lane l: rows 8q + 4(l / 32) + 0..3 of the 32 x 32 tile, column l % 32.
+constexpr int RED_WG_PER_TILE = 16;
+template <bool SP>
+__global__ __launch_bounds__(256) void k_gemm_mx_reduce(MxGemmParams p) {
+  using T = MxTile<SP>;
+  constexpr int TI = T::TI, TJ = T::TJ, WM = T::WM, WN = T::WN, NWX = T::NWX;
+  constexpr int SLOTS = T::BM * T::BN / 4;                 // float4 per partial tile
+  constexpr int PER_T = SLOTS / RED_WG_PER_TILE / 256;     // float4 per thread
+  const int nst = p.K / BK2;
+  const int total = gemm_tile_count<T::BM, T::BN>(p.M, p.N, p.groups, p.offsets);
+  const GemmSplit sp = gemm_split(total, p.cus, p.split_max, SP ? nst / 2 : nst);
+  const int u = blockIdx.x / RED_WG_PER_TILE;
+  if (u >= sp.r) return;
+  const int base = (blockIdx.x % RED_WG_PER_TILE) * (SLOTS / RED_WG_PER_TILE) + threadIdx.x;
+  const f32x4* src = reinterpret_cast<const f32x4*>(p.part) + (size_t)u * sp.S * SLOTS + base;
+  f32x4 v[PER_T];
+#pragma unroll
+  for (int k = 0; k < PER_T; ++k) v[k] = __builtin_nontemporal_load(src + 256 * k);
+  for (int q = 1; q < sp.S; ++q) {
+    f32x4 w[PER_T];
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) w[k] = __builtin_nontemporal_load(src + (size_t)q * SLOTS + 256 * k);
+    __builtin_amdgcn_sched_barrier(0);   // all of this part's loads in flight before the first add
+#pragma unroll
+    for (int k = 0; k < PER_T; ++k) {
+      v[k][0] += w[k][0];
+      v[k][1] += w[k][1];
+      v[k][2] += w[k][2];
+      v[k][3] += w[k][3];
+    }
+  }
+  GemmTile tile;
+  gemm_tile_at<T::BM, T::BN, GROUP_M>(sp.full + u, p.M, p.N, p.groups, p.offsets, tile);
+#pragma unroll
+  for (int k = 0; k < PER_T; ++k) {
+    const int idx = base + 256 * k;
+    const int lane = idx & 63, rest = idx >> 6;
+    const int q = rest & 3, j = (rest >> 2) % TJ, i = (rest >> 2) / TJ % TI, wave = (rest >> 2) / (TJ * TI);
+    const int wy = wave / NWX, wx = wave % NWX;
+    const int col = tile.n0 + wx * WN + j * 32 + (lane & 31);
+    const int row0 = tile.m0 + wy * WM + i * 32 + 8 * q + 4 * (lane >> 5);
+    if (col >= p.N) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = row0 + e;
+      if (row >= tile.m_end) break;
+      if (p.c_bf16)
+        reinterpret_cast<uint16_t*>(p.c)[(size_t)row * p.ldc + col] = (uint16_t)f32_to_bf16_rne(v[k][e]);
+      else
+        reinterpret_cast<float*>(p.c)[(size_t)row * p.ldc + col] = v[k][e];
+    }
+  }
 }
 
 // Tile configuration used for every MXFP4 product.
 constexpr int GBM = 256, GBN = 256, GWM = 128, GWN = 128;
+constexpr int kGemmSplitMax = 4;    // K parts per split tile
+
+size_t gemm_mx_split_bytes(int64_t M, int64_t N, int64_t K, int groups, int cus) {
+  if (K % BK2 != 0 || M <= 0 || N <= 0 || cus < 2) return 0;
+  const int64_t bound = gemm_tile_bound(M, N, GBM, GBN, groups);
+  if (groups == 0 && bound % cus == 0) return 0;   // whole rounds: nothing to split
+  const int64_t tiles = bound * kGemmSplitMax < cus ? bound * kGemmSplitMax : cus;
+  return (size_t)tiles * GBM * GBN * sizeof(float);
+}
 
 hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                           const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                          int groups, const int32_t* offsets, hipStream_t st) {
+                          int groups, const int32_t* offsets, hipStream_t st, float* part, size_t part_bytes,
+                          int cus) {
   MxGemmParams p;
   p.a_codes = a_codes; p.a_scales = a_scales; p.b_codes = b_codes; p.b_scales = b_scales;
   p.c = c; p.ldc = ldc; p.M = (int)M; p.N = (int)N; p.K = (int)K;
@@ -496,15 +616,30 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
   const int64_t tiles = gemm_tile_bound(M, N, GBM, GBN, groups);
   int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
+  // The split needs a partial tile for each part: at most min(cus, tiles x
+  // kGemmSplitMax) of them (r split tiles x S parts, r * S <= cus).
+  const size_t need = gemm_mx_split_bytes(M, N, K, groups, cus);
+  const bool split = part && need > 0 && part_bytes >= need;
+  const int64_t parts = (int64_t)(need / (GBM * GBN * sizeof(float)));   // workgroups for the parts
+  const int64_t rmax = tiles < cus ? tiles : cus;                        // split tiles at most
+  p.split_max = split ? kGemmSplitMax : 1;
+  p.cus = cus;
+  p.part = split ? part : nullptr;
   constexpr int NT = (GBM / GWM) * (GBN / GWN) * 64;
-  if (K % (2 * BK2) == 0)
-    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, true>), dim3((unsigned)grid), dim3(NT), 0, st, p);
-  else if (K % BK2 == 0)
-    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, false>), dim3((unsigned)grid), dim3(NT), 0, st, p);
-  else if (K % MX_BK == 0)
+  constexpr int RWG = RED_WG_PER_TILE;                                   // reduce workgroups per tile
+  if (K % (2 * BK2) == 0) {
+    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, true>), dim3((unsigned)(grid + (split ? parts : 0))), dim3(NT),
+                       0, st, p);
+    if (split) hipLaunchKernelGGL((k_gemm_mx_reduce<true>), dim3((unsigned)(rmax * RWG)), dim3(256), 0, st, p);
+  } else if (K % BK2 == 0) {
+    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, false>), dim3((unsigned)(grid + (split ? parts : 0))),
+                       dim3(NT), 0, st, p);
+    if (split) hipLaunchKernelGGL((k_gemm_mx_reduce<false>), dim3((unsigned)(rmax * RWG)), dim3(256), 0, st, p);
+  } else if (K % MX_BK == 0) {
     hipLaunchKernelGGL((k_gemm_mx_ring<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
-  else
+  } else {
     hipLaunchKernelGGL((k_gemm_mx<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
+  }
   return hipGetLastError();
 }
 

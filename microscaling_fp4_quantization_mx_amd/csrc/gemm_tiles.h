@@ -22,26 +22,26 @@ struct GemmTile {
   int m0, n0;     // first row and column of the tile
 };
 
-// false: this workgroup has no tile (the grid is rounded up to whole XCD runs)
-template <int BM, int BN, int GM>
-__device__ __forceinline__ bool gemm_tile(int bid, int M, int N, int groups, const int32_t* offsets, GemmTile& o) {
+// Tiles of the product: every group adds ceil(rows_g / BM) tile rows of
+// ceil(N / BN) tiles.
+template <int BM, int BN>
+__device__ __forceinline__ int gemm_tile_count(int M, int N, int groups, const int32_t* offsets) {
   const int tn_count = (N + BN - 1) / BN;
-  int total;
-  if (groups == 0) {
-    total = ((M + BM - 1) / BM) * tn_count;
-  } else {
-    total = 0;
-    for (int i = 0; i < groups; ++i) {
-      const int o0 = min(max(offsets[i], 0), M), o1 = min(max(offsets[i + 1], 0), M);
-      const int rows = o1 > o0 ? o1 - o0 : 0;
-      total += ((rows + BM - 1) / BM) * tn_count;
-    }
+  if (groups == 0) return ((M + BM - 1) / BM) * tn_count;
+  int total = 0;
+  for (int i = 0; i < groups; ++i) {
+    const int o0 = min(max(offsets[i], 0), M), o1 = min(max(offsets[i + 1], 0), M);
+    const int rows = o1 > o0 ? o1 - o0 : 0;
+    total += ((rows + BM - 1) / BM) * tn_count;
   }
-  const int per_xcd = (total + 7) / 8;
-  const int local = bid / 8;
-  if (local >= per_xcd) return false;
-  const int t = (bid % 8) * per_xcd + local;
-  if (t >= total) return false;
+  return total;
+}
+
+// Geometry of tile t (0 <= t < gemm_tile_count) in raster order: groups in
+// turn; within a group, GM tile rows at a time walk all tile columns.
+template <int BM, int BN, int GM>
+__device__ __forceinline__ void gemm_tile_at(int t, int M, int N, int groups, const int32_t* offsets, GemmTile& o) {
+  const int tn_count = (N + BN - 1) / BN;
   o.g = 0;
   o.m_begin = 0;
   o.m_end = M;
@@ -67,7 +67,48 @@ __device__ __forceinline__ bool gemm_tile(int bid, int M, int N, int groups, con
   const int in_grp = tl % per_group;
   o.m0 = o.m_begin + (first_m + in_grp % gm) * BM;
   o.n0 = (in_grp / gm) * BN;
+}
+
+// Workgroup bid of a grid of ceil(total / 8) * 8: its tile, XCD-remapped
+// (false: no tile; the grid is rounded up to whole XCD runs).
+__device__ __forceinline__ int gemm_tile_remap(int bid, int total) {
+  const int per_xcd = (total + 7) / 8;
+  const int local = bid / 8;
+  if (local >= per_xcd) return -1;
+  const int t = (bid % 8) * per_xcd + local;
+  return t < total ? t : -1;
+}
+
+// false: this workgroup has no tile (the grid is rounded up to whole XCD runs)
+template <int BM, int BN, int GM>
+__device__ __forceinline__ bool gemm_tile(int bid, int M, int N, int groups, const int32_t* offsets, GemmTile& o) {
+  const int t = gemm_tile_remap(bid, gemm_tile_count<BM, BN>(M, N, groups, offsets));
+  if (t < 0) return false;
+  gemm_tile_at<BM, BN, GM>(t, M, N, groups, offsets, o);
   return true;
+}
+
+// Split of the last, partly filled round of tiles along K.  With T tiles on
+// `cus` workgroup slots (one workgroup per CU), the last r = T % cus tiles
+// would run alone for a whole tile's time; instead each is cut into S K-parts
+// (S <= split_max, r * S <= cus, at most `parts` pieces of K), computed by
+// r * S workgroups that follow the T - r whole tiles.  S = 1: no split.
+struct GemmSplit {
+  int full;   // whole tiles (the first `full` in raster order)
+  int r;      // split tiles (the rest)
+  int S;      // K parts per split tile
+};
+__device__ __forceinline__ GemmSplit gemm_split(int T, int cus, int split_max, int parts) {
+  GemmSplit o{T, 0, 1};
+  if (split_max < 2 || cus < 2 || T <= 0) return o;
+  const int r = T % cus;
+  if (r == 0) return o;
+  const int S = min(min(split_max, cus / r), parts);
+  if (S < 2) return o;
+  o.full = T - r;
+  o.r = r;
+  o.S = S;
+  return o;
 }
 
 // Upper bound of the tile count for the launch grid: every group adds at

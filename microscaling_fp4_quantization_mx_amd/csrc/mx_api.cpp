@@ -110,6 +110,21 @@ bool fused_shape(const mx_gemm_args* a) {
          mxk::fused_fits(a->M, a->N, a->K, a->groups, kFusedCUs / 8);
 }
 
+// Scratch for the K parts of a partly filled last round of the MXFP4 x MXFP4
+// GEMM (K % 256 == 0 paths; not the fused kernel, which splits on its own).
+size_t split_bytes(const mx_gemm_args* a) {
+  if (!a->b || a->b->fmt != MX_FMT_MXFP4 || fused_shape(a)) return 0;
+  if ((a->a ? a->a->fmt : dyn_a_fmt(a)) != MX_FMT_MXFP4) return 0;
+  if (a->M <= 0 || a->N <= 0 || a->K <= 0 || a->groups < 0) return 0;
+  return mxk::gemm_mx_split_bytes(a->M, a->N, pad_to(a->K, 32), a->groups, device_cus());
+}
+// Bytes of the workspace that the dynamic path's quantized A takes.
+size_t ws_a_bytes(const mx_gemm_args* a) {
+  if (!a->a && !(a->a_codes_out && a->a_scales_out) && a->M > 0 && a->K > 0 && dyn_fmt_ok(dyn_a_fmt(a)))
+    return dyn_a_bytes(dyn_a_fmt(a), a->M, a->K);
+  return 0;
+}
+
 }  // namespace
 
 #pragma GCC visibility push(default)
@@ -142,11 +157,11 @@ size_t mx_workspace_bytes(int32_t op, const void* desc, int32_t flags) {
   }
   if (op == MX_OP_GEMM) {
     const mx_gemm_args* a = static_cast<const mx_gemm_args*>(desc);
-    size_t n = 0;
-    if (!a->a && !(a->a_codes_out && a->a_scales_out) && a->M > 0 && a->K > 0 && dyn_fmt_ok(dyn_a_fmt(a)))
-      n = dyn_a_bytes(dyn_a_fmt(a), a->M, a->K);
-    if (fused_shape(a)) n += round256(mxk::fused_workspace_bytes());
-    return n;
+    // layout: [fused kernel's counters and partials][quantized A][split partials]
+    const size_t n = ws_a_bytes(a);
+    if (fused_shape(a)) return n + round256(mxk::fused_workspace_bytes());
+    const size_t sb = split_bytes(a);
+    return sb ? round256(n) + sb : n;
   }
   if (op == MX_OP_MOE_ROUTE) {
     const int32_t experts = *static_cast<const int32_t*>(desc);
@@ -348,9 +363,18 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
                                         const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), s);
     if (e != hipSuccess) return MX_ERR_HIP;
   }
-  if (fmt == MX_FMT_MXFP4)
+  if (fmt == MX_FMT_MXFP4) {
+    // split partials after what the workspace already holds (none: no split)
+    const size_t off = fused_ws + round256(a->a_codes_out ? 0 : ws_a_bytes(a));
+    float* part = nullptr;
+    size_t part_bytes = 0;
+    if (a->workspace && al16(a->workspace) && a->workspace_bytes > off && split_bytes(a) > 0) {
+      part = reinterpret_cast<float*>(static_cast<uint8_t*>(a->workspace) + off);
+      part_bytes = a->workspace_bytes - off;
+    }
     return hip_status(mxk::launch_gemm_mx(a_codes, a_scales, a->b->codes, a->b->scales, a->c, cbf, a->ldc, a->M, a->N,
-                                          Kp, a->groups, a->group_offsets, s));
+                                          Kp, a->groups, a->group_offsets, s, part, part_bytes, device_cus()));
+  }
   return hip_status(mxk::launch_gemm_nv(a_codes, a_scales, a_global, a->b->codes, a->b->scales, a->b->global_scale,
                                         a->c, cbf, a->ldc, a->M, a->N, a->K, s));
 }

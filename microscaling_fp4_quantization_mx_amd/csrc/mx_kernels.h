@@ -19,9 +19,14 @@ hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t row
                            uint8_t* scales, float* gscale, bool static_global, uint32_t* partial, hipStream_t st);
 hipError_t launch_dequant(bool nv, const uint8_t* codes, const uint8_t* scales, const float* gscale, int64_t rows,
                           int64_t cols, void* y, bool out_bf16, int64_t ldy, hipStream_t st);
+// part / part_bytes: device scratch for the K parts of a last round that
+// would leave CUs idle (at least gemm_mx_split_bytes; else no split); cus:
+// the device's CU count.
 hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                           const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                          int groups, const int32_t* offsets, hipStream_t st);
+                          int groups, const int32_t* offsets, hipStream_t st, float* part = nullptr,
+                          size_t part_bytes = 0, int cus = 0);
+size_t gemm_mx_split_bytes(int64_t M, int64_t N, int64_t K, int groups, int cus);
 // Dynamic MXFP4 quantization fused with the (grouped) GEMM (gemm_fused.hip):
 // one persistent launch (after a one-workgroup counter reset) for K % 512 == 0
 // on a 256-CU device; the workspace holds fused_workspace_bytes() of counters
