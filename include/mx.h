@@ -241,12 +241,13 @@ int mx_dequantize(const mx_tensor *in, void *y, int32_t y_dtype, int64_t ld_y, v
  * not faster: a workgroup needs 157 KiB of LDS, one per CU, so the
  * memory-bound quantization cannot run beside the matrix-core work and
  * costs its full time in either form.
- * MXFP4 x MXFP4 with K % 256 == 0 (outside the fused kernel): one workgroup
- * per CU takes a 256 x 256 output tile, so when the tile count T is not a
- * multiple of the device's CU count the last T mod CUs tiles would run alone;
- * they are cut into up to 4 K parts instead, whose fp32 partial tiles a
- * second launch adds in part order (repeated calls give identical C; it
- * agrees with the unsplit kernel within the fp32 summation-order tolerance).
+ * MXFP4 x MXFP4 and NVFP4 x NVFP4 with K % 256 == 0 (outside the fused
+ * kernel): one workgroup per CU takes a 256 x 256 output tile, so when the
+ * tile count T is not a multiple of the device's CU count the last T mod CUs
+ * tiles would run alone; they are cut into up to 4 K parts instead, whose
+ * fp32 partial tiles a second launch adds in part order (then times gA gB
+ * for NVFP4; repeated calls give identical C; it agrees with the unsplit
+ * kernel within the fp32 summation-order tolerance).
  * The partials live in the workspace after the quantized A (if any), which
  * mx_workspace_bytes then includes (up to CUs x 256 KiB, none for a dense
  * product that fills whole rounds); a workspace too small for them runs the

@@ -24,6 +24,7 @@
 #include "mx_device.h"
 #include "gemm_mx_tile.h"
 #include "gemm_tiles.h"
+#include "gemm_split.h"
 #include "mx_kernels.h"
 
 namespace mxk {
@@ -519,90 +520,21 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_mx_k256(MxG
     mx_tile_store<SP>(smem, p.c, p.ldc, p.c_bf16, p.N, m0, m_end, n0, acc);
     return;
   }
-  // the partial tile, in the accumulators' own layout: 16 bytes per lane and
-  // store, consecutive lanes consecutive
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  f32x4* mine = reinterpret_cast<f32x4*>(p.part) + (size_t)(u * sp.S + part) * (BM * BN / 4);
-#pragma unroll
-  for (int i = 0; i < T::TI; ++i)
-#pragma unroll
-    for (int j = 0; j < T::TJ; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        __builtin_nontemporal_store(f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]},
-                                    mine + (((wave * T::TI + i) * T::TJ + j) * 4 + q) * 64 + lane);
-}
-
-// C of the split tiles: the S partial tiles added in part order (so C does not
-// depend on which part finished first), then rounded as the whole-tile
-// epilogue rounds.  Sixteen workgroups per tile, each a sixteenth of the
-// partial slots, 4 float4 per thread (consecutive threads consecutive slots,
-// the loads of a part all in flight at once).  Partial slot idx holds
-// accumulator registers 4q .. 4q + 3 of tile (i, j) of a wave's 128 x 128
-// block, lane l: rows 8q + 4(l / 32) + 0..3 of the 32 x 32 tile, column l % 32.
-constexpr int RED_WG_PER_TILE = 16;
-template <bool SP>
-__global__ __launch_bounds__(256) void k_gemm_mx_reduce(MxGemmParams p) {
-  using T = MxTile<SP>;
-  constexpr int TI = T::TI, TJ = T::TJ, WM = T::WM, WN = T::WN, NWX = T::NWX;
-  constexpr int SLOTS = T::BM * T::BN / 4;                 // float4 per partial tile
-  constexpr int PER_T = SLOTS / RED_WG_PER_TILE / 256;     // float4 per thread
-  const int nst = p.K / BK2;
-  const int total = gemm_tile_count<T::BM, T::BN>(p.M, p.N, p.groups, p.offsets);
-  const GemmSplit sp = gemm_split(total, p.cus, p.split_max, SP ? nst / 2 : nst);
-  const int u = blockIdx.x / RED_WG_PER_TILE;
-  if (u >= sp.r) return;
-  const int base = (blockIdx.x % RED_WG_PER_TILE) * (SLOTS / RED_WG_PER_TILE) + threadIdx.x;
-  const f32x4* src = reinterpret_cast<const f32x4*>(p.part) + (size_t)u * sp.S * SLOTS + base;
-  f32x4 v[PER_T];
-#pragma unroll
-  for (int k = 0; k < PER_T; ++k) v[k] = __builtin_nontemporal_load(src + 256 * k);
-  for (int q = 1; q < sp.S; ++q) {
-    f32x4 w[PER_T];
-#pragma unroll
-    for (int k = 0; k < PER_T; ++k) w[k] = __builtin_nontemporal_load(src + (size_t)q * SLOTS + 256 * k);
-    __builtin_amdgcn_sched_barrier(0);   // all of this part's loads in flight before the first add
-#pragma unroll
-    for (int k = 0; k < PER_T; ++k) {
-      v[k][0] += w[k][0];
-      v[k][1] += w[k][1];
-      v[k][2] += w[k][2];
-      v[k][3] += w[k][3];
-    }
-  }
-  GemmTile tile;
-  gemm_tile_at<T::BM, T::BN, GROUP_M>(sp.full + u, p.M, p.N, p.groups, p.offsets, tile);
-#pragma unroll
-  for (int k = 0; k < PER_T; ++k) {
-    const int idx = base + 256 * k;
-    const int lane = idx & 63, rest = idx >> 6;
-    const int q = rest & 3, j = (rest >> 2) % TJ, i = (rest >> 2) / TJ % TI, wave = (rest >> 2) / (TJ * TI);
-    const int wy = wave / NWX, wx = wave % NWX;
-    const int col = tile.n0 + wx * WN + j * 32 + (lane & 31);
-    const int row0 = tile.m0 + wy * WM + i * 32 + 8 * q + 4 * (lane >> 5);
-    if (col >= p.N) continue;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = row0 + e;
-      if (row >= tile.m_end) break;
-      if (p.c_bf16)
-        reinterpret_cast<uint16_t*>(p.c)[(size_t)row * p.ldc + col] = (uint16_t)f32_to_bf16_rne(v[k][e]);
-      else
-        reinterpret_cast<float*>(p.c)[(size_t)row * p.ldc + col] = v[k][e];
-    }
-  }
+  gemm_split_store_partial<T::TI, T::TJ>(acc, p.part, u, sp.S, part);
 }
 
 // Tile configuration used for every MXFP4 product.
 constexpr int GBM = 256, GBN = 256, GWM = 128, GWN = 128;
-constexpr int kGemmSplitMax = 4;    // K parts per split tile
+
+// K parts available to a split tile of the K = 256-stage kernel (paired
+// scale stages when K % 512 == 0)
+static int gemm_mx_parts(int64_t K) {
+  if (K % BK2 != 0) return 0;
+  return (int)(K % (2 * BK2) == 0 ? K / (2 * BK2) : K / BK2);
+}
 
 size_t gemm_mx_split_bytes(int64_t M, int64_t N, int64_t K, int groups, int cus) {
-  if (K % BK2 != 0 || M <= 0 || N <= 0 || cus < 2) return 0;
-  const int64_t bound = gemm_tile_bound(M, N, GBM, GBN, groups);
-  if (groups == 0 && bound % cus == 0) return 0;   // whole rounds: nothing to split
-  const int64_t tiles = bound * kGemmSplitMax < cus ? bound * kGemmSplitMax : cus;
-  return (size_t)tiles * GBM * GBN * sizeof(float);
+  return gemm_split_bytes(M, N, groups, cus, gemm_mx_parts(K));
 }
 
 hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
@@ -620,21 +552,25 @@ hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const
   // kGemmSplitMax) of them (r split tiles x S parts, r * S <= cus).
   const size_t need = gemm_mx_split_bytes(M, N, K, groups, cus);
   const bool split = part && need > 0 && part_bytes >= need;
-  const int64_t parts = (int64_t)(need / (GBM * GBN * sizeof(float)));   // workgroups for the parts
-  const int64_t rmax = tiles < cus ? tiles : cus;                        // split tiles at most
+  const int64_t nparts = (int64_t)(need / (kSplitTileFloats * sizeof(float)));   // workgroups for the parts
+  const int64_t rmax = tiles < cus ? tiles : cus;                                // split tiles at most
   p.split_max = split ? kGemmSplitMax : 1;
   p.cus = cus;
   p.part = split ? part : nullptr;
   constexpr int NT = (GBM / GWM) * (GBN / GWN) * 64;
-  constexpr int RWG = RED_WG_PER_TILE;                                   // reduce workgroups per tile
-  if (K % (2 * BK2) == 0) {
-    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, true>), dim3((unsigned)(grid + (split ? parts : 0))), dim3(NT),
-                       0, st, p);
-    if (split) hipLaunchKernelGGL((k_gemm_mx_reduce<true>), dim3((unsigned)(rmax * RWG)), dim3(256), 0, st, p);
-  } else if (K % BK2 == 0) {
-    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, false>), dim3((unsigned)(grid + (split ? parts : 0))),
+  if (K % (2 * BK2) == 0)
+    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, true>), dim3((unsigned)(grid + (split ? nparts : 0))),
                        dim3(NT), 0, st, p);
-    if (split) hipLaunchKernelGGL((k_gemm_mx_reduce<false>), dim3((unsigned)(rmax * RWG)), dim3(256), 0, st, p);
+  else if (K % BK2 == 0)
+    hipLaunchKernelGGL((k_gemm_mx_k256<GBM, GBN, GWM, GWN, false>), dim3((unsigned)(grid + (split ? nparts : 0))),
+                       dim3(NT), 0, st, p);
+  if (K % BK2 == 0) {
+    if (split) {
+      GemmSplitReduce r{part, c, ldc, c_bf16, (int)M, (int)N, groups, offsets, cus, kGemmSplitMax,
+                        gemm_mx_parts(K), nullptr, nullptr};
+      hipLaunchKernelGGL((k_gemm_split_reduce<GROUP_M>), dim3((unsigned)(rmax * kSplitReduceWgPerTile)), dim3(256), 0,
+                         st, r);
+    }
   } else if (K % MX_BK == 0) {
     hipLaunchKernelGGL((k_gemm_mx_ring<GBM, GBN, GWM, GWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
   } else {

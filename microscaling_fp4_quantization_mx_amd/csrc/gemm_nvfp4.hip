@@ -24,6 +24,7 @@
 // eight 16-byte chunks are XOR-swizzled), XCD-aware tile order.
 #include "mx_device.h"
 #include "mx_kernels.h"
+#include "gemm_split.h"
 
 namespace mxk {
 
@@ -44,6 +45,10 @@ struct NvGemmParams {
   int64_t ldc;
   int M, N, K;
   int c_bf16;
+  // split of the last round along K (k_gemm_nv_k256 only; split_max < 2: none)
+  int split_max;
+  int cus;                 // workgroup slots of the device (one per CU)
+  float* part;             // fp32 partial tiles
 };
 
 // E4M3 byte -> (power of two of its exponent, fp16 significand) with
@@ -272,26 +277,30 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
   const int wave = tid >> 6;
   const int wy = wave / NWX, wx = wave % NWX;
 
-  const int tn_count = (p.N + BN - 1) / BN;
-  const int tm_count = (p.M + BM - 1) / BM;
-  int tm, tn;
-  {
-    const int total = tm_count * tn_count;
-    const int per_xcd = (total + 7) / 8;
-    const int bid = blockIdx.x;
-    const int local = bid / 8;
-    if (local >= per_xcd) return;
-    const int t = (bid % 8) * per_xcd + local;
-    if (t >= total) return;
-    const int per_group = NV_GROUP_M * tn_count;
-    const int grp = t / per_group;
-    const int first_m = grp * NV_GROUP_M;
-    const int gm = min(tm_count - first_m, NV_GROUP_M);
-    const int in_grp = t % per_group;
-    tm = first_m + in_grp % gm;
-    tn = in_grp / gm;
+  // Whole tiles take workgroups [0, nfull) (XCD-remapped, tile rows in
+  // raster groups of NV_GROUP_M); with a split of the last round, the K parts
+  // of its tiles follow, part-major within a tile.
+  const int nst = p.K / NVK_BK;
+  const GemmSplit sp = gemm_split(gemm_tile_count<BM, BN>(p.M, p.N, 0, nullptr), p.cus, p.split_max, nst);
+  const int nfull = (sp.full + 7) / 8 * 8;
+  const int bid = blockIdx.x;
+  int t, u = 0, part = 0;
+  if (bid < nfull) {
+    t = gemm_tile_remap(bid, sp.full);
+    if (t < 0) return;
+  } else {
+    const int j = bid - nfull;
+    if (j >= sp.r * sp.S) return;
+    u = j / sp.S;
+    part = j % sp.S;
+    t = sp.full + u;
   }
-  const int m0 = tm * BM, n0 = tn * BN;
+  GemmTile tile;
+  gemm_tile_at<BM, BN, NV_GROUP_M>(t, p.M, p.N, 0, nullptr, tile);
+  const int m0 = tile.m0, n0 = tile.n0;
+  // stages [s0, s1): all of K, or K part `part` of S
+  const int s0 = bid < nfull ? 0 : part * nst / sp.S;
+  const int s1 = bid < nfull ? nst : (part + 1) * nst / sp.S;
   const int KB = p.K / 2, KS = p.K / 16;
   const int a_rows = min(BM, p.M - m0), b_rows = min(BN, p.N - n0);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
@@ -317,17 +326,16 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
   int soff[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) soff[u] = (64 * wave + 16 * u + (lane >> 2)) * KS + (lane & 3) * 4;
-  const int nst = p.K / NVK_BK;
 
   // The 24 loads of a stage per wave (16 code copies, 8 scale copies), in
   // four parts of six: the refill of a slot goes out over four MFMA steps, so
   // the four waves never ask the texture unit for a whole stage at once.
-  auto issue_part = [&](int st, int part) {
+  auto issue_part = [&](int st, int piece) {
     uint8_t* slot = smem + (st & 1) * SLOT;
-    const bool in = st < nst;
+    const bool in = st < s1;
     const int kb0 = st * NVK_BKB, ks0 = st * NVK_BKS;
 #pragma unroll
-    for (int idx = 6 * part; idx < 6 * part + 6; ++idx) {
+    for (int idx = 6 * piece; idx < 6 * piece + 6; ++idx) {
       if (idx < 8) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(slot + (wave * 8 + idx) * 1024), 16,
                                                  in ? voff[idx] + kb0 : 0x7ffffff0, 0, 0, 0);
@@ -347,7 +355,7 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
   };
   auto issue = [&](int st) {
 #pragma unroll
-    for (int part = 0; part < 4; ++part) issue_part(st, part);
+    for (int piece = 0; piece < 4; ++piece) issue_part(st, piece);
   };
 
   f32x16 acc[TI][TJ];
@@ -405,14 +413,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
   // reads the fragments of sub-stage kk+1.  At t = 12 (all of stage s read):
   // counted wait for stage s+1, barrier, refill of this slot with stage s+2
   // (interleaved with steps 12-15), read of stage s+1's first sub-stage.
-  issue(0);
-  issue(1);
-  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");   // stage 0 landed (stage 1's 24 loads may be in flight)
+  issue(s0);
+  issue(s0 + 1);
+  asm volatile("s_waitcnt vmcnt(24)" ::: "memory");   // stage s0 landed (stage s0+1's 24 loads may be in flight)
   block_barrier();
-  read_kk(0, smem, 0);
-  read_kk(1, smem, 1);
+  read_kk(0, smem + (s0 & 1) * SLOT, 0);
+  read_kk(1, smem + (s0 & 1) * SLOT, 1);
   expand_step(0, 0, 0);
-  for (int s = 0; s < nst; ++s) {
+  for (int s = s0; s < s1; ++s) {
     const uint8_t* cur = smem + (s & 1) * SLOT;
     const uint8_t* nxt = smem + ((s + 1) & 1) * SLOT;
 #pragma unroll
@@ -452,6 +460,10 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (bid >= nfull) {   // a K part: its partial tile (gA * gB is applied to the sum)
+    gemm_split_store_partial<TI, TJ>(acc, p.part, u, sp.S, part);
+    return;
+  }
 
   // ---- epilogue through LDS (as in the MXFP4 kernel), times gA * gB
   const float gg = (*p.a_global) * (*p.b_global);
@@ -509,9 +521,14 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void k_gemm_nv_k256(NvG
 
 constexpr int NBM = 256, NBN = 256, NWM = 128, NWN = 128;
 
+size_t gemm_nv_split_bytes(int64_t M, int64_t N, int64_t K, int cus) {
+  return K % NVK_BK == 0 ? gemm_split_bytes(M, N, 0, cus, (int)(K / NVK_BK)) : 0;
+}
+
 hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_global, void* c, int c_bf16,
-                          int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+                          int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st, float* part, size_t part_bytes,
+                          int cus) {
   NvGemmParams p;
   p.a_codes = a_codes; p.a_scales = a_scales; p.a_global = a_global;
   p.b_codes = b_codes; p.b_scales = b_scales; p.b_global = b_global;
@@ -519,11 +536,27 @@ hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const
   const int64_t tiles = ((M + NBM - 1) / NBM) * ((N + NBN - 1) / NBN);
   const int64_t grid = (tiles + 7) / 8 * 8;
   if (grid == 0) return hipSuccess;
+  // the last round's K parts (see gemm_split.h), when the scratch holds them
+  const size_t need = gemm_nv_split_bytes(M, N, K, cus);
+  const bool split = part && need > 0 && part_bytes >= need;
+  const int64_t nparts = (int64_t)(need / (kSplitTileFloats * sizeof(float)));
+  p.split_max = split ? kGemmSplitMax : 1;
+  p.cus = cus;
+  p.part = split ? part : nullptr;
   constexpr int NT = (NBM / NWM) * (NBN / NWN) * 64;
-  if (K % NVK_BK == 0)
-    hipLaunchKernelGGL((k_gemm_nv_k256<NBM, NBN, NWM, NWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
-  else
+  if (K % NVK_BK == 0) {
+    hipLaunchKernelGGL((k_gemm_nv_k256<NBM, NBN, NWM, NWN>), dim3((unsigned)(grid + (split ? nparts : 0))), dim3(NT), 0,
+                       st, p);
+    if (split) {
+      const int64_t rmax = tiles < cus ? tiles : cus;
+      GemmSplitReduce r{part, c, ldc, c_bf16, (int)M, (int)N, 0, nullptr, cus, kGemmSplitMax, (int)(K / NVK_BK),
+                        a_global, b_global};
+      hipLaunchKernelGGL((k_gemm_split_reduce<NV_GROUP_M>), dim3((unsigned)(rmax * kSplitReduceWgPerTile)), dim3(256), 0,
+                         st, r);
+    }
+  } else {
     hipLaunchKernelGGL((k_gemm_nv<NBM, NBN, NWM, NWN>), dim3((unsigned)grid), dim3(NT), 0, st, p);
+  }
   return hipGetLastError();
 }
 

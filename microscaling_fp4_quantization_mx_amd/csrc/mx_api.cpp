@@ -113,10 +113,14 @@ bool fused_shape(const mx_gemm_args* a) {
 // Scratch for the K parts of a partly filled last round of the MXFP4 x MXFP4
 // GEMM (K % 256 == 0 paths; not the fused kernel, which splits on its own).
 size_t split_bytes(const mx_gemm_args* a) {
-  if (!a->b || a->b->fmt != MX_FMT_MXFP4 || fused_shape(a)) return 0;
-  if ((a->a ? a->a->fmt : dyn_a_fmt(a)) != MX_FMT_MXFP4) return 0;
+  if (!a->b || fused_shape(a)) return 0;
   if (a->M <= 0 || a->N <= 0 || a->K <= 0 || a->groups < 0) return 0;
-  return mxk::gemm_mx_split_bytes(a->M, a->N, pad_to(a->K, 32), a->groups, device_cus());
+  const int32_t af = a->a ? a->a->fmt : dyn_a_fmt(a);
+  if (a->b->fmt == MX_FMT_MXFP4 && af == MX_FMT_MXFP4)
+    return mxk::gemm_mx_split_bytes(a->M, a->N, pad_to(a->K, 32), a->groups, device_cus());
+  if (a->b->fmt == MX_FMT_NVFP4 && af == MX_FMT_NVFP4 && a->a && a->groups == 0)
+    return mxk::gemm_nv_split_bytes(a->M, a->N, a->K, device_cus());
+  return 0;
 }
 // Bytes of the workspace that the dynamic path's quantized A takes.
 size_t ws_a_bytes(const mx_gemm_args* a) {
@@ -363,20 +367,19 @@ int mx_gemm(const mx_gemm_args* a, void* stream) {
                                         const_cast<uint8_t*>(a_codes), const_cast<uint8_t*>(a_scales), s);
     if (e != hipSuccess) return MX_ERR_HIP;
   }
-  if (fmt == MX_FMT_MXFP4) {
-    // split partials after what the workspace already holds (none: no split)
-    const size_t off = fused_ws + round256(a->a_codes_out ? 0 : ws_a_bytes(a));
-    float* part = nullptr;
-    size_t part_bytes = 0;
-    if (a->workspace && al16(a->workspace) && a->workspace_bytes > off && split_bytes(a) > 0) {
-      part = reinterpret_cast<float*>(static_cast<uint8_t*>(a->workspace) + off);
-      part_bytes = a->workspace_bytes - off;
-    }
+  // split partials after what the workspace already holds (none: no split)
+  const size_t off = fused_ws + round256(a->a_codes_out ? 0 : ws_a_bytes(a));
+  float* part = nullptr;
+  size_t part_bytes = 0;
+  if (a->workspace && al16(a->workspace) && a->workspace_bytes > off && split_bytes(a) > 0) {
+    part = reinterpret_cast<float*>(static_cast<uint8_t*>(a->workspace) + off);
+    part_bytes = a->workspace_bytes - off;
+  }
+  if (fmt == MX_FMT_MXFP4)
     return hip_status(mxk::launch_gemm_mx(a_codes, a_scales, a->b->codes, a->b->scales, a->c, cbf, a->ldc, a->M, a->N,
                                           Kp, a->groups, a->group_offsets, s, part, part_bytes, device_cus()));
-  }
   return hip_status(mxk::launch_gemm_nv(a_codes, a_scales, a_global, a->b->codes, a->b->scales, a->b->global_scale,
-                                        a->c, cbf, a->ldc, a->M, a->N, a->K, s));
+                                        a->c, cbf, a->ldc, a->M, a->N, a->K, s, part, part_bytes, device_cus()));
 }
 
 int mx_moe_route(const int32_t* topk_ids, int64_t tokens, int32_t topk, int32_t experts, int32_t* offsets,

@@ -37,9 +37,12 @@ hipError_t launch_gemm_mx_fused(const void* x, int x_bf16, int64_t ldx, uint8_t*
                                 const uint8_t* b_codes, const uint8_t* b_scales, void* c, int c_bf16, int64_t ldc,
                                 int64_t M, int64_t N, int64_t K, int groups, const int32_t* offsets, void* ws,
                                 int wpl, hipStream_t st);
+// part / part_bytes / cus: as for launch_gemm_mx (K % 256 == 0 only).
 hipError_t launch_gemm_nv(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
                           const uint8_t* b_codes, const uint8_t* b_scales, const float* b_global, void* c, int c_bf16,
-                          int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st);
+                          int64_t ldc, int64_t M, int64_t N, int64_t K, hipStream_t st, float* part = nullptr,
+                          size_t part_bytes = 0, int cus = 0);
+size_t gemm_nv_split_bytes(int64_t M, int64_t N, int64_t K, int cus);
 // Wider MX elements; fmt is the block-scaled MFMA's element code (E4M3 0,
 // E5M2 1, E2M3 2, E3M2 3; the GEMM also takes E2M1 4).
 hipError_t launch_quant_wide(int fmt, const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols,
