@@ -223,7 +223,7 @@ def bench_main(args, torch, mx, W):
     qw_bytes = N * K * 4 + N * K // 2 + N * K // 32
     gemm_bytes = (M + N) * (K // 2 + K // 32) + M * N * 2
     gemm_tflops = flops / (g_ms * 1e-3) / 1e12
-    gfiles = ["gemm_mxfp4.hip", "gemm_mx_tile.h", "gemm_tiles.h", "mx_device.h"]
+    gfiles = ["gemm_mxfp4.hip", "gemm_mx_tile.h", "gemm_tiles.h", "gemm_split.h", "mx_device.h"]
     gsum = "mxfp4_gemm_4096x8192x8192_counters.txt"
     traffic = kernel_counter(gsum, gfiles, "k_gemm_mx_k256", 131072, "hbm_bytes")
     res = {
