@@ -15,6 +15,8 @@
 // then writes its own packed codes (2 or 4 bytes), one lane per block the
 // scale byte.  Several vectors per lane are loaded before any is used so that
 // enough bytes are in flight to cover HBM latency.
+#include <type_traits>
+
 #include "mx_device.h"
 #include "nv_codes.h"
 #include "mx_kernels.h"
@@ -128,27 +130,39 @@ __global__ __launch_bounds__(QT) void k_quant_mx(const TIn* __restrict__ x, int6
 // ---------------------------------------------------------------------------
 // NVFP4: tensor max |x| (partials per workgroup), then quantize
 // ---------------------------------------------------------------------------
+// A lane keeps AU 16-byte vectors in flight: each step of the grid-stride
+// loop issues all of its loads (every one a contiguous 1 KiB per wave) before
+// it reduces any of them.
+constexpr int AU = 8;
 template <typename TIn, bool CONTIG>
 __global__ __launch_bounds__(QT) void k_absmax(const TIn* __restrict__ x, int64_t ldx, uint32_t vpr, uint32_t nvec,
                                                uint32_t* __restrict__ partial) {
   constexpr int EPL = 16 / (int)sizeof(TIn);
   __shared__ uint32_t red[QT / 64];
   uint32_t am = 0;
-  for (uint32_t v = blockIdx.x * QT + threadIdx.x; v < nvec; v += gridDim.x * QT) {
-    const TIn* p;
-    if (CONTIG) {
-      p = x + (size_t)v * EPL;
-    } else {
-      uint32_t r = v / vpr, c = v - r * vpr;
-      p = x + (size_t)r * ldx + (size_t)c * EPL;
+  for (uint32_t base = blockIdx.x * (QT * AU); base < nvec; base += gridDim.x * (QT * AU)) {
+    u32x4 d[AU];
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+      const uint32_t v = base + u * QT + threadIdx.x;
+      const TIn* p;
+      if (CONTIG) {
+        p = x + (size_t)v * EPL;
+      } else {
+        const uint32_t r = v / vpr, c = v - r * vpr;
+        p = x + (size_t)r * ldx + (size_t)c * EPL;
+      }
+      d[u] = v < nvec ? *reinterpret_cast<const u32x4*>(p) : u32x4{0, 0, 0, 0};
     }
-    u32x4 d = *reinterpret_cast<const u32x4*>(p);
-    if constexpr (EPL == 4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) am = max(am, d[i] & 0x7fffffffu);
-    } else {
+    for (int u = 0; u < AU; ++u) {
+      if constexpr (EPL == 4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) am = max(am, max(d[i] & 0x7fffu, (d[i] >> 16) & 0x7fffu) << 16);
+        for (int i = 0; i < 4; ++i) am = max(am, d[u][i] & 0x7fffffffu);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) am = max(am, max(d[u][i] & 0x7fffu, (d[u][i] >> 16) & 0x7fffu) << 16);
+      }
     }
   }
 #pragma unroll
@@ -192,11 +206,20 @@ __device__ __forceinline__ float nv_global_from_partials(const u32x4 (&pv)[NV_PV
   return r == 0 ? 1.0f : ffrom(r) / 2688.0f;
 }
 
-// One lane per 16-element block (QB blocks in flight per lane): the block's
-// scale and its seven decision boundaries (fp64 work) are computed once per
-// block rather than once per 16-byte vector, and no lane exchange is needed.
-// The first iteration's loads go out before the per-tensor scale is reduced
-// from the partial maxima (they do not depend on it).
+// One lane per 16-element block: the block's scale and its seven decision
+// boundaries (fp64 work) are computed once per block rather than once per
+// 16-byte vector.  A wave takes 64 consecutive blocks per step.  Its loads
+// are coalesced (load q of lane l is vector 64 q + l of the wave's range, so
+// each load instruction reads 1 KiB of contiguous memory), and the vectors
+// reach their block's lane through a 4 KiB (fp32; 2 KiB bf16) LDS area of the
+// wave: piece p of block b sits in 16-byte slot VPB b + (p ^ f(b)), f(b) =
+// (b / (16 / VPB)) mod VPB, which keeps both the writes and the block-wise
+// reads free of bank conflicts; a wave's LDS operations complete in order,
+// so no barrier is needed.  The grid is sized so that every wave walks the
+// same number of steps (launch_quant_nv), and each step first issues the
+// loads of the wave's next step.  The first step's loads go out before the
+// per-tensor scale is reduced from the partial maxima (they do not depend
+// on it).
 template <typename TIn, bool CONTIG>
 __global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int64_t ldx, uint32_t bpr,
                                                  uint32_t nblk, uint8_t* __restrict__ codes,
@@ -204,33 +227,86 @@ __global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int6
                                                  const uint32_t* __restrict__ partial, int npart) {
   constexpr int EPL = 16 / (int)sizeof(TIn);   // elements per 16-byte vector
   constexpr int VPB = 16 / EPL;                // vectors per block (4 or 2)
-  constexpr int QB = 2;                        // blocks per lane per iteration
   __shared__ uint32_t red[QT / 64];
-  const int lane = threadIdx.x & 63;
-  const uint32_t wave_global = (blockIdx.x * QT + threadIdx.x) >> 6;
-  const uint32_t nwaves = (gridDim.x * QT) >> 6;
-  const uint32_t stride = nwaves * (64 * QB);
-  auto load = [&](u32x4 (&d)[QB][VPB], uint32_t base) {
+  __shared__ u32x4 stage[QT / 64][64 * VPB];
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u32x4* ws = stage[wave];
+  const uint32_t nvec = nblk * VPB, vpr = bpr * VPB;
+  const uint32_t step = gridDim.x * QT;        // blocks per step of the grid
+  // loads of the wave's 64 blocks from block wb on; vectors past the end read
+  // the last vector again (their blocks are not stored)
+  auto load = [&](u32x4 (&d)[VPB], uint32_t wb) {
 #pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      const uint32_t b = base + u * 64 + lane;
+    for (int q = 0; q < VPB; ++q) {
+      const uint32_t v = min(wb * VPB + q * 64 + lane, nvec - 1);
       const TIn* p;
       if (CONTIG) {
-        p = x + (size_t)b * 16;
+        p = x + (size_t)v * EPL;
       } else {
-        const uint32_t r = b / bpr, c = b - r * bpr;
-        p = x + (size_t)r * ldx + (size_t)c * 16;
+        const uint32_t r = v / vpr, c = v - r * vpr;
+        p = x + (size_t)r * ldx + (size_t)c * EPL;
       }
-#pragma unroll
-      for (int q = 0; q < VPB; ++q)
-        d[u][q] = (b < nblk) ? *reinterpret_cast<const u32x4*>(p + q * EPL) : u32x4{0, 0, 0, 0};
+      d[q] = *reinterpret_cast<const u32x4*>(p);
     }
   };
-  u32x4 d[QB][VPB];
+  auto slot = [](uint32_t b, uint32_t piece) { return VPB * b + (piece ^ ((b / (16 / VPB)) % VPB)); };
+  // ALL: every block of the step exists, so the stores are not tested
+  auto code_step = [&](const u32x4 (&d)[VPB], uint32_t wb, double g, auto all) {
+#pragma unroll
+    for (int q = 0; q < VPB; ++q) {
+      const uint32_t lv = q * 64 + lane;       // the vector's place in the step
+      ws[slot(lv / VPB, lv % VPB)] = d[q];
+    }
+    u32x4 e[VPB];
+#pragma unroll
+    for (int q = 0; q < VPB; ++q) e[q] = ws[slot(lane, q)];
+    const uint32_t b = wb + lane;
+    uint32_t xb[16];
+#pragma unroll
+    for (int q = 0; q < VPB; ++q) {
+      if constexpr (EPL == 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xb[q * 4 + i] = e[q][i];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xb[q * 8 + 2 * i] = e[q][i] << 16;
+          xb[q * 8 + 2 * i + 1] = e[q][i] & 0xffff0000u;
+        }
+      }
+    }
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) am = max(am, xb[i] & 0x7fffffffu);
+    // s_b = E4M3 nearest to amax / (6 g); unit y = s_b * g is exact in fp64.
+    const uint32_t sc = e4m3_rne_sat((double)ffrom(am) / (6.0 * g));
+    const double y = (double)e4m3_to_f32(sc) * g;
+    const NvFast nf = nv_fast_setup(y, am);
+    uint32_t lo, hi;
+    const bool fast_lo = nv_fast_codes8(xb, nf, lo), fast_hi = nv_fast_codes8(xb + 8, nf, hi);
+    if (!(nf.ok && fast_lo && fast_hi)) {   // an element within 2^-20 of a boundary: exact test
+      uint32_t U[7];
+      nv_boundaries(y, U);
+      lo = hi = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo |= nv_code(xb[i], U) << (4 * i);
+        hi |= nv_code(xb[8 + i], U) << (4 * i);
+      }
+    }
+    if (decltype(all)::value || b < nblk) {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      *reinterpret_cast<u32x2_t*>(codes + (size_t)b * 8) = u32x2_t{lo, hi};
+      scales[b] = (uint8_t)sc;
+    }
+  };
+  const std::true_type all;
+  const std::false_type some;
+  u32x4 d[VPB], dn[VPB];
   u32x4 pv[NV_PV];
   if (partial) nv_partials_load(partial, npart, pv);
-  uint32_t base = wave_global * (64 * QB);
-  if (base < nblk) load(d, base);
+  uint32_t wb = blockIdx.x * QT + wave * 64;   // first block of the wave's step
+  load(d, wb);
   float g;
   if (partial) {
     g = nv_global_from_partials(pv, red);
@@ -238,51 +314,19 @@ __global__ __launch_bounds__(QT) void k_quant_nv(const TIn* __restrict__ x, int6
   } else {
     g = *gout;  // static per-tensor scale supplied by the caller
   }
-  const double six_g = 6.0 * (double)g;
-  for (; base < nblk; base += stride) {
-    if (base != wave_global * (64 * QB)) load(d, base);   // the first iteration's blocks are in flight already
+  // while this and the next step are whole, then the last steps with tested
+  // stores; the trip counts are uniform over a wave
+  for (; (uint64_t)wb + step + 63 < nblk; wb += step) {
+    load(dn, wb + step);
+    code_step(d, wb, (double)g, all);
 #pragma unroll
-    for (int u = 0; u < QB; ++u) {
-      const uint32_t b = base + u * 64 + lane;
-      uint32_t xb[16];
+    for (int q = 0; q < VPB; ++q) d[q] = dn[q];
+  }
+  for (; wb < nblk; wb += step) {
+    load(dn, wb + step);
+    code_step(d, wb, (double)g, some);
 #pragma unroll
-      for (int q = 0; q < VPB; ++q) {
-        if constexpr (EPL == 4) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) xb[q * 4 + i] = d[u][q][i];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            xb[q * 8 + 2 * i] = d[u][q][i] << 16;
-            xb[q * 8 + 2 * i + 1] = d[u][q][i] & 0xffff0000u;
-          }
-        }
-      }
-      uint32_t am = 0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) am = max(am, xb[i] & 0x7fffffffu);
-      // s_b = E4M3 nearest to amax / (6 g); unit y = s_b * g is exact in fp64.
-      const uint32_t sc = e4m3_rne_sat((double)ffrom(am) / six_g);
-      const double y = (double)e4m3_to_f32(sc) * (double)g;
-      const NvFast nf = nv_fast_setup(y, am);
-      uint32_t lo, hi;
-      const bool fast_lo = nv_fast_codes8(xb, nf, lo), fast_hi = nv_fast_codes8(xb + 8, nf, hi);
-      if (!(nf.ok && fast_lo && fast_hi)) {   // an element within 2^-20 of a boundary: exact test
-        uint32_t U[7];
-        nv_boundaries(y, U);
-        lo = hi = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          lo |= nv_code(xb[i], U) << (4 * i);
-          hi |= nv_code(xb[8 + i], U) << (4 * i);
-        }
-      }
-      if (b < nblk) {
-        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<u32x2_t*>(codes + (size_t)b * 8) = u32x2_t{lo, hi};
-        scales[b] = (uint8_t)sc;
-      }
-    }
+    for (int q = 0; q < VPB; ++q) d[q] = dn[q];
   }
 }
 
@@ -589,6 +633,10 @@ int nv_partials_count(int64_t rows, int64_t cols, int xdt_bf16) {
   return ((nvec <= (1ull << 23) && n > 1024 ? 1024 : n) + 3) & ~3;
 }
 
+// k_quant_nv workgroups per CU: as many as its registers keep resident (5
+// waves per SIMD for fp32 input, 6 for bf16)
+constexpr int QNV_WG_PER_CU_F32 = 5, QNV_WG_PER_CU_BF16 = 6;
+
 hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols, uint8_t* codes,
                            uint8_t* scales, float* gscale, bool static_global, uint32_t* partial, hipStream_t st) {
   const int epl = xdt_bf16 ? 8 : 4;
@@ -606,7 +654,12 @@ hipError_t launch_quant_nv(const void* x, int xdt_bf16, int64_t ldx, int64_t row
     if (e != hipSuccess) return e;
   }
   const uint32_t bpr = (uint32_t)(cols / 16), nblk = (uint32_t)(rows * cols / 16);
-  const int grid = grid_for(nblk, QT * 2);
+  if (nblk == 0) return hipSuccess;   // (the entry point returns before this for empty tensors)
+  // Only resident workgroups, each wave walking the same number of steps:
+  // no partly filled last round of waves.
+  const uint64_t cap_lanes = (uint64_t)(xdt_bf16 ? QNV_WG_PER_CU_BF16 : QNV_WG_PER_CU_F32) * 256 * QT;
+  const uint64_t steps = (nblk + cap_lanes - 1) / cap_lanes;
+  const int grid = (int)((nblk + steps * QT - 1) / (steps * QT));
   const uint32_t* pp = static_global ? nullptr : partial;
 #define MX_QNV(T, C) hipLaunchKernelGGL((k_quant_nv<T, C>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, bpr, nblk, codes, scales, gscale, pp, npart)
   if (xdt_bf16) { if (contig) MX_QNV(uint16_t, true); else MX_QNV(uint16_t, false); }
