@@ -100,14 +100,10 @@ __device__ __forceinline__ void nv_boundaries(double y, uint32_t U[7]) {
 // The boundaries increase with j, so the count is found by bisection: three
 // compares instead of seven.
 __device__ __forceinline__ uint32_t nv_code(uint32_t xbits, const uint32_t U[7]) {
-  // a three-step binary search; the thresholds are chosen with masks (value
-  // selects), so that the array stays in registers
   const uint32_t a = xbits & 0x7fffffffu;
-  const uint32_t m4 = a >= U[3] ? ~0u : 0u;
-  const uint32_t t2 = (U[1] & ~m4) | (U[5] & m4);
-  const uint32_t m2 = a >= t2 ? ~0u : 0u;
-  const uint32_t t1 = (((U[0] & ~m2) | (U[2] & m2)) & ~m4) | (((U[4] & ~m2) | (U[6] & m2)) & m4);
-  const uint32_t c = (m4 & 4u) | (m2 & 2u) | (a >= t1 ? 1u : 0u);
+  uint32_t c = a >= U[3] ? 4u : 0u;
+  c += a >= (c ? U[5] : U[1]) ? 2u : 0u;
+  c += a >= ((c & 4u) ? ((c & 2u) ? U[6] : U[4]) : ((c & 2u) ? U[2] : U[0])) ? 1u : 0u;
   return c | ((xbits >> 31) << 3);
 }
 
