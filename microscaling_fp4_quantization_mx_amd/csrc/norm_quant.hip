@@ -17,8 +17,9 @@
 //   y_k = fp32(fp32(x_k * r) * gamma_k);
 //   y is then quantized exactly as mx_quantize quantizes an fp32 tensor
 //   (MXFP4, or NVFP4 with the caller's per-tensor scale).
-// A workgroup walks rows (the next row's loads in flight); a row stays in
-// registers between the two passes; gamma is loaded once per workgroup.
+// A workgroup walks rows with the next row's loads in flight; a row is read
+// with coalesced loads, reaches its chunk-owning threads through LDS and stays
+// in registers between the two passes; gamma is loaded once per workgroup.
 #include "mx_device.h"
 #include "nv_codes.h"
 #include "mx_kernels.h"
@@ -61,24 +62,42 @@ __global__ __launch_bounds__(NQ_T) void k_rmsnorm_quant(const uint16_t* __restri
         gm[j][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rg, o + q * 16, 0, 0));
     }
   }
-  // the next row's chunks are loaded while this row is reduced and quantized
-  u32x4 xv[CH][4], xn[CH][4];
-  auto load_row = [&](u32x4 (&dst)[CH][4], int64_t row) {
+  // Row loads are coalesced: load s of thread t is the row's 16-byte vector
+  // 256 s + t, so each load instruction reads 1 KiB of contiguous memory.
+  // The vectors reach their chunk's thread through LDS (piece p of chunk c
+  // in slot 4 c + (p ^ ((c >> 2) & 3)), conflict-free for both sides).  Two
+  // register sets alternate: while one row is staged, reduced and coded, the
+  // next row's loads are in flight in the other.
+  __shared__ u32x4 stage[NQ_T * CH * 4];
+  auto slot = [](int c, int p) { return 4 * c + (p ^ ((c >> 2) & 3)); };
+  auto load_row = [&](u32x4 (&dst)[CH * 4], int64_t row) {
     // rows past the end load zeros (an empty range)
     const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(x + (size_t)(row < rows ? row : 0) * ldx), 0, row < rows ? K * 2 : 0, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const uint32_t o = chunk_off(j);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[j][q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, o + q * 16, 0, 2));
+    for (int v = 0; v < CH * 4; ++v) {
+      const int vec = v * NQ_T + tid;
+      dst[v] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, vec < nch * 4 ? (uint32_t)vec * 16 : FAR, 0, 2));
     }
   };
-  load_row(xv, blockIdx.x);
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
-    load_row(xn, row + gridDim.x);
+  u32x4 xa[CH * 4], xb[CH * 4];
+  auto do_row = [&](const u32x4 (&cur)[CH * 4], u32x4 (&nxt)[CH * 4], int64_t row) {
+    load_row(nxt, row + gridDim.x);
     wait_vmcnt<CH * 4>();                          // this row (and gamma) landed; the next is in flight
+#pragma unroll
+    for (int v = 0; v < CH * 4; ++v) {
+      const int vec = v * NQ_T + tid;
+      stage[slot(vec >> 2, vec & 3)] = cur[v];
+    }
+    __syncthreads();
+    u32x4 xv[CH][4];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int c = tid + j * NQ_T;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[j][q] = stage[slot(c, q)];
+    }
     float part = 0.0f;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
@@ -94,9 +113,11 @@ __global__ __launch_bounds__(NQ_T) void k_rmsnorm_quant(const uint16_t* __restri
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) part = fadd_xor(part, m);
     if (lane == 0) wsum[wave] = part;
+    // (the stage reads above finished before the sums used them, so after this
+    // barrier the stage may be rewritten; wsum is rewritten only after the next
+    // row's first barrier, which every thread reaches after reading it)
     __syncthreads();
     const float total = (wsum[0] + wsum[1]) + (wsum[2] + wsum[3]);
-    __syncthreads();   // wsum is rewritten for the next row
     const float r = (float)(1.0 / sqrt((double)total / (double)K + (double)eps));
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
@@ -167,7 +188,7 @@ __global__ __launch_bounds__(NQ_T) void k_rmsnorm_quant(const uint16_t* __restri
             for (int q = 0; q < 2; ++q) {
               uint32_t o = 0;
 #pragma unroll
-              for (int i = 0; i < 8; ++i) o |= nv_code(yb[q * 8 + i], U) << (4 * i);
+              for (int i = 0; i < 8; ++i) o |= nv_code_sel(yb[q * 8 + i], U) << (4 * i);
               w[h * 2 + q] = o;
             }
           }
@@ -177,10 +198,12 @@ __global__ __launch_bounds__(NQ_T) void k_rmsnorm_quant(const uint16_t* __restri
         *reinterpret_cast<uint16_t*>(scales + (size_t)row * (K / 16) + c * 2) = (uint16_t)sc2;
       }
     }
-#pragma unroll
-    for (int j = 0; j < CH; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) xv[j][q] = xn[j][q];
+  };
+  load_row(xa, blockIdx.x);
+  for (int64_t row = blockIdx.x; row < rows; row += 2 * (int64_t)gridDim.x) {
+    do_row(xa, xb, row);
+    if (row + gridDim.x >= rows) break;
+    do_row(xb, xa, row + gridDim.x);
   }
 }
 

@@ -52,4 +52,18 @@ __device__ __forceinline__ bool nv_fast_codes8(const uint32_t* xb, const NvFast&
   return lo == hi;
 }
 
+// nv_code (the E2M1 state of |x| against the seven fp32 thresholds U of a
+// block, sign kept) with the thresholds picked by value masks rather than by
+// index, so that U stays in registers (selects by index have made the compiler
+// place U in scratch memory).
+__device__ __forceinline__ uint32_t nv_code_sel(uint32_t xbits, const uint32_t U[7]) {
+  const uint32_t a = xbits & 0x7fffffffu;
+  const uint32_t m4 = a >= U[3] ? ~0u : 0u;
+  const uint32_t t2 = (U[1] & ~m4) | (U[5] & m4);
+  const uint32_t m2 = a >= t2 ? ~0u : 0u;
+  const uint32_t t1 = (((U[0] & ~m2) | (U[2] & m2)) & ~m4) | (((U[4] & ~m2) | (U[6] & m2)) & m4);
+  const uint32_t c = (m4 & 4u) | (m2 & 2u) | (a >= t1 ? 1u : 0u);
+  return c | ((xbits >> 31) << 3);
+}
+
 }  // namespace mxk

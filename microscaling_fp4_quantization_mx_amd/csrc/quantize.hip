@@ -206,19 +206,6 @@ __device__ __forceinline__ float nv_global_from_partials(const u32x4 (&pv)[NV_PV
   return r == 0 ? 1.0f : ffrom(r) / 2688.0f;
 }
 
-// nv_code (the E2M1 state of |x| against the seven fp32 thresholds U of a
-// block, sign kept) with the thresholds picked by value masks rather than by
-// index, so that U stays in registers inside the quantize loop.
-__device__ __forceinline__ uint32_t nv_code_sel(uint32_t xbits, const uint32_t U[7]) {
-  const uint32_t a = xbits & 0x7fffffffu;
-  const uint32_t m4 = a >= U[3] ? ~0u : 0u;
-  const uint32_t t2 = (U[1] & ~m4) | (U[5] & m4);
-  const uint32_t m2 = a >= t2 ? ~0u : 0u;
-  const uint32_t t1 = (((U[0] & ~m2) | (U[2] & m2)) & ~m4) | (((U[4] & ~m2) | (U[6] & m2)) & m4);
-  const uint32_t c = (m4 & 4u) | (m2 & 2u) | (a >= t1 ? 1u : 0u);
-  return c | ((xbits >> 31) << 3);
-}
-
 // One lane per 16-element block: the block's scale and its seven decision
 // boundaries (fp64 work) are computed once per block rather than once per
 // 16-byte vector.  A wave takes 64 consecutive blocks per step.  Its loads
