@@ -60,7 +60,9 @@ def check_against_definition(x_bf16, gamma_vals, eps, fmt, g, got_codes, got_sca
     assert nfrag <= max_frac * firm.size, f"{what}: {nfrag} fragile decisions of {firm.size}"
 
 
-@pytest.mark.parametrize("R,K", [(5, 256), (64, 8192), (7, 14336), (3, 32768), (300, 96), (1, 32)])
+# (1030, 256): more rows than workgroups, so workgroups walk three rows and
+# both register sets of the row pipeline are used
+@pytest.mark.parametrize("R,K", [(5, 256), (64, 8192), (7, 14336), (3, 32768), (300, 96), (1, 32), (1030, 256)])
 @pytest.mark.parametrize("gdt", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4"])
 def test_rmsnorm_quantize_matches_definition(R, K, gdt, fmt):
