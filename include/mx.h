@@ -312,8 +312,9 @@ int mx_gemm(const mx_gemm_args *args, void *stream);
  *     the weight stream, the bound from M = 4 on.
  * MXFP8 (E4M3 / E5M2) and MXFP6 (E2M3 / E3M2) weights (W8A16, W6A16) are
  * expanded the same way (exact: at most 4 significant bits, in bf16's normal
- * range for every tensor the quantizer writes) and take the vector ALU for
- * every M.  A scale byte 0 gives a zero block.
+ * range for every tensor the quantizer writes) and take the same two routes:
+ * the vector ALU for M <= 3 or K % 256 != 0, the bf16 matrix cores for
+ * 4 <= M <= 16 with K % 256 == 0.  A scale byte 0 gives a zero block.
  * 1 <= M <= 16; x bf16 [M, K] pitch ld_x; y bf16 [M, N] pitch ld_y.
  * Requires K % 32 == 0.
  */

@@ -19,8 +19,10 @@
 //  * M = 4 .. 16: one dot2 per weight pair and activation row would make the
 //    VALU the bound, so the matrix cores take the products (bf16 MFMA).
 // Weights in the wider MX elements (MXFP8 E4M3 / E5M2, MXFP6 E2M3 / E3M2:
-// W8A16 / W6A16) take the second kernel for every M, with the block's 32 /
-// 24 code bytes expanded by the matching scaled conversion (mx_expand.h).
+// W8A16 / W6A16) take the second kernel for M <= 3 (and any M when K is not a
+// multiple of 256) and a matrix-core kernel of the third kind otherwise, with
+// the block's 32 / 24 code bytes expanded by the matching scaled conversion
+// (mx_expand.h).
 #include "mx_device.h"
 #include "mx_expand.h"
 #include "mx_kernels.h"
@@ -468,10 +470,157 @@ __global__ __launch_bounds__(GM_T) void k_gemv_mf(const uint16_t* __restrict__ x
   if (i < M && n < N) y[(size_t)i * ldy + n] = (uint16_t)f32_to_bf16_rne(sum);
 }
 
+// The same matrix-core route for MXFP8 / MXFP6 weights (W8A16 / W6A16,
+// 4 <= M <= 16, K % 256 == 0).  A block's codes are 32 (FP8) or 24 (FP6)
+// bytes, and the whole block goes to one lane: in chunk position s of its
+// wave, lane l (row or column l % 16, lane group g = l / 16) holds block
+// 4 qd + g of its row, expands its 32 codes at once (mx_expand.h; for FP6 one
+// 32-wide conversion), and the four MFMAs of the step take its elements
+// 8 i .. 8 i + 7, i = 0 .. 3 -- the matrix core sums over the lane groups,
+// so MFMA i adds piece i of four different blocks, and over i every element
+// of the four blocks once.  The activations are staged as in k_gemv_mf and
+// read to match (piece 4 b + i of row m).  A row's 16 blocks of a chunk sit
+// in LDS at positions XOR-swizzled by the row (block p ^ (row & 15) at
+// position p), filled by LDS-DMA copies of 16 (FP8: two per wave and chunk)
+// or 4 (FP6: six per wave and chunk) bytes per lane.  MA: activation rows
+// staged (8 or 16); the rows count M is taken at run time.
+template <int F, int MA>
+__global__ __launch_bounds__(GM_T) void k_gemv_mfw(const uint16_t* __restrict__ x, int64_t ldx, const uint8_t* __restrict__ wc,
+                                                   const uint8_t* __restrict__ ws, int N, int K,
+                                                   uint16_t* __restrict__ y, int64_t ldy, int M) {
+  typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+  static_assert(F >= 0 && F <= 3 && (MA == 8 || MA == 16), "wide formats, 8 or 16 staged rows");
+  constexpr int R = 4;                             // ring slots; chunks in flight: R - 1
+  constexpr int CB = MxElem<F>::DW * 4;            // code bytes per block: 32 or 24
+  constexpr int PB = CB == 32 ? 16 : 4;            // bytes per lane of a weight copy
+  constexpr int WROW = 16 * CB;                    // a row's bytes in one chunk
+  constexpr int WOFF = MA * 1024;                  // weight codes after the activations
+  constexpr int SLOT = WOFF + 32 * WROW;
+  constexpr int WPW = 32 * WROW / (64 * PB) / 8;   // weight copies per wave and chunk (2 or 6)
+  static_assert(WPW * 8 * 64 * PB == 32 * WROW && CB % PB == 0, "whole copies of whole blocks");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[R * SLOT];
+  auto ring = [&](int p) -> uint8_t* { return smem + p * SLOT; };
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15, g = lane >> 4;
+  const int cg = wave & 1, qd = wave >> 1;         // column group, quarter of the chunk's blocks
+  const int n0 = blockIdx.x * 32;
+  const int KB = K / 32 * CB, KS = K / 32;
+  const int rows_ok = __builtin_amdgcn_readfirstlane(max(0, min(32, N - n0)));
+  const __amdgpu_buffer_rsrc_t rwc = __builtin_amdgcn_make_buffer_rsrc((void*)(wc + (size_t)n0 * KB), 0, rows_ok * KB, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rws = __builtin_amdgcn_make_buffer_rsrc((void*)(ws + (size_t)n0 * KS), 0, rows_ok * KS, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)x, 0, __builtin_amdgcn_readfirstlane((int)(((M - 1) * ldx + K) * 2)), 0x00020000);
+  const int nck = (K + GM_CK - 1) / GM_CK;
+  const int np = (nck + R - 1) / R * R;            // chunk slots the loop runs through (uniform)
+  const int rot = blockIdx.x % np;                 // position v holds chunk (v + rot) mod np
+  constexpr uint32_t FAR = 0x40000000u;            // past every buffer: the load returns zeros
+
+  uint32_t sc[R];
+  auto issue = [&](int p, int v) {
+    const int c = v >= np ? nck : (v + rot < np ? v + rot : v + rot - np);
+    const int b0 = c * (GM_CK / 32);               // first block of the chunk
+    uint8_t* slot = ring(p);
+#pragma unroll
+    for (int i = 0; i < WPW; ++i) {
+      const int ci = wave * WPW + i;               // copy ci: pieces 64 ci .. 64 ci + 63 of the slot
+      const int pc = ci * 64 + lane;
+      const int row = pc / (WROW / PB), pr = pc % (WROW / PB);
+      const int pos = pr / (CB / PB), part = pr % (CB / PB);
+      const int blk = b0 + (pos ^ (row & 15));
+      const uint32_t off = blk < KS ? (uint32_t)(row * KB + blk * CB + part * PB) : FAR;
+      if constexpr (PB == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rwc, (lds_ptr_t)(slot + WOFF + ci * 64 * PB), 16, off, 0, 0, GV_NT);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rwc, (lds_ptr_t)(slot + WOFF + ci * 64 * PB), 4, off, 0, 0, GV_NT);
+    }
+#pragma unroll
+    for (int e = 0; e < MA / 8; ++e) {             // rows m >= M copy zeros (no memory traffic)
+      const int m = wave + 8 * e;
+      const int k = c * GM_CK + 8 * (lane ^ m);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(slot + m * 1024), 16,
+                                               (m < M && k < K) ? (uint32_t)(m * ldx + k) * 2 : FAR, 0, 0, 0);
+    }
+    const int sb = b0 + 4 * qd;
+    sc[p] = __builtin_amdgcn_raw_buffer_load_b32(rws, sb < KS ? (uint32_t)((16 * cg + j) * KS + sb) : FAR, 0, GV_NT);
+  };
+  constexpr int LPC = WPW + MA / 8 + 1;            // vector-memory ops per chunk and wave
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](int p) {
+    const uint8_t* slot = ring(p);
+    const int r = 16 * cg + j, b = 4 * qd + g;     // the lane's row and block
+    const uint8_t* wp = slot + WOFF + r * WROW + (b ^ (r & 15)) * CB;
+    uint32_t w[MxElem<F>::DW];
+    if constexpr (CB == 32) {
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(wp), w1 = *reinterpret_cast<const u32x4*>(wp + 16);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) { w[d] = w0[d]; w[4 + d] = w1[d]; }
+    } else {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        const u32x2 t = *reinterpret_cast<const u32x2*>(wp + 8 * d);
+        w[2 * d] = t[0];
+        w[2 * d + 1] = t[1];
+      }
+    }
+    const float sf = pow2f((int)((sc[p] >> (8 * g)) & 0xff) - 127);   // byte 0 gives +0.0
+    uint32_t o[16];
+    expand_block_bf16<F>(w, sf, o);
+    // (rows j >= MA repeat rows j - 8; their outputs are never stored)
+    const int ja = j & (MA - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const u32x4 av = *reinterpret_cast<const u32x4*>(slot + ja * 1024 + (((4 * b + i) ^ ja) << 4));
+      const u32x4 bw = {o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av), __builtin_bit_cast(bf16x8, bw), acc,
+                                                    0, 0, 0);
+    }
+  };
+
+  // the ring walk of k_gemv_mf
+#pragma unroll
+  for (int p = 0; p < R - 1; ++p) issue(p, p);
+  for (int v0 = 0; v0 < nck; v0 += R) {
+#pragma unroll
+    for (int u = 0; u < R; ++u) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      wait_vmcnt<(R - 2) * LPC>();
+      block_barrier();
+      issue((u + R - 1) % R, v0 + u + R - 1);
+      compute(u);
+    }
+  }
+  wait_vmcnt<0>();
+
+  block_barrier();                                 // every wave is done with the ring
+  float(*red)[16][16] = reinterpret_cast<float(*)[16][16]>(smem);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[wave][4 * g + q][j] = acc[q];
+  __syncthreads();
+  const int t = threadIdx.x;
+  const int c = t >> 8, i = (t >> 4) & 15, jj = t & 15;
+  float sum = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sum += red[c + 2 * q][i][jj];
+  const int n = n0 + 16 * c + jj;
+  if (i < M && n < N) y[(size_t)i * ldy + n] = (uint16_t)f32_to_bf16_rne(sum);
+}
+
 hipError_t launch_gemv(int fmt, const void* x, int64_t ldx, int64_t M, const uint8_t* wc, const uint8_t* ws, int64_t N,
                        int64_t K, void* y, int64_t ldy, hipStream_t st) {
   if (N == 0) return hipSuccess;
   if (fmt < 0 || fmt > 4 || M < 1 || M > 16) return hipErrorInvalidValue;
+  if (fmt != 4 && M >= GV_MF_MIN_M && K % 256 == 0 && K < (1 << 25) && ((M - 1) * ldx + K) * 2 < (int64_t)0x3ffffff0) {
+    const int grid = (int)((N + 31) / 32);
+#define MX_GVMW(FF, MA) \
+  hipLaunchKernelGGL((k_gemv_mfw<FF, MA>), dim3(grid), dim3(GM_T), 0, st, (const uint16_t*)x, ldx, wc, ws, (int)N, (int)K, (uint16_t*)y, ldy, (int)M)
+#define MX_GVMWF(FF) case FF: if (M <= 8) MX_GVMW(FF, 8); else MX_GVMW(FF, 16); break;
+    switch (fmt) { MX_GVMWF(0) MX_GVMWF(1) MX_GVMWF(2) MX_GVMWF(3) }
+#undef MX_GVMWF
+#undef MX_GVMW
+    return hipGetLastError();
+  }
   if (fmt != 4) {
     constexpr int RB = GV_LG_RB;
     const int grid = (int)((N + 8 * RB - 1) / (8 * RB));

@@ -360,6 +360,25 @@ def test_wide_gemv(fmt, M):
     assert not bad.any(), (np.argwhere(bad)[:5], np.abs(y - yref).max())
 
 
+@pytest.mark.parametrize("fmt", WIDE)
+@pytest.mark.parametrize("M,N,K", [(4, 300, 4096), (5, 70, 768), (8, 33, 256), (11, 96, 2560), (16, 300, 1280)])
+def test_wide_gemv_matrix_cores(fmt, M, N, K):
+    """4 <= M <= 16 with K a multiple of 256 (the matrix-core kernel): ragged
+    last workgroups of 32 rows, chunks of 512 elements with a half chunk at
+    the end (768, 2560, 1280), a single chunk (256), 8 and 16 staged rows."""
+    announce(f"wide gemv matrix cores {fmt} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 17 + N + K + WIDE.index(fmt))
+    x = bf16_values(rng.standard_normal((M, K)).astype(np.float32) * 2)
+    w = hard_inputs(N, K, M + 3, fmt) * np.float32(1e-3)
+    wq = mx.mx_quantize(torch.from_numpy(w).to(DEV), fmt)
+    wh = O.dequantize_fmt(fmt, host(wq.codes), host(wq.scales))
+    y = host(mx.mx_gemv(torch.from_numpy(x).to(torch.bfloat16).to(DEV), wq).float()).astype(np.float64)
+    yref = O.gemm(x, wh, out="bf16")
+    tol = O.gemm_tolerance(x, wh, yref, out="bf16")
+    bad = np.abs(y - yref) > tol
+    assert not bad.any(), (np.argwhere(bad)[:5], np.abs(y - yref).max())
+
+
 @pytest.mark.parametrize("fmt", ["mxfp8_e4m3", "mxfp6_e3m2"])
 def test_wide_gemv_strided(fmt):
     """Activation and output rows as column slices of wider tensors."""
