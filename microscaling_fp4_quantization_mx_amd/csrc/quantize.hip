@@ -480,10 +480,44 @@ __global__ __launch_bounds__(QT) void k_quant_wide(const TIn* __restrict__ x, in
       const int e = wide_block_exp<F, FLOOR>(am);
       const float inv = pow2f(-e);
       uint32_t c[EPL];
+      uint32_t hw[EPL / 4];                       // FP8 codes from the hardware conversion
+      if constexpr (BITS == 8 && !FLOOR) {
+        // The scaled conversion divides by 2^e and rounds to nearest even
+        // (subnormal codes included); under this exponent rule no element
+        // exceeds the format's largest value, so its overflow handling never
+        // applies.  The floor rule saturates and keeps the software encoder.
+        const float sc = pow2f(e);
+        typedef short s16x2 __attribute__((ext_vector_type(2)));
+        // (bf16 inputs go through their exact fp32 values: the bf16-source
+        // form of the conversion came out of the compiler with its second
+        // and later sources replaced by the first)
 #pragma unroll
-      for (int i = 0; i < EPL; ++i) c[i] = wide_encode<F>(xb[i], inv);
+        for (int h = 0; h < EPL / 4; ++h) {
+          s16x2 r = {0, 0};
+          const float x0 = ffrom(xb[4 * h]), x1 = ffrom(xb[4 * h + 1]);
+          const float x2 = ffrom(xb[4 * h + 2]), x3 = ffrom(xb[4 * h + 3]);
+          if constexpr (F == 0) {
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, x0, x1, sc, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, x2, x3, sc, true);
+          } else {
+            r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, x0, x1, sc, false);
+            r = __builtin_amdgcn_cvt_scalef32_pk_bf8_f32(r, x2, x3, sc, true);
+          }
+          hw[h] = __builtin_bit_cast(uint32_t, r);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) c[i] = wide_encode<F>(xb[i], inv);
+      }
       if (v < nvec) {
-        if constexpr (BITS == 8) {
+        if constexpr (BITS == 8 && !FLOOR) {
+          if constexpr (EPL == 4) {
+            reinterpret_cast<uint32_t*>(codes)[v] = hw[0];
+          } else {
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            reinterpret_cast<u32x2*>(codes)[v] = u32x2{hw[0], hw[1]};
+          }
+        } else if constexpr (BITS == 8) {
           uint32_t w0 = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
           if constexpr (EPL == 4) {
             reinterpret_cast<uint32_t*>(codes)[v] = w0;

@@ -88,6 +88,37 @@ def test_wide_quantize_bit_exact(fmt, dtype, rows, cols, pad):
     assert np.array_equal(gc, rc), np.argwhere(gc != rc)[:5]
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8_e4m3", "mxfp8_e5m2"])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_wide_quantize_fp8_every_bf16(fmt, dtype):
+    """Every finite bf16 magnitude, both signs, coded at its own block scale
+    and at 1, 2, 4, 8 and 12 scale steps above it (subnormal codes, ties and
+    underflow to zero): blocks of one scale-setting maximum Emax * 2^e and
+    31 values; codes and scale bytes bit-exact against the oracle."""
+    announce(f"wide quantize every bf16 {fmt} {dtype}")
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)          # positive finite bf16 patterns
+    vals = (bits << 16).view(np.float32).astype(np.float64)
+    pad = (-len(vals)) % 31
+    groups = np.concatenate([vals, vals[:pad]]).reshape(-1, 31)
+    groups = groups * np.where(np.arange(31) % 2 == 0, 1.0, -1.0)
+    emax = float(O.element_positive_values(fmt)[-1])
+    a = np.abs(groups).max(axis=1)
+    e0 = np.ceil(np.log2(a / emax))
+    e0 = np.where(emax * np.exp2(e0 - 1) >= a, e0 - 1, e0)   # the smallest e with a <= emax 2^e
+    rows = []
+    for d in (0, 1, 2, 4, 8, 12):
+        m = emax * np.exp2(e0 + d)
+        ok = m <= 3.3e38                                   # a finite bf16 maximum
+        rows.append(np.concatenate([m[ok, None], groups[ok]], axis=1))
+    x = np.concatenate(rows).astype(np.float32)
+    assert np.array_equal(bf16_values(x), x)
+    q = mx.mx_quantize(torch.from_numpy(x).to(dtype).to(DEV), fmt)
+    rc, rs = O.mx_quantize_fmt(x, fmt)
+    gc, gs = host(q.codes), host(q.scales)
+    assert np.array_equal(gs, rs), np.argwhere(gs != rs)[:5]
+    assert np.array_equal(gc, rc), np.argwhere(gc != rc)[:5]
+
+
 @pytest.mark.parametrize("fmt", WIDE)
 def test_wide_dequantize_exact(fmt):
     announce(f"wide dequantize {fmt}")
