@@ -88,9 +88,9 @@ def test_wide_quantize_bit_exact(fmt, dtype, rows, cols, pad):
     assert np.array_equal(gc, rc), np.argwhere(gc != rc)[:5]
 
 
-@pytest.mark.parametrize("fmt", ["mxfp8_e4m3", "mxfp8_e5m2"])
+@pytest.mark.parametrize("fmt", WIDE)
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
-def test_wide_quantize_fp8_every_bf16(fmt, dtype):
+def test_wide_quantize_every_bf16(fmt, dtype):
     """Every finite bf16 magnitude, both signs, coded at its own block scale
     and at 1, 2, 4, 8 and 12 scale steps above it (subnormal codes, ties and
     underflow to zero): blocks of one scale-setting maximum Emax * 2^e and
