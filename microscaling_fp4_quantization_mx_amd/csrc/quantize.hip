@@ -559,6 +559,106 @@ __global__ __launch_bounds__(QT) void k_quant_wide(const TIn* __restrict__ x, in
   }
 }
 
+// MXFP6 (E2M3 / E3M2) under the pages' exponent rule: the hardware converts
+// a whole 32-element block at once (v_cvt_scalef32_2xpk16_fp6_f32 / _bf6_f32:
+// divide by 2^e, round to nearest even), so a lane owns a block.  The
+// instruction interleaves its two 16-value sources (6-bit field 2i from the
+// first source's value i, field 2i + 1 from the second's; probed), so the
+// block's even elements go in the first and its odd elements in the second,
+// which gives element j at bits 6j .. 6j + 5.  The walk and the coalesced
+// loads are those of k_quant_nv: a wave takes 64 consecutive blocks per step,
+// load q of lane l is vector 64 q + l of that range, and the vectors reach
+// their block's lane through an LDS area of the wave (piece p of block b in
+// slot VPB b + (p ^ f(b)), f(b) = (b / (16 / VPB)) mod VPB).  bf16 inputs are
+// converted from their exact fp32 values.
+template <typename TIn, int F, bool CONTIG>
+__global__ __launch_bounds__(QT) void k_quant_fp6(const TIn* __restrict__ x, int64_t ldx, uint32_t bpr, uint32_t nblk,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  static_assert(F == 2 || F == 3, "FP6 element formats");
+  constexpr int EPL = 16 / (int)sizeof(TIn);   // elements per 16-byte vector
+  constexpr int VPB = 32 / EPL;                // vectors per block (8 or 4)
+  __shared__ u32x4 stage[QT / 64][64 * VPB];
+  const uint32_t lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  u32x4* ws = stage[wave];
+  const uint32_t nvec = nblk * VPB, vpr = bpr * VPB;
+  const uint32_t step = gridDim.x * QT;        // blocks per step of the grid
+  auto load = [&](u32x4 (&d)[VPB], uint32_t wb) {
+#pragma unroll
+    for (int q = 0; q < VPB; ++q) {
+      const uint32_t v = min(wb * VPB + q * 64 + lane, nvec - 1);   // past the end: the last vector again
+      const TIn* p;
+      if (CONTIG) {
+        p = x + (size_t)v * EPL;
+      } else {
+        const uint32_t r = v / vpr, c = v - r * vpr;
+        p = x + (size_t)r * ldx + (size_t)c * EPL;
+      }
+      d[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    }
+  };
+  auto slot = [](uint32_t b, uint32_t piece) { return VPB * b + (piece ^ ((b / (16 / VPB)) % VPB)); };
+  auto code_step = [&](const u32x4 (&d)[VPB], uint32_t wb, auto all) {
+#pragma unroll
+    for (int q = 0; q < VPB; ++q) {
+      const uint32_t lv = q * 64 + lane;
+      ws[slot(lv / VPB, lv % VPB)] = d[q];
+    }
+    typedef float f32x16 __attribute__((ext_vector_type(16)));
+    f32x16 ev, od;                             // even and odd elements of the block
+    uint32_t am = 0;
+#pragma unroll
+    for (int q = 0; q < VPB; ++q) {
+      const u32x4 t = ws[slot(lane, q)];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (EPL == 4) {
+          const int k = q * 4 + i;
+          am = max(am, t[i] & 0x7fffffffu);
+          if (k % 2 == 0) ev[k / 2] = ffrom(t[i]); else od[k / 2] = ffrom(t[i]);
+        } else {
+          const int k = q * 8 + 2 * i;         // elements k (low half) and k + 1
+          const uint32_t a = t[i] << 16, b = t[i] & 0xffff0000u;
+          am = max(am, max(a & 0x7fffffffu, b & 0x7fffffffu));
+          ev[k / 2] = ffrom(a);
+          od[k / 2] = ffrom(b);
+        }
+      }
+    }
+    const int e = wide_block_exp<F, false>(am);
+    const float sc = pow2f(e);
+    typedef uint32_t u32x6_t __attribute__((ext_vector_type(6)));
+    u32x6_t r;
+    if constexpr (F == 2) r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(ev, od, sc);
+    else r = __builtin_amdgcn_cvt_scalef32_2xpk16_bf6_f32(ev, od, sc);
+    const uint32_t b = wb + lane;
+    if (decltype(all)::value || b < nblk) {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      u32x2_t* dst = reinterpret_cast<u32x2_t*>(codes + (size_t)b * 24);
+      dst[0] = u32x2_t{r[0], r[1]};
+      dst[1] = u32x2_t{r[2], r[3]};
+      dst[2] = u32x2_t{r[4], r[5]};
+      scales[b] = (uint8_t)(e + 127);
+    }
+  };
+  const std::true_type all;
+  const std::false_type some;
+  u32x4 d[VPB], dn[VPB];
+  uint32_t wb = blockIdx.x * QT + wave * 64;   // first block of the wave's step
+  load(d, wb);
+  for (; (uint64_t)wb + step + 63 < nblk; wb += step) {
+    load(dn, wb + step);
+    code_step(d, wb, all);
+#pragma unroll
+    for (int q = 0; q < VPB; ++q) d[q] = dn[q];
+  }
+  for (; wb < nblk; wb += step) {
+    load(dn, wb + step);
+    code_step(d, wb, some);
+#pragma unroll
+    for (int q = 0; q < VPB; ++q) d[q] = dn[q];
+  }
+}
+
 // value(code) * 2^(E-127): each lane expands 16 elements (half a block).
 template <int F>
 __device__ __forceinline__ float wide_decode(uint32_t code) {
@@ -720,12 +820,30 @@ hipError_t launch_dequant(bool nv, const uint8_t* codes, const uint8_t* scales, 
   return hipGetLastError();
 }
 
+constexpr int QF6_WG_PER_CU_F32 = 4, QF6_WG_PER_CU_BF16 = 5;   // k_quant_fp6: resident workgroups per CU
+
 hipError_t launch_quant_wide(int fmt, const void* x, int xdt_bf16, int64_t ldx, int64_t rows, int64_t cols,
                              uint8_t* codes, uint8_t* scales, hipStream_t st, bool floor_rule) {
   const int epl = xdt_bf16 ? 8 : 4;
   const uint32_t vpr = (uint32_t)(cols / epl);
   const uint32_t nvec = (uint32_t)(rows * cols / epl);
   const bool contig = ldx == cols;
+  if ((fmt == 2 || fmt == 3) && !floor_rule) {
+    // one lane per block; only resident workgroups, each wave walking the
+    // same number of steps
+    const uint32_t bpr = (uint32_t)(cols / 32), nblk = (uint32_t)(rows * cols / 32);
+    if (nblk == 0) return hipSuccess;
+    const uint64_t cap = (uint64_t)(xdt_bf16 ? QF6_WG_PER_CU_BF16 : QF6_WG_PER_CU_F32) * 256 * QT;
+    const uint64_t steps = (nblk + cap - 1) / cap;
+    const int g6 = (int)((nblk + steps * QT - 1) / (steps * QT));
+#define MX_QF6(T, F, C) hipLaunchKernelGGL((k_quant_fp6<T, F, C>), dim3(g6), dim3(QT), 0, st, (const T*)x, ldx, bpr, nblk, codes, scales)
+#define MX_QF6C(T, F) if (contig) MX_QF6(T, F, true); else MX_QF6(T, F, false)
+    if (xdt_bf16) { if (fmt == 2) { MX_QF6C(uint16_t, 2); } else { MX_QF6C(uint16_t, 3); } }
+    else { if (fmt == 2) { MX_QF6C(float, 2); } else { MX_QF6C(float, 3); } }
+#undef MX_QF6C
+#undef MX_QF6
+    return hipGetLastError();
+  }
   const int grid = grid_for(nvec, QT * QU);
 #define MX_QW4(T, F, C, FL) hipLaunchKernelGGL((k_quant_wide<T, F, C, FL>), dim3(grid), dim3(QT), 0, st, (const T*)x, ldx, vpr, nvec, codes, scales)
 #define MX_QW3(T, F, C) if (floor_rule) MX_QW4(T, F, C, true); else MX_QW4(T, F, C, false)
